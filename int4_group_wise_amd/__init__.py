@@ -1,0 +1,16 @@
+"""Group-wise 4-bit weight-only quantization and the W4A16 linear on MI355X.
+
+The compute path is the HIP library ``libw4.so`` (C ABI declared in
+``include/w4.h``); ``int4_group_wise_amd.w4`` is its thin Python binding.
+Its names are re-exported here on first access, so importing the package (or
+its ``workloads`` module) does not load the library.
+"""
+_EXPORTS = ("SYM", "ASYM", "W4Error", "library_path", "load", "quantize_pack",
+            "dequantize", "linear", "linear_workspace_bytes")
+
+
+def __getattr__(name):
+    if name in _EXPORTS:
+        from . import w4
+        return getattr(w4, name)
+    raise AttributeError(name)

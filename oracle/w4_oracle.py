@@ -1,0 +1,291 @@
+"""Oracle: the plain CPU definition of group-wise 4-bit weight-only quantization
+(quantize, pack, unpack, dequantize) and of the W4A16 linear
+``y = x . dequant(W)^T + b``.
+
+TEST INFRASTRUCTURE.  Only the test suite, the smoke check and the benchmark's
+CPU-baseline leg import this module.  The HIP library never imports it, and the
+two share no code, tables or constants.
+
+Sources, cited by page and section:
+  [LoopQ]  LoopQ ``packed_weight.py`` page: ``PackedLoopQWeight.validate``,
+           ``payload_bytes``, ``_dequantize_validated``, ``state_dict``,
+           ``pack_weight``.
+  [Keras]  keras-nightly ``dense.py`` diff page: ``Dense._int4_build``,
+           ``Dense._int4_call``, the int4 branch of ``Dense.quantize``.
+  [Gemma]  Gemma peft ``_quantization_utils.py`` page: ``uniform_quantize``.
+  [Paddle] PaddleNLP ``quantization_linear.py`` page: ``quant_weight_forward``,
+           ``QuantizationLinearFunc``.
+  [MAX]    Modular MAX ``graph/quantization.py`` page: ``QuantizationConfig``.
+
+Arithmetic.  The codec runs in fp32: ``np.float32`` arrays and constants only,
+IEEE round-to-nearest-even division, ``np.rint`` (round half to even).  The
+linear runs in fp64.  bf16 values travel as ``uint16`` bit patterns.
+
+Readings taken where the pages leave a step open:
+  R1  Scales multiply: ``dq = v * s`` ([LoopQ] ``_dequantize_validated``).
+  R2  Signed codes: the quantizer emits [-7, 7]; the decoder maps nibble
+      values >= 8 to value - 16, so the reserved code 8 reads as -8
+      ([LoopQ] ``validate``, format versions 1 and 2).
+  R3  Symmetric group scale ``s = fp32(amax / 7)``;
+      ``q = clamp(rint(fp32(w / s)), -7, 7)``.
+  R4  Asymmetric (zero-point) group: ``lo = min(0, min w)``,
+      ``hi = max(0, max w)``, ``s = fp32(fp32(hi - lo) / 15)``,
+      ``z = clamp(rint(fp32(-lo / s)), 0, 15)``,
+      ``q = clamp(rint(fp32(w / s)) + z, 0, 15)``; decode ``v = q - z``.
+      (The quantizer's body is not on the [Keras] page; only its name and
+      output shapes are.)
+  R5  A group whose computed scale is 0 (all zeros, or underflow) gets s = 1.
+  R6  The group of column k is ``g_idx[k]`` when a g_idx is given, else
+      ``k // G`` ([Keras] ``_int4_build``, the g_idx initializer).
+  R7  The linear uses the bf16-rounded dequantized weight (the [Keras] forward
+      casts the dequantized kernel to the compute dtype before the matmul),
+      accumulates in fp64 and adds the bias in fp64.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+F32 = np.float32
+SYM = "sym"     # signed two's-complement nibbles, no zero-point
+ASYM = "asym"   # unsigned nibbles with a per-group zero-point
+
+__all__ = [
+    "SYM", "ASYM", "n_groups", "group_of_columns", "bf16_bits_to_f32",
+    "f32_to_bf16_bits", "quantize", "pack_nibbles", "unpack_nibbles",
+    "decode", "dequantize", "quantize_pack", "linear", "validate_packed",
+    "payload_bytes",
+]
+
+
+# ---------------------------------------------------------------------------
+# shapes and groups
+# ---------------------------------------------------------------------------
+def n_groups(K: int, G: int) -> int:
+    """Groups per row, ``ceil(K / G)`` ([Keras] ``_int4_build`` n_groups;
+    [LoopQ] ``validate`` scale shape with G = 32)."""
+    return -(-K // G)
+
+
+def group_of_columns(K: int, G: int, g_idx=None) -> np.ndarray:
+    """Group id of every input column (R6).  Default: contiguous blocks of G
+    columns ([Keras] ``_int4_build``: floor of arange(input_dim) / block_size)."""
+    if g_idx is None:
+        return np.arange(K, dtype=np.int64) // G
+    gid = np.asarray(g_idx).astype(np.int64)
+    if gid.shape != (K,):
+        raise ValueError("g_idx must have one entry per input column")
+    if gid.size and (gid.min() < 0 or gid.max() >= n_groups(K, G)):
+        raise ValueError("g_idx entries must lie in [0, ceil(K/G))")
+    return gid
+
+
+# ---------------------------------------------------------------------------
+# bf16 <-> fp32 (R7, [LoopQ] ``_dequantize_validated`` final ``.to(dtype)``)
+# ---------------------------------------------------------------------------
+def bf16_bits_to_f32(bits) -> np.ndarray:
+    """Exact widening: a bf16 value is the top 16 bits of an fp32."""
+    b = np.asarray(bits).astype(np.uint16)
+    return (b.astype(np.uint32) << 16).view(F32)
+
+
+def f32_to_bf16_bits(x) -> np.ndarray:
+    """Nearest bf16 to each finite fp32 value, ties to the even significand.
+
+    Written as the definition: the two bf16 neighbours are the fp32 value
+    truncated to 16 bits (toward zero) and the next bf16 away from zero; pick
+    the nearer one, and on a tie the one whose last significand bit is 0.
+    Distances are exact in fp64.
+    """
+    x = np.ascontiguousarray(x, dtype=F32)
+    u = x.view(np.uint32)
+    toward_zero = (u & np.uint32(0xFFFF0000)).astype(np.uint32)
+    away = (toward_zero + np.uint32(0x10000)).astype(np.uint32)
+    mag = np.abs(x.astype(np.float64))
+    lo = np.abs(toward_zero.view(F32).astype(np.float64))
+    with np.errstate(over="ignore", invalid="ignore"):
+        hi = np.abs(away.view(F32).astype(np.float64))
+        d_lo = mag - lo
+        d_hi = hi - mag
+    even_lo = ((toward_zero >> np.uint32(16)) & np.uint32(1)) == 0
+    pick_away = (d_hi < d_lo) | ((d_hi == d_lo) & ~even_lo)
+    out = np.where(pick_away, away, toward_zero) >> np.uint32(16)
+    return out.astype(np.uint16)
+
+
+# ---------------------------------------------------------------------------
+# quantize (R3, R4, R5)
+# ---------------------------------------------------------------------------
+def quantize(w, G: int, mode: str, g_idx=None):
+    """Group-wise int4 quantization of ``w`` [N, K] (fp32 values).
+
+    Returns ``(q, scales, zeros)``: ``q`` int16 [N, K] holding the integer
+    codes (sym: [-7, 7]; asym: [0, 15]), ``scales`` fp32 [N, ceil(K/G)] and
+    ``zeros`` uint8 [N, ceil(K/G)] (asym) or ``None`` (sym).
+
+    Group statistics run over the member columns {k : gid(k) = g}; a group that
+    no column maps to keeps s = 1 and z = 0 (R5).  Sym follows the absmax rule
+    scale = max|w| / 7 with round half to even ([Gemma] ``uniform_quantize``
+    uses the same rounding; [LoopQ] v1 forbids code -8, so the range is
+    [-7, 7]).  Asym follows R4.
+    """
+    w = np.asarray(w, dtype=F32)
+    if w.ndim != 2:
+        raise ValueError("w must be a matrix")
+    N, K = w.shape
+    if mode not in (SYM, ASYM):
+        raise ValueError("mode must be 'sym' or 'asym'")
+    NG = n_groups(K, G)
+    gid = group_of_columns(K, G, g_idx)
+    q = np.zeros((N, K), dtype=np.int16)
+    scales = np.ones((N, NG), dtype=F32)
+    zeros = np.zeros((N, NG), dtype=np.uint8) if mode == ASYM else None
+    for g in range(NG):
+        cols = np.nonzero(gid == g)[0]
+        if cols.size == 0:
+            continue
+        blk = w[:, cols]
+        if mode == SYM:
+            amax = np.max(np.abs(blk), axis=1)
+            s = (amax / F32(7)).astype(F32)
+            s[s == F32(0)] = F32(1)
+            r = np.rint((blk / s[:, None]).astype(F32))
+            q[:, cols] = np.clip(r, -7, 7).astype(np.int16)
+        else:
+            lo = np.minimum(np.min(blk, axis=1), F32(0))
+            hi = np.maximum(np.max(blk, axis=1), F32(0))
+            span = (hi - lo).astype(F32)
+            s = (span / F32(15)).astype(F32)
+            s[s == F32(0)] = F32(1)
+            z = np.clip(np.rint((-lo / s).astype(F32)), 0, 15)
+            r = np.rint((blk / s[:, None]).astype(F32))
+            q[:, cols] = np.clip(r + z[:, None], 0, 15).astype(np.int16)
+            zeros[:, g] = z.astype(np.uint8)
+        scales[:, g] = s
+    return q, scales, zeros
+
+
+# ---------------------------------------------------------------------------
+# pack / unpack ([LoopQ] ``pack_weight``, ``_dequantize_validated``)
+# ---------------------------------------------------------------------------
+def pack_nibbles(q) -> np.ndarray:
+    """Two codes per byte along the row: nibble = q & 15 (two's complement for
+    negative codes); column 2j goes to the low nibble of byte j and column
+    2j+1 to the high nibble; an odd row is padded with a 0 nibble
+    ([LoopQ] ``pack_weight``, nibble order 'even_column_low')."""
+    q = np.asarray(q)
+    N, K = q.shape
+    u = (q.astype(np.int16) & 15).astype(np.uint8)
+    if K % 2:
+        u = np.concatenate([u, np.zeros((N, 1), np.uint8)], axis=1)
+    return (u[:, 0::2] | (u[:, 1::2] << 4)).astype(np.uint8)
+
+
+def unpack_nibbles(codes, K: int) -> np.ndarray:
+    """Inverse of ``pack_nibbles``: uint8 [N, K] nibble values 0..15
+    ([LoopQ] ``_dequantize_validated``: low nibble first, then slice to
+    width)."""
+    c = np.asarray(codes, dtype=np.uint8)
+    N = c.shape[0]
+    pairs = np.stack([c & 15, c >> 4], axis=-1).reshape(N, -1)
+    return pairs[:, :K].astype(np.uint8)
+
+
+def decode(u, mode: str, zeros=None, gid=None) -> np.ndarray:
+    """Integer value of each nibble.  Sym: two's complement, v = u - 16 for
+    u >= 8 ([LoopQ] ``_dequantize_validated``).  Asym: v = u - z[n, gid(k)]
+    (R4), exact in integers."""
+    u = np.asarray(u).astype(np.int32)
+    if mode == SYM:
+        return np.where(u >= 8, u - 16, u)
+    return u - np.asarray(zeros).astype(np.int32)[:, gid]
+
+
+def dequantize(codes, scales, zeros, g_idx, K: int, G: int, mode: str,
+               out: str = "bf16") -> np.ndarray:
+    """Dense weight from packed codes: ``d = fp32(v) * s[n, gid(k)]`` (one
+    fp32 multiply), then cast ([LoopQ] ``_dequantize_validated``; [Keras]
+    ``_int4_call`` dequantize-with-scale/zero map).  ``out='bf16'`` returns
+    uint16 bit patterns (R7), ``out='f32'`` the fp32 values."""
+    gid = group_of_columns(K, G, g_idx)
+    v = decode(unpack_nibbles(codes, K), mode, zeros, gid)
+    s = np.asarray(scales, dtype=F32)[:, gid]
+    d = (v.astype(F32) * s).astype(F32)
+    if out == "f32":
+        return d
+    if out == "bf16":
+        return f32_to_bf16_bits(d)
+    raise ValueError("out must be 'bf16' or 'f32'")
+
+
+def quantize_pack(w, G: int, mode: str, g_idx=None):
+    """quantize then pack: ``(codes uint8 [N, ceil(K/2)], scales, zeros)``
+    ([LoopQ] ``pack_weight``; [Keras] ``quantize`` int4 branch)."""
+    q, scales, zeros = quantize(w, G, mode, g_idx)
+    return pack_nibbles(q), scales, zeros
+
+
+# ---------------------------------------------------------------------------
+# linear ([Keras] ``_int4_call``; [Paddle] ``quant_weight_forward``)
+# ---------------------------------------------------------------------------
+def linear(x_bits, codes, scales, zeros, g_idx, K: int, G: int, mode: str,
+           bias_bits=None, row_chunk: int = 4096) -> np.ndarray:
+    """``y[m, n] = sum_k x[m, k] * Wd[n, k] + b[n]`` in fp64, where Wd is the
+    bf16-rounded dequantized weight (R7).  ``x_bits`` uint16 [M, K] and
+    ``bias_bits`` uint16 [N] are bf16 bit patterns.  Returns fp64 [M, N].
+    Rows of W are processed in chunks only to bound memory."""
+    x = bf16_bits_to_f32(x_bits).astype(np.float64)
+    codes = np.asarray(codes)
+    N = codes.shape[0]
+    y = np.empty((x.shape[0], N), dtype=np.float64)
+    for n0 in range(0, N, row_chunk):
+        n1 = min(N, n0 + row_chunk)
+        z = None if zeros is None else np.asarray(zeros)[n0:n1]
+        wd = bf16_bits_to_f32(dequantize(codes[n0:n1], np.asarray(scales)[n0:n1],
+                                         z, g_idx, K, G, mode, "bf16"))
+        y[:, n0:n1] = x @ wd.astype(np.float64).T
+    if bias_bits is not None:
+        y += bf16_bits_to_f32(bias_bits).astype(np.float64)[None, :]
+    return y
+
+
+# ---------------------------------------------------------------------------
+# format checks ([LoopQ] ``validate``, ``payload_bytes``)
+# ---------------------------------------------------------------------------
+def validate_packed(codes, scales, zeros, K: int, G: int, mode: str,
+                    g_idx=None, narrow: bool = True) -> None:
+    """Raise ValueError unless the packed tensors satisfy the format rules:
+    codes uint8 [N, ceil(K/2)]; scales fp32 [N, ceil(K/G)], finite and > 0;
+    zeros uint8 with the scales' shape and values <= 15 (asym); a 0 high
+    nibble in the last byte when K is odd; with ``narrow`` (LoopQ format v1),
+    no signed code 8 (-8)."""
+    codes = np.asarray(codes)
+    scales = np.asarray(scales)
+    if codes.dtype != np.uint8 or codes.ndim != 2 or codes.shape[1] != -(-K // 2):
+        raise ValueError("packed code shape/dtype mismatch")
+    N = codes.shape[0]
+    if scales.dtype != F32 or scales.shape != (N, n_groups(K, G)):
+        raise ValueError("scale shape/dtype mismatch")
+    if not np.all(np.isfinite(scales)) or not np.all(scales > 0):
+        raise ValueError("scales must be finite and positive")
+    if K % 2 and np.any(codes[:, -1] >> 4):
+        raise ValueError("nonzero unused high nibble")
+    if mode == ASYM:
+        zeros = np.asarray(zeros)
+        if zeros.dtype != np.uint8 or zeros.shape != scales.shape or np.any(zeros > 15):
+            raise ValueError("zero-point shape/dtype/range mismatch")
+    elif zeros is not None:
+        raise ValueError("symmetric codes carry no zero-points")
+    elif narrow:
+        u = unpack_nibbles(codes, K)
+        if np.any(u == 8):
+            raise ValueError("code -8 is outside the narrow signed range")
+    group_of_columns(K, G, g_idx)
+
+
+def payload_bytes(codes, scales, zeros=None) -> int:
+    """Tensor payload only: code bytes + 4 bytes per scale (+ 1 byte per
+    zero-point) ([LoopQ] ``payload_bytes``)."""
+    n = int(np.asarray(codes).size) + 4 * int(np.asarray(scales).size)
+    if zeros is not None:
+        n += int(np.asarray(zeros).size)
+    return n

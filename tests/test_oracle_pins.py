@@ -1,0 +1,344 @@
+"""Pins for the CPU oracle: checks against what the pages and the mathematics
+fix, never against the oracle's own formulas retyped.
+
+  * hand-worked examples (tests/golden/hand_worked.json, each with its source);
+  * library routines: torch's fp32 -> bf16 conversion, numpy's int8 sign
+    extension, a pure-Python brute-force matmul;
+  * invariants: code ranges, positive finite scales, the half-step error
+    bound, a code of magnitude 7 in every non-zero symmetric group, the zero
+    high nibble for odd K, pack/unpack round trip;
+  * special cases: G = K against the Gemma per-channel formula (scale as an
+    inverse, multiply instead of divide); g_idx = k // G against no g_idx; a
+    column permutation against g_idx;
+  * the identity activation, whose linear output is the dequantized weight.
+"""
+import numpy as np
+import pytest
+import torch
+
+from oracle import w4_oracle as O
+from int4_group_wise_amd.workloads import workload, generate, bf16_bits
+
+F32 = np.float32
+
+
+def _arr(v, dt):
+    return None if v is None else np.array(v, dtype=dt)
+
+
+# --------------------------------------------------------------------------
+# hand-worked examples
+# --------------------------------------------------------------------------
+def test_golden_quantize_pack_dequant(golden):
+    for c in golden["cases"]:
+        w = np.array(c["w"], F32)
+        g_idx = _arr(c["g_idx"], np.int32)
+        q, s, z = O.quantize(w, c["G"], c["mode"], g_idx)
+        assert q.tolist() == c["q"], c["name"]
+        assert s.tolist() == c["scales"], c["name"]
+        if c["zeros"] is None:
+            assert z is None
+        else:
+            assert z.tolist() == c["zeros"], c["name"]
+        codes, s2, z2 = O.quantize_pack(w, c["G"], c["mode"], g_idx)
+        assert codes.tolist() == c["codes"], c["name"]
+        d = O.dequantize(codes, s2, z2, g_idx, c["K"], c["G"], c["mode"], "f32")
+        assert d.tolist() == c["dequant"], c["name"]
+        if "dequant_bf16_bits" in c:
+            db = O.dequantize(codes, s2, z2, g_idx, c["K"], c["G"], c["mode"], "bf16")
+            assert db.tolist() == c["dequant_bf16_bits"], c["name"]
+        O.validate_packed(codes, s2, z2, c["K"], c["G"], c["mode"], g_idx)
+
+
+def test_golden_decode(golden):
+    d = golden["decode"]
+    u = O.unpack_nibbles(np.array([d["bytes"]], np.uint8), 4)
+    assert O.decode(u, O.SYM).ravel().tolist() == d["values"]
+    with pytest.raises(ValueError):
+        O.validate_packed(np.array([d["bytes"]], np.uint8), np.ones((1, 1), F32), None, 4, 32, O.SYM)
+    O.validate_packed(np.array([d["bytes"]], np.uint8), np.ones((1, 1), F32), None, 4, 32, O.SYM,
+                      narrow=False)
+
+
+def test_golden_linear(golden):
+    lin = golden["linear"]
+    c = next(c for c in golden["cases"] if c["name"] == lin["case"])
+    codes, s, z = O.quantize_pack(np.array(c["w"], F32), c["G"], c["mode"])
+    xb = O.f32_to_bf16_bits(np.array(lin["x"], F32))
+    bb = O.f32_to_bf16_bits(np.array(lin["bias"], F32))
+    y = O.linear(xb, codes, s, z, None, c["K"], c["G"], c["mode"], bb)
+    assert y.tolist() == lin["y"]
+
+
+# --------------------------------------------------------------------------
+# bit-level pins against library routines
+# --------------------------------------------------------------------------
+def test_bf16_rounding_matches_torch():
+    rng = np.random.default_rng(1)
+    parts = [
+        rng.standard_normal(200000).astype(F32),
+        (rng.standard_normal(50000) * 1e-39).astype(F32),     # fp32 subnormals
+        (rng.standard_normal(50000) * 1e30).astype(F32),
+        np.array([0.0, -0.0, 1.0, -1.0, 3.0e38, -3.0e38], F32),
+    ]
+    # exact ties: low 16 bits = 0x8000, both parities of bit 16
+    u = rng.integers(0, 2**32, 100000, dtype=np.uint64).astype(np.uint32)
+    u = (u & np.uint32(0xFFFF0000)) | np.uint32(0x8000)
+    u = u[((u >> 23) & 0xFF) < 0xFE]                          # keep finite after rounding
+    parts.append(u.view(F32))
+    x = np.concatenate(parts)
+    ours = O.f32_to_bf16_bits(x)
+    ref = torch.from_numpy(x.copy()).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(ours, ref)
+    assert np.array_equal(O.bf16_bits_to_f32(ref), torch.from_numpy(ref.view(np.int16).copy())
+                          .view(torch.bfloat16).float().numpy())
+
+
+def test_all_bytes_decode_against_sign_extension():
+    b = np.arange(256, dtype=np.uint8)[None, :]
+    u = O.unpack_nibbles(b, 512)
+    assert np.array_equal(u[0, 0::2], np.arange(256) & 15)
+    assert np.array_equal(u[0, 1::2], np.arange(256) >> 4)
+    # two's-complement nibble = arithmetic shift of the nibble placed at the top of an int8
+    ref = ((u.astype(np.uint8) << 4).view(np.int8) >> 4).astype(np.int32)
+    assert np.array_equal(O.decode(u, O.SYM), ref)
+    # closed form (c xor 8) - 8
+    assert np.array_equal(O.decode(u, O.SYM), (u.astype(np.int32) ^ 8) - 8)
+
+
+@pytest.mark.parametrize("K", [1, 2, 7, 8, 33, 64])
+def test_pack_unpack_round_trip(K):
+    rng = np.random.default_rng(K)
+    q = rng.integers(-8, 8, size=(5, K))
+    codes = O.pack_nibbles(q)
+    assert codes.shape == (5, (K + 1) // 2) and codes.dtype == np.uint8
+    assert np.array_equal(O.decode(O.unpack_nibbles(codes, K), O.SYM), q)
+    if K % 2:
+        assert not np.any(codes[:, -1] >> 4)
+    u = rng.integers(0, 16, size=(3, K))
+    assert np.array_equal(O.unpack_nibbles(O.pack_nibbles(u), K), u)
+
+
+# --------------------------------------------------------------------------
+# invariants of quantize (|w - dq| <= s/2 up to fp32 rounding)
+# --------------------------------------------------------------------------
+BOUND = 0.5 + 2.0 ** -19   # half a step plus fp32 rounding of w/s and of v*s
+
+
+def _check_invariants(w, G, mode, g_idx=None):
+    N, K = w.shape
+    codes, s, z = O.quantize_pack(w, G, mode, g_idx)
+    O.validate_packed(codes, s, z, K, G, mode, g_idx)
+    gid = O.group_of_columns(K, G, g_idx)
+    u = O.unpack_nibbles(codes, K)
+    v = O.decode(u, mode, z, gid)
+    d = O.dequantize(codes, s, z, g_idx, K, G, mode, "f32")
+    sk = s[:, gid]
+    err = np.abs(w.astype(np.float64) - d.astype(np.float64))
+    assert np.all(err <= BOUND * sk.astype(np.float64))
+    if mode == O.SYM:
+        assert v.min() >= -7 and v.max() <= 7
+        for g in np.unique(gid):
+            cols = gid == g
+            nz = np.any(w[:, cols] != 0, axis=1)
+            assert np.all(np.max(np.abs(v[:, cols]), axis=1)[nz] == 7)
+    else:
+        assert u.max() <= 15 and z.max() <= 15
+        # the zero-point code dequantizes to exactly 0
+        assert np.all(d[u == z[:, gid]] == 0)
+    return codes, s, z
+
+
+@pytest.mark.parametrize("mode", [O.SYM, O.ASYM])
+@pytest.mark.parametrize("K,G", [(512, 32), (8191 % 700, 32), (384, 128), (100, 64), (33, 8)])
+def test_quantize_invariants(mode, K, G):
+    rng = np.random.default_rng(K * 7 + G)
+    w = (rng.standard_normal((24, K)) * 0.02).astype(F32)
+    w[3] = 0                                       # all-zero row
+    w[4, :G] = np.abs(w[4, :G])                    # one-signed groups
+    w[5, :G] = -np.abs(w[5, :G])
+    w[6, ::5] *= 8                                 # outliers
+    _check_invariants(w, G, mode)
+
+
+def test_quantize_invariants_workload_tiny():
+    wl = workload("tiny")
+    t = generate(wl)
+    _check_invariants(t["w"].numpy(), wl.G, wl.mode)
+
+
+def test_quantize_invariants_prefill_like_act_order():
+    wl = workload("prefill", N=64, K=512, M=4)
+    t = generate(wl)
+    _check_invariants(t["w"].numpy(), wl.G, wl.mode, t["g_idx"].numpy())
+
+
+def test_asym_recovers_group_extremes():
+    rng = np.random.default_rng(5)
+    w = (rng.standard_normal((16, 256)) * 0.02).astype(F32)
+    codes, s, z = O.quantize_pack(w, 64, O.ASYM)
+    d = O.dequantize(codes, s, z, None, 256, 64, O.ASYM, "f32").reshape(16, 4, 64)
+    wg = w.reshape(16, 4, 64)
+    tol = BOUND * s[:, :, None]
+    assert np.all(np.abs(d.max(-1, keepdims=True) - wg.max(-1, keepdims=True)) <= tol)
+    assert np.all(np.abs(d.min(-1, keepdims=True) - wg.min(-1, keepdims=True)) <= tol)
+
+
+# --------------------------------------------------------------------------
+# special cases
+# --------------------------------------------------------------------------
+def test_per_channel_matches_gemma_uniform_quantize():
+    """G = K reduces to per-channel symmetric absmax.  The Gemma page computes
+    codes as clip(round(x * (7 / max|x|)), -8, 7), an inverse-scale multiply
+    instead of a divide; the two agree except for +-1 at near-ties."""
+    rng = np.random.default_rng(11)
+    K = 1024
+    w = (rng.standard_normal((512, K)) * 0.02).astype(F32)
+    q, s, _ = O.quantize(w, K, O.SYM)
+    inv = (F32(7) * (F32(1) / np.max(np.abs(w), axis=1))).astype(F32)
+    qg = np.clip(np.rint((w * inv[:, None]).astype(F32)), -8, 7)
+    diff = q.astype(np.int32) - qg.astype(np.int32)
+    assert np.all(np.abs(diff) <= 1)
+    assert np.mean(diff != 0) < 1e-4
+    # every disagreement sits at a near-tie of the exact quotient
+    xs = w.astype(np.float64) / s.astype(np.float64)
+    frac = np.abs(np.abs(xs - np.floor(xs)) - 0.5)
+    assert np.all(frac[diff != 0] < 1e-5)
+    # the scale is max|w| / 7 to within one fp32 rounding
+    np.testing.assert_allclose(s[:, 0], np.max(np.abs(w), axis=1) / 7.0, rtol=2 ** -23)
+
+
+@pytest.mark.parametrize("mode", [O.SYM, O.ASYM])
+def test_default_g_idx_equals_contiguous(mode):
+    rng = np.random.default_rng(3)
+    K, G = 300, 32
+    w = (rng.standard_normal((20, K)) * 0.02).astype(F32)
+    a = O.quantize_pack(w, G, mode)
+    b = O.quantize_pack(w, G, mode, (np.arange(K) // G).astype(np.int32))
+    for x, y in zip(a, b):
+        assert (x is None and y is None) or np.array_equal(x, y)
+
+
+@pytest.mark.parametrize("mode", [O.SYM, O.ASYM])
+def test_g_idx_is_column_permutation(mode):
+    """With every group holding exactly G columns, quantizing with g_idx equals
+    quantizing the column-sorted matrix with contiguous groups."""
+    rng = np.random.default_rng(4)
+    K, G = 256, 32
+    w = (rng.standard_normal((16, K)) * 0.02).astype(F32)
+    g_idx = (rng.permutation(K) // G).astype(np.int32)
+    P = np.argsort(g_idx, kind="stable")
+    q1, s1, z1 = O.quantize(w, G, mode, g_idx)
+    q2, s2, z2 = O.quantize(w[:, P], G, mode)
+    assert np.array_equal(q1[:, P], q2) and np.array_equal(s1, s2)
+    if mode == O.ASYM:
+        assert np.array_equal(z1, z2)
+    d1 = O.dequantize(O.pack_nibbles(q1), s1, z1, g_idx, K, G, mode, "bf16")
+    d2 = O.dequantize(O.pack_nibbles(q2), s2, z2, None, K, G, mode, "bf16")
+    assert np.array_equal(d1[:, P], d2)
+
+
+def test_dequant_bf16_is_rounded_f32():
+    rng = np.random.default_rng(6)
+    w = (rng.standard_normal((8, 200)) * 0.02).astype(F32)
+    c, s, z = O.quantize_pack(w, 32, O.ASYM)
+    f = O.dequantize(c, s, z, None, 200, 32, O.ASYM, "f32")
+    b = O.dequantize(c, s, z, None, 200, 32, O.ASYM, "bf16")
+    ref = torch.from_numpy(f.copy()).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(b, ref)
+    # fp32 product of a small integer and the scale, checked in fp64
+    v = O.decode(O.unpack_nibbles(c, 200), O.ASYM, z, np.arange(200) // 32)
+    exact = v * s[:, np.arange(200) // 32].astype(np.float64)
+    assert np.all(np.abs(f - exact) <= np.abs(exact) * 2.0 ** -24)
+
+
+# --------------------------------------------------------------------------
+# linear
+# --------------------------------------------------------------------------
+def _brute_linear(xf, wd, b):
+    M, K = xf.shape
+    N = wd.shape[0]
+    y = [[0.0] * N for _ in range(M)]
+    for m in range(M):
+        for n in range(N):
+            acc = 0.0
+            for k in range(K):
+                acc += float(xf[m][k]) * float(wd[n][k])
+            y[m][n] = acc + (float(b[n]) if b is not None else 0.0)
+    return np.array(y)
+
+
+@pytest.mark.parametrize("mode,g_act", [(O.SYM, False), (O.ASYM, True)])
+def test_linear_brute_force(mode, g_act):
+    rng = np.random.default_rng(9)
+    M, N, K, G = 3, 5, 37, 8
+    w = (rng.standard_normal((N, K)) * 0.02).astype(F32)
+    g_idx = (rng.permutation(K) % O.n_groups(K, G)).astype(np.int32) if g_act else None
+    codes, s, z = O.quantize_pack(w, G, mode, g_idx)
+    xb = O.f32_to_bf16_bits(rng.standard_normal((M, K)).astype(F32))
+    bb = O.f32_to_bf16_bits((rng.standard_normal(N) * 0.01).astype(F32))
+    y = O.linear(xb, codes, s, z, g_idx, K, G, mode, bb, row_chunk=2)
+    # brute force from the pieces: unpack by hand, decode, scale, round via torch
+    gid = np.arange(K) // G if g_idx is None else g_idx
+    wd = np.zeros((N, K))
+    for n in range(N):
+        for k in range(K):
+            byte = int(codes[n, k // 2])
+            nib = (byte >> 4) if (k & 1) else (byte & 15)
+            if mode == O.SYM:
+                val = nib - 16 if nib >= 8 else nib
+            else:
+                val = nib - int(z[n, gid[k]])
+            prod = np.float32(np.float32(val) * s[n, gid[k]])
+            wd[n, k] = torch.tensor(float(prod), dtype=torch.float32).to(torch.bfloat16).item()
+    xf = torch.from_numpy(xb.view(np.int16).copy()).view(torch.bfloat16).double().numpy()
+    bf = torch.from_numpy(bb.view(np.int16).copy()).view(torch.bfloat16).double().numpy()
+    yb = _brute_linear(xf, wd, bf)
+    np.testing.assert_allclose(y, yb, rtol=1e-12, atol=1e-15)
+
+
+def test_linear_identity_returns_dequantized_weight():
+    rng = np.random.default_rng(12)
+    N, K, G = 9, 40, 8
+    w = (rng.standard_normal((N, K)) * 0.02).astype(F32)
+    codes, s, z = O.quantize_pack(w, G, O.ASYM)
+    eye = O.f32_to_bf16_bits(np.eye(K, dtype=F32))
+    y = O.linear(eye, codes, s, z, None, K, G, O.ASYM)
+    wd = O.bf16_bits_to_f32(O.dequantize(codes, s, z, None, K, G, O.ASYM, "bf16"))
+    assert np.array_equal(y.T, wd.astype(np.float64))
+
+
+def test_workload_inputs_are_seeded_and_shaped():
+    wl = workload("prefill", N=32, K=256, M=8)
+    a, b = generate(wl), generate(wl)
+    assert torch.equal(a["w"], b["w"]) and torch.equal(a["x"], b["x"])
+    g = a["g_idx"].numpy()
+    assert np.array_equal(np.bincount(g), np.full(256 // 128, 128))
+    t = generate(workload("codec", N=4, K=33))
+    assert t["w"].dtype == torch.bfloat16 and t["x"] is None
+    assert bf16_bits(t["w"]).dtype == np.uint16
+
+
+def test_payload_bytes_matches_format():
+    codes = np.zeros((3, 5), np.uint8)
+    scales = np.ones((3, 1), F32)
+    assert O.payload_bytes(codes, scales) == 15 + 12
+    assert O.payload_bytes(codes, scales, np.zeros((3, 1), np.uint8)) == 15 + 12 + 3
+
+
+def test_validate_rejects_malformed():
+    codes = np.zeros((2, 3), np.uint8)
+    s = np.ones((2, 1), F32)
+    O.validate_packed(codes, s, None, 5, 32, O.SYM)
+    bad = codes.copy()
+    bad[1, 2] = 0x10                                   # odd width, high nibble set
+    with pytest.raises(ValueError):
+        O.validate_packed(bad, s, None, 5, 32, O.SYM)
+    with pytest.raises(ValueError):
+        O.validate_packed(codes, np.zeros((2, 1), F32), None, 5, 32, O.SYM)
+    with pytest.raises(ValueError):
+        O.validate_packed(codes, np.full((2, 1), np.inf, F32), None, 5, 32, O.SYM)
+    with pytest.raises(ValueError):
+        O.validate_packed(codes, s, np.full((2, 1), 16, np.uint8), 5, 32, O.ASYM)
+    with pytest.raises(ValueError):
+        O.validate_packed(codes, s, None, 5, 32, O.SYM, g_idx=np.array([0, 0, 1, 0, 0]))
