@@ -1,0 +1,285 @@
+"""Benchmark of the W4A16 group-wise int4 hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-secondary]
+
+A step is one w4_linear call on the decode workload (x bf16 [1, 4096],
+W [14336, 4096] zero-point int4, G = 128, bf16 bias).  Steps run as HIP-graph
+replays that rotate over enough weight copies to overflow the 256 MB
+Infinity Cache, so each call streams its weights from HBM as it would in a
+model with many layers.  The JSON line reports whole-job HBM GB/s of the
+algorithmic bytes, the decode kernel's roofline (its average launch duration
+measured with HIP events on the launch stream), and the CPU oracle on a
+bounded sample.  Secondary entries cover the prefill GEMM (TFLOP/s), the
+batched decode and the codec round trip.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+BF16_MFMA_PEAK_TFS = 2516.6    # MI355X dense bf16 matrix cores
+MALL_BYTES = 256 << 20         # Infinity Cache
+
+
+def algorithmic_bytes_linear(M, N, K, G, asym, bias):
+    NG = -(-K // G)
+    b = N * ((K + 1) // 2) + 4 * N * NG + M * K * 2 + M * N * 2
+    if asym:
+        b += N * NG
+    if bias:
+        b += 2 * N
+    return b
+
+
+def codec_bytes(N, K, G, w_bytes):
+    NG = -(-K // G)
+    packed = N * ((K + 1) // 2) + 4 * N * NG
+    return N * K * w_bytes + packed, packed + N * K * 2   # quantize_pack, dequantize (bf16 out)
+
+
+class Rotation:
+    """B independent copies of the packed weight, enough to exceed twice the
+    Infinity Cache, used round-robin by consecutive calls."""
+
+    def __init__(self, tensors, min_bytes):
+        per = sum(t.numel() * t.element_size() for t in tensors if t is not None)
+        self.count = max(2, math.ceil(min_bytes / per))
+        self.sets = [tuple(None if t is None else t.clone() for t in tensors) for _ in range(self.count)]
+        self.bytes_per_set = per
+
+
+def time_graph(call, n_calls, steps, warmup, rot_count):
+    """Capture `n_calls` calls (call(i) uses rotation set i % rot_count) in one
+    graph; replay it so that exactly `warmup` then `steps` calls run.  Returns
+    milliseconds of the timed region measured by events on the replay stream
+    and by the host clock."""
+    g = torch.cuda.CUDAGraph()
+    cap = torch.cuda.Stream()
+    with torch.cuda.stream(cap):
+        call(0)                                  # eager warm call (loads code objects)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g, stream=cap):
+        for i in range(n_calls):
+            call(i % rot_count)
+    tail = None
+    if steps % n_calls:
+        tail = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(tail, stream=cap):
+            for i in range(steps % n_calls):
+                call(i % rot_count)
+    for _ in range(max(1, -(-warmup // n_calls))):
+        g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record()
+    for _ in range(steps // n_calls):
+        g.replay()
+    if tail is not None:
+        tail.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    return e0.elapsed_time(e1), (t1 - t0) * 1e3
+
+
+def bench_decode(w4, steps, warmup):
+    from int4_group_wise_amd.workloads import workload, generate
+    wl = workload("decode")
+    t = generate(wl)
+    dev = "cuda:0"
+    codes, scales, zeros = w4.quantize_pack(t["w"].to(dev), wl.G, wl.mode)
+    x = t["x"].to(dev)
+    bias = t["bias"].to(dev)
+    rot = Rotation([codes, scales, zeros, bias], 2 * MALL_BYTES)
+    ys = [torch.empty(wl.M, wl.N, dtype=torch.bfloat16, device=dev) for _ in range(rot.count)]
+    del codes, scales, zeros
+
+    def call(i):
+        c, s, z, b = rot.sets[i]
+        w4.linear(x, c, s, z, None, wl.K, wl.G, wl.mode, b, out=ys[i])
+
+    n_calls = rot.count * max(1, 128 // rot.count)
+    ev_ms, host_ms = time_graph(call, n_calls, steps, warmup, rot.count)
+    nbytes = algorithmic_bytes_linear(wl.M, wl.N, wl.K, wl.G, True, True)
+    return wl, nbytes, ev_ms, host_ms, rot
+
+
+def bench_secondary(w4):
+    """Prefill GEMM, batched decode and codec round trip, each timed the same way."""
+    from int4_group_wise_amd.workloads import workload, generate
+    dev = "cuda:0"
+    out = {}
+
+    # prefill: M = 2048, act-order zero-point weights
+    wl = workload("prefill")
+    t = generate(wl)
+    gi = t["g_idx"].to(dev)
+    c, s, z = w4.quantize_pack(t["w"].to(dev), wl.G, wl.mode, gi)
+    x = t["x"].to(dev)
+    y = torch.empty(wl.M, wl.N, dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(w4.linear_workspace_bytes(wl.M, wl.N, wl.K, wl.G, wl.mode, True), dtype=torch.uint8, device=dev)
+    steps = 200
+    ev_ms, host_ms = time_graph(lambda i: w4.linear(x, c, s, z, gi, wl.K, wl.G, wl.mode, None, out=y, workspace=ws),
+                                20, steps, 20, 1)
+    flops = 2.0 * wl.M * wl.N * wl.K
+    tfs = flops * steps / (ev_ms * 1e-3) / 1e12
+    out["prefill_gemm"] = {"metric": "W4A16 linear TFLOP/s M=2048", "value": round(tfs, 2), "unit": "TFLOP/s",
+                           "us_per_call": round(ev_ms * 1e3 / steps, 2),
+                           "roofline": {"bound": "mfma", "achieved": round(tfs, 2), "peak": BF16_MFMA_PEAK_TFS,
+                                        "unit": "TFLOP/s", "frac": round(tfs / BF16_MFMA_PEAK_TFS, 4)},
+                           "config": {"workload": "prefill", "M": wl.M, "N": wl.N, "K": wl.K, "G": wl.G,
+                                      "mode": wl.mode, "act_order": True}}
+    del c, s, z, x, y, ws, t, gi
+
+    # batched decode: M = 16
+    wl = workload("batched_decode")
+    t = generate(wl)
+    c, s, z = w4.quantize_pack(t["w"].to(dev), wl.G, wl.mode)
+    del t["w"]
+    x = t["x"].to(dev)
+    rot = Rotation([c, s], 2 * MALL_BYTES)
+    del c, s
+    y = torch.empty(wl.M, wl.N, dtype=torch.bfloat16, device=dev)
+    steps = 100
+
+    def call_b(i):
+        cc, ss = rot.sets[i]
+        w4.linear(x, cc, ss, None, None, wl.K, wl.G, wl.mode, None, out=y)
+
+    ev_ms, _ = time_graph(call_b, rot.count * 5, steps, rot.count, rot.count)
+    nb = algorithmic_bytes_linear(wl.M, wl.N, wl.K, wl.G, False, False)
+    gbs = nb * steps / (ev_ms * 1e-3) / 1e9
+    out["batched_decode"] = {"metric": "W4A16 linear HBM GB/s M=16", "value": round(gbs, 1), "unit": "GB/s",
+                             "us_per_call": round(ev_ms * 1e3 / steps, 2),
+                             "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
+                                          "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4)},
+                             "config": {"workload": "batched_decode", "M": wl.M, "N": wl.N, "K": wl.K,
+                                        "G": wl.G, "mode": wl.mode}}
+    del rot, x, y
+
+    # codec: bf16 W [28672, 8191] -> quantize_pack -> dequantize (bf16)
+    wl = workload("codec")
+    t = generate(wl)
+    w = t["w"].to(dev)
+    del t
+    c, s, _ = w4.quantize_pack(w, wl.G, wl.mode)
+    d = torch.empty(wl.N, wl.K, dtype=torch.bfloat16, device=dev)
+    steps = 20
+    c2, s2 = torch.empty_like(c), torch.empty_like(s)
+    ev_q, _ = time_graph(lambda i: w4.quantize_pack(w, wl.G, wl.mode, out=(c2, s2, None)), 5, steps, 5, 1)
+    ev_d, _ = time_graph(lambda i: w4.dequantize(c, s, None, None, wl.K, wl.G, wl.mode, out=d), 5, steps, 5, 1)
+    qb, db = codec_bytes(wl.N, wl.K, wl.G, 2)
+    gq = qb * steps / (ev_q * 1e-3) / 1e9
+    gd = db * steps / (ev_d * 1e-3) / 1e9
+    out["codec"] = {"metric": "codec HBM GB/s (quantize_pack + dequantize)",
+                    "value": round((qb + db) * steps / ((ev_q + ev_d) * 1e-3) / 1e9, 1), "unit": "GB/s",
+                    "quantize_pack": {"GB/s": round(gq, 1), "us": round(ev_q * 1e3 / steps, 1), "frac": round(gq / HBM_PEAK_GBS, 4)},
+                    "dequantize": {"GB/s": round(gd, 1), "us": round(ev_d * 1e3 / steps, 1), "frac": round(gd / HBM_PEAK_GBS, 4)},
+                    "config": {"workload": "codec", "N": wl.N, "K": wl.K, "G": wl.G, "mode": wl.mode, "w_dtype": "bf16"}}
+    return out
+
+
+def cpu_baseline(seconds=12.0):
+    """The oracle, untuned, on a bounded sample of the decode workload: the
+    linear (dequantize to bf16 + fp64 matmul) over the first rows of W,
+    repeated until `seconds` have passed.  One BLAS thread."""
+    from oracle import w4_oracle as O
+    from int4_group_wise_amd.workloads import workload, generate, bf16_bits
+    try:
+        from threadpoolctl import threadpool_limits
+    except ImportError:                                    # pragma: no cover
+        threadpool_limits = None
+    wl = workload("decode")
+    t = generate(wl)
+    rows = 1024
+    wr = t["w"][:rows].numpy()
+    codes, sc, z = O.quantize_pack(wr, wl.G, O.ASYM)
+    xb = bf16_bits(t["x"])
+    bb = bf16_bits(t["bias"])[:rows]
+    ctx = threadpool_limits(limits=1) if threadpool_limits else None
+    n = 0
+    t0 = time.perf_counter()
+    try:
+        if ctx:
+            ctx.__enter__()
+        while True:
+            O.linear(xb, codes, sc, z, None, wl.K, wl.G, O.ASYM, bb)
+            n += 1
+            if time.perf_counter() - t0 >= seconds:
+                break
+    finally:
+        if ctx:
+            ctx.__exit__(None, None, None)
+    el = time.perf_counter() - t0
+    per_row = algorithmic_bytes_linear(wl.M, wl.N, wl.K, wl.G, True, True) / wl.N
+    gbs = per_row * rows * n / el / 1e9
+    return {"value": round(gbs, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"oracle linear (dequantize to bf16, fp64 matmul, bias) on the first {rows} of "
+                      f"{wl.N} weight rows of the decode workload, {n} repetitions in {el:.1f} s, "
+                      f"bytes scaled per row"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20000)
+    ap.add_argument("--warmup", type=int, default=1000)
+    ap.add_argument("--no-secondary", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (run with --gpus 1)",
+              file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    torch.cuda.set_device(0)
+    from int4_group_wise_amd import w4
+    w4.load()
+
+    wl, nbytes, ev_ms, host_ms, rot = bench_decode(w4, args.steps, args.warmup)
+    us_per = ev_ms * 1e3 / args.steps
+    gbs = nbytes * args.steps / (ev_ms * 1e-3) / 1e9
+    line = {
+        "metric": "W4A16 linear: GEMV HBM GB/s (%peak) M=1; GEMM TFLOPS (%MFMA peak) M=2048",
+        "value": round(gbs, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ev_ms / args.steps, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "decode", "M": wl.M, "N": wl.N, "K": wl.K, "G": wl.G, "mode": wl.mode,
+                   "bias": True, "weight_copies_rotated": rot.count,
+                   "rotated_bytes": rot.count * rot.bytes_per_set,
+                   "algorithmic_bytes_per_step": nbytes, "host_ms": round(host_ms, 3)},
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "gemv_dot2_kernel<1, true>", "us_per_launch": round(us_per, 3)},
+    }
+    del rot
+    torch.cuda.empty_cache()
+    if not args.no_secondary:
+        line["secondary"] = bench_secondary(w4)
+        torch.cuda.empty_cache()
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline()
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

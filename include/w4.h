@@ -1,0 +1,147 @@
+/*
+ * w4.h — C ABI of libw4.so: group-wise 4-bit weight-only quantization and the
+ * W4A16 linear  y = x . dequant(W)^T + b  on AMD MI355X (gfx950).
+ *
+ * Data format (shared by every entry point)
+ * -----------------------------------------
+ *   W       [N, K]  the dense weight (N output features, K input features).
+ *   codes   uint8 [N, ceil(K/2)], row-major.  Two 4-bit codes per byte along a
+ *           row: column 2j in the low nibble of byte j, column 2j+1 in the high
+ *           nibble; when K is odd the unused high nibble of each row's last
+ *           byte is 0.  (LoopQ packed_weight.py page: pack_weight, validate,
+ *           nibble order 'even_column_low'.)
+ *   scales  fp32 [N, ceil(K/G)], row-major: one multiplicative scale per row
+ *           and group (same page: _dequantize_validated multiplies).
+ *   zeros   uint8 [N, ceil(K/G)] zero-points 0..15, one per byte (W4_ASYM
+ *           only; the keras dense.py diff page stores a kernel_zero per group).
+ *   g_idx   int32 [K] group of each input column, values in [0, ceil(K/G));
+ *           NULL means column k belongs to group k / G (keras dense.py diff
+ *           page: _int4_build g_idx initializer; MAX quantization.py page:
+ *           desc_act, activation order).
+ *
+ * Code modes
+ *   W4_SYM   signed two's-complement nibbles: nibble c means c - 16 when c >= 8
+ *            (LoopQ page, _dequantize_validated).  The quantizer emits
+ *            [-7, 7]: scale = max|w| / 7 over the group.  Decoding accepts -8.
+ *   W4_ASYM  unsigned nibbles with a per-group zero-point z: value = c - z.
+ *            Quantizer: lo = min(0, min w), hi = max(0, max w),
+ *            s = (hi - lo) / 15, z = clamp(rint(-lo / s), 0, 15),
+ *            c = clamp(rint(w / s) + z, 0, 15).
+ *   Both: a group whose computed scale is 0 gets scale 1.  Divisions are IEEE
+ *   fp32 round-to-nearest, rint rounds half to even.
+ *
+ * Conventions for every call
+ *   - Pointers are device pointers (hipMalloc / PyTorch-ROCm allocations) on
+ *     the current device, owned by the caller, dense row-major, 16-byte aligned
+ *     base addresses.  The library keeps no reference after returning.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *     Calls only enqueue work on it and return; they never synchronize.
+ *   - Arguments are checked on the host before any launch.  On failure the
+ *     call returns a non-zero status, writes nothing, and w4_last_error()
+ *     describes the problem.  No C++ exception crosses this boundary.
+ *   - Not checked (the caller's responsibility, as the LoopQ page's owner
+ *     validates before use): finite weights, g_idx values in range, zeros
+ *     <= 15, finite positive scales, a 0 pad nibble.  Violations give
+ *     unspecified values but every access stays in bounds.
+ */
+#ifndef W4_H
+#define W4_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define W4_ABI_VERSION 1
+
+typedef enum {
+  W4_OK = 0,
+  W4_ERR_INVALID_ARG = 1,  /* bad size, null pointer, misaligned pointer, mode */
+  W4_ERR_UNSUPPORTED = 2,  /* valid request this build does not implement   */
+  W4_ERR_HIP = 3           /* a HIP runtime call or kernel launch failed     */
+} w4_status;
+
+typedef enum { W4_F32 = 0, W4_BF16 = 1 } w4_dtype;
+typedef enum { W4_SYM = 0, W4_ASYM = 1 } w4_mode;
+
+/* Version of this ABI (W4_ABI_VERSION). */
+int w4_abi_version(void);
+
+/* Static text for a status code. */
+const char* w4_status_string(int status);
+
+/* Detail of the last failed call on this host thread ("" if none). */
+const char* w4_last_error(void);
+
+/*
+ * w4_quantize_pack — quantize W group-wise and pack the codes.
+ *   (LoopQ packed_weight.py page: pack_weight; keras dense.py diff page:
+ *    Dense.quantize, int4 branch with block_size.)
+ *   w        [N, K] weights, fp32 (w_dtype = W4_F32) or bf16 (W4_BF16).
+ *   N, K     >= 1 (an empty matrix is rejected, as pack_weight rejects it).
+ *   G        group size, 8 <= G <= 4096 and G % 8 == 0.
+ *   mode     W4_SYM or W4_ASYM.
+ *   g_idx    int32 [K] or NULL (contiguous groups).  Group statistics run over
+ *            the columns mapped to each group; a group no column maps to gets
+ *            scale 1 (and zero-point 0).
+ *   codes    out uint8 [N, ceil(K/2)].
+ *   scales   out fp32  [N, ceil(K/G)].
+ *   zeros    out uint8 [N, ceil(K/G)] for W4_ASYM; must be NULL for W4_SYM.
+ * Outputs are bit-exact functions of the inputs (no atomics on values).
+ */
+w4_status w4_quantize_pack(const void* w, int w_dtype, int64_t N, int64_t K,
+                           int64_t G, int mode, const int32_t* g_idx,
+                           uint8_t* codes, float* scales, uint8_t* zeros,
+                           void* stream);
+
+/*
+ * w4_dequantize — dense weight from packed codes.
+ *   (LoopQ packed_weight.py page: _dequantize_validated; keras dense.py diff
+ *    page: dequantize with scale/zero map and g_idx; PaddleNLP
+ *    quantization_linear.py page: weight_dequantize.)
+ *   out[n, k] = fp32(value(n, k)) * scales[n, gid(k)]   (one fp32 multiply),
+ *   stored as fp32 (out_dtype = W4_F32) or rounded to nearest-even bf16
+ *   (W4_BF16).  Arguments as in w4_quantize_pack; out is [N, K].
+ */
+w4_status w4_dequantize(const uint8_t* codes, const float* scales,
+                        const uint8_t* zeros, const int32_t* g_idx,
+                        int64_t N, int64_t K, int64_t G, int mode,
+                        void* out, int out_dtype, void* stream);
+
+/*
+ * w4_linear_workspace_bytes — device scratch w4_linear needs for this shape
+ * (0 when none).  The prefill path (M > 16) stages the bf16 dequantized weight
+ * [N, K] there.
+ */
+size_t w4_linear_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t G,
+                                 int mode, int has_g_idx);
+
+/*
+ * w4_linear — W4A16 linear  y[m, n] = sum_k x[m, k] * Wd[n, k] + bias[n].
+ *   (keras dense.py diff page: Dense._int4_call, sub-channel branch, then the
+ *    bias add; PaddleNLP quantization_linear.py page: weight_only_linear with
+ *    group_size.)
+ *   x        bf16 [M, K] activations (not quantized: weight-only, A16).
+ *   M        >= 0 (M = 0 returns W4_OK and launches nothing).
+ *   codes, scales, zeros, g_idx, N, K, G, mode  as in w4_dequantize.
+ *   bias     bf16 [N] or NULL.
+ *   y        out bf16 [M, N]; products accumulate in fp32, the bias is added
+ *            in fp32, one rounding to bf16 at the end.
+ *   workspace, workspace_bytes  device scratch of at least
+ *            w4_linear_workspace_bytes(...) bytes (may be NULL when that is 0).
+ * Results are deterministic: the same inputs give the same bits.
+ */
+w4_status w4_linear(const void* x, int64_t M,
+                    const uint8_t* codes, const float* scales,
+                    const uint8_t* zeros, const int32_t* g_idx,
+                    int64_t N, int64_t K, int64_t G, int mode,
+                    const void* bias, void* y,
+                    void* workspace, size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* W4_H */

@@ -1,0 +1,139 @@
+// C ABI of libw4.so (declared in include/w4.h): host-side argument checks and
+// dispatch to the gfx950 kernels.  Nothing here allocates device memory.
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "w4.h"
+#include "w4_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+w4_status fail(w4_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+w4_status hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return W4_OK;
+  return fail(W4_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+constexpr int64_t kMaxDim = int64_t(1) << 30;       // per-dimension limit (32-bit index math)
+constexpr int64_t kMaxGrid = (int64_t(1) << 31) - 1;
+
+// Checks shared by the three compute entry points.
+w4_status check_format(int64_t N, int64_t K, int64_t G, int mode, const void* zeros,
+                       const void* g_idx, const char* fn) {
+  if (N < 1 || K < 1) return fail(W4_ERR_INVALID_ARG, "%s: N and K must be >= 1 (got N=%lld K=%lld)", fn, (long long)N, (long long)K);
+  if (N > kMaxDim || K > kMaxDim) return fail(W4_ERR_UNSUPPORTED, "%s: N and K must be <= 2^30", fn);
+  if (G < 8 || G > 4096 || G % 8 != 0)
+    return fail(W4_ERR_INVALID_ARG, "%s: group size G must be a multiple of 8 in [8, 4096] (got %lld)", fn, (long long)G);
+  if (mode != W4_SYM && mode != W4_ASYM) return fail(W4_ERR_INVALID_ARG, "%s: mode must be W4_SYM or W4_ASYM", fn);
+  if (mode == W4_ASYM && zeros == nullptr) return fail(W4_ERR_INVALID_ARG, "%s: W4_ASYM needs zero-points", fn);
+  if (mode == W4_SYM && zeros != nullptr) return fail(W4_ERR_INVALID_ARG, "%s: W4_SYM takes no zero-points (pass NULL)", fn);
+  if (zeros && !aligned16(zeros)) return fail(W4_ERR_INVALID_ARG, "%s: zeros must be 16-byte aligned", fn);
+  if (g_idx && !aligned16(g_idx)) return fail(W4_ERR_INVALID_ARG, "%s: g_idx must be 16-byte aligned", fn);
+  return W4_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int w4_abi_version(void) { return W4_ABI_VERSION; }
+
+const char* w4_status_string(int status) {
+  switch (status) {
+    case W4_OK: return "ok";
+    case W4_ERR_INVALID_ARG: return "invalid argument";
+    case W4_ERR_UNSUPPORTED: return "unsupported";
+    case W4_ERR_HIP: return "HIP error";
+    default: return "unknown status";
+  }
+}
+
+const char* w4_last_error(void) { return g_last_error.c_str(); }
+
+w4_status w4_quantize_pack(const void* w, int w_dtype, int64_t N, int64_t K, int64_t G, int mode,
+                           const int32_t* g_idx, uint8_t* codes, float* scales, uint8_t* zeros,
+                           void* stream) {
+  g_last_error.clear();
+  const char* fn = "w4_quantize_pack";
+  if (w4_status st = check_format(N, K, G, mode, zeros, g_idx, fn)) return st;
+  if (w_dtype != W4_F32 && w_dtype != W4_BF16) return fail(W4_ERR_INVALID_ARG, "%s: w_dtype must be W4_F32 or W4_BF16", fn);
+  if (!w || !codes || !scales) return fail(W4_ERR_INVALID_ARG, "%s: w, codes and scales must be non-NULL", fn);
+  if (!aligned16(w) || !aligned16(codes) || !aligned16(scales))
+    return fail(W4_ERR_INVALID_ARG, "%s: w, codes and scales must be 16-byte aligned", fn);
+  const int64_t NG = (K + G - 1) / G;
+  if (NG > w4::kMaxGroupsPerRow)
+    return fail(W4_ERR_UNSUPPORTED, "%s: at most %lld groups per row (got %lld)", fn, (long long)w4::kMaxGroupsPerRow, (long long)NG);
+  if (N > kMaxGrid) return fail(W4_ERR_UNSUPPORTED, "%s: too many rows", fn);
+  w4::QuantArgs a{w, w_dtype == W4_BF16, N, K, G, NG, mode == W4_ASYM, g_idx, codes, scales, zeros};
+  return hip_status(w4::launch_quantize_pack(a, static_cast<hipStream_t>(stream)), fn);
+}
+
+w4_status w4_dequantize(const uint8_t* codes, const float* scales, const uint8_t* zeros,
+                        const int32_t* g_idx, int64_t N, int64_t K, int64_t G, int mode,
+                        void* out, int out_dtype, void* stream) {
+  g_last_error.clear();
+  const char* fn = "w4_dequantize";
+  if (w4_status st = check_format(N, K, G, mode, zeros, g_idx, fn)) return st;
+  if (out_dtype != W4_F32 && out_dtype != W4_BF16) return fail(W4_ERR_INVALID_ARG, "%s: out_dtype must be W4_F32 or W4_BF16", fn);
+  if (!codes || !scales || !out) return fail(W4_ERR_INVALID_ARG, "%s: codes, scales and out must be non-NULL", fn);
+  if (!aligned16(codes) || !aligned16(scales) || !aligned16(out))
+    return fail(W4_ERR_INVALID_ARG, "%s: codes, scales and out must be 16-byte aligned", fn);
+  const int64_t NG = (K + G - 1) / G;
+  const int64_t chunk_blocks = ((K + 7) / 8 + 255) / 256;
+  if (N * chunk_blocks > kMaxGrid) return fail(W4_ERR_UNSUPPORTED, "%s: matrix too large for one launch", fn);
+  w4::DequantArgs a{codes, scales, zeros, g_idx, N, K, G, NG, mode == W4_ASYM, out, out_dtype == W4_BF16};
+  return hip_status(w4::launch_dequantize(a, static_cast<hipStream_t>(stream)), fn);
+}
+
+size_t w4_linear_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t G, int mode, int has_g_idx) {
+  (void)G; (void)mode; (void)has_g_idx;
+  if (M <= 16 || N < 1 || K < 1) return 0;
+  return static_cast<size_t>(N) * static_cast<size_t>(K) * 2u;   // bf16 dequantized weight
+}
+
+w4_status w4_linear(const void* x, int64_t M, const uint8_t* codes, const float* scales,
+                    const uint8_t* zeros, const int32_t* g_idx, int64_t N, int64_t K, int64_t G,
+                    int mode, const void* bias, void* y, void* workspace, size_t workspace_bytes,
+                    void* stream) {
+  g_last_error.clear();
+  const char* fn = "w4_linear";
+  if (w4_status st = check_format(N, K, G, mode, zeros, g_idx, fn)) return st;
+  if (M < 0) return fail(W4_ERR_INVALID_ARG, "%s: M must be >= 0", fn);
+  if (M > kMaxDim) return fail(W4_ERR_UNSUPPORTED, "%s: M must be <= 2^30", fn);
+  if (M == 0) return W4_OK;
+  if (!x || !codes || !scales || !y) return fail(W4_ERR_INVALID_ARG, "%s: x, codes, scales and y must be non-NULL", fn);
+  if (!aligned16(x) || !aligned16(codes) || !aligned16(scales) || !aligned16(y) || (bias && !aligned16(bias)))
+    return fail(W4_ERR_INVALID_ARG, "%s: x, codes, scales, bias and y must be 16-byte aligned", fn);
+  const int64_t NG = (K + G - 1) / G;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  w4::LinearArgs a{static_cast<const uint16_t*>(x), M, codes, scales, zeros, g_idx, N, K, G, NG,
+                   mode == W4_ASYM, static_cast<const uint16_t*>(bias), static_cast<uint16_t*>(y)};
+  if (w4::skinny_supported(a)) return hip_status(w4::launch_linear_skinny(a, s), fn);
+  const size_t need = w4_linear_workspace_bytes(M, N, K, G, mode, g_idx != nullptr);
+  if (workspace_bytes < need || (need && !workspace))
+    return fail(W4_ERR_INVALID_ARG, "%s: workspace of %zu bytes needed (got %zu)", fn, need, workspace_bytes);
+  if (!aligned16(workspace)) return fail(W4_ERR_INVALID_ARG, "%s: workspace must be 16-byte aligned", fn);
+  const int64_t chunk_blocks = ((K + 7) / 8 + 255) / 256;
+  const int64_t gemm_blocks = K % 8 == 0 ? ((M + 127) / 128) * ((N + 127) / 128) : (M * N + 255) / 256;
+  if (N * chunk_blocks > kMaxGrid || gemm_blocks > kMaxGrid)
+    return fail(W4_ERR_UNSUPPORTED, "%s: matrix too large for one launch", fn);
+  w4::DequantArgs d{codes, scales, zeros, g_idx, N, K, G, NG, mode == W4_ASYM, workspace, 1};
+  if (w4_status st = hip_status(w4::launch_dequantize(d, s), fn)) return st;
+  return hip_status(w4::launch_gemm_bf16(a.x, static_cast<const uint16_t*>(workspace), a.bias, a.y, M, N, K, s), fn);
+}
+
+}  // extern "C"

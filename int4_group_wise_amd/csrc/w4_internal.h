@@ -1,0 +1,62 @@
+// Host-side launchers shared between the libw4 translation units.  Arguments
+// are validated by the C-ABI layer (w4_api.hip) before any of these run.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace w4 {
+
+struct QuantArgs {
+  const void* w;
+  int w_bf16;           // 0: fp32 weights, 1: bf16 weights
+  int64_t N, K, G, NG;
+  int asym;             // 0: signed codes, 1: codes with zero-points
+  const int32_t* g_idx; // NULL: contiguous groups
+  uint8_t* codes;
+  float* scales;
+  uint8_t* zeros;
+};
+
+struct DequantArgs {
+  const uint8_t* codes;
+  const float* scales;
+  const uint8_t* zeros;
+  const int32_t* g_idx;
+  int64_t N, K, G, NG;
+  int asym;
+  void* out;
+  int out_bf16;         // 0: fp32 output, 1: bf16 output
+};
+
+struct LinearArgs {
+  const uint16_t* x;    // bf16 [M, K]
+  int64_t M;
+  const uint8_t* codes;
+  const float* scales;
+  const uint8_t* zeros;
+  const int32_t* g_idx;
+  int64_t N, K, G, NG;
+  int asym;
+  const uint16_t* bias; // bf16 [N] or NULL
+  uint16_t* y;          // bf16 [M, N]
+};
+
+// Largest group count the quantizer's per-row LDS tables hold.
+constexpr int64_t kMaxGroupsPerRow = 4096;
+
+hipError_t launch_quantize_pack(const QuantArgs& a, hipStream_t s);
+hipError_t launch_dequantize(const DequantArgs& a, hipStream_t s);
+
+// Skinny linear (M <= 16).  Returns hipErrorInvalidValue if no skinny kernel
+// covers the request (the caller then takes the prefill path).
+bool skinny_supported(const LinearArgs& a);
+hipError_t launch_linear_skinny(const LinearArgs& a, hipStream_t s);
+
+// Dense bf16 GEMM  y = x . wd^T + bias  (x [M, K], wd [N, K], y [M, N]).
+hipError_t launch_gemm_bf16(const uint16_t* x, const uint16_t* wd,
+                            const uint16_t* bias, uint16_t* y, int64_t M,
+                            int64_t N, int64_t K, hipStream_t s);
+
+}  // namespace w4

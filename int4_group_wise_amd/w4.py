@@ -1,0 +1,189 @@
+"""Thin Python binding of libw4.so (C ABI in include/w4.h).
+
+Argument marshalling only: these functions check tensor dtypes, shapes and
+devices, allocate outputs with torch on the tensors' device, and pass raw
+device pointers plus the current HIP stream to the library.  Every step of the
+computation runs in the library's HIP kernels; there is no fallback.  If the
+library is not built, the first call raises W4Error.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+SYM = 0    # W4_SYM: signed two's-complement nibbles
+ASYM = 1   # W4_ASYM: unsigned nibbles with per-group zero-points
+_F32, _BF16 = 0, 1
+
+_STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported", 3: "HIP error"}
+_LIB = None
+
+
+class W4Error(RuntimeError):
+    """A libw4 call failed (status and the library's message)."""
+
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{_STATUS.get(status, status)}: {message}")
+        self.status = status
+
+
+def library_path() -> str:
+    return os.path.join(os.path.dirname(os.path.abspath(__file__)), "libw4.so")
+
+
+def load() -> ctypes.CDLL:
+    """Load libw4.so once and declare its signatures."""
+    global _LIB
+    if _LIB is not None:
+        return _LIB
+    path = library_path()
+    if not os.path.exists(path):
+        raise W4Error(-1, f"{path} is not built (run: python -m int4_group_wise_amd.build)")
+    lib = ctypes.CDLL(path)
+    P, I64, I32, SZ = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_size_t
+    lib.w4_abi_version.restype = I32
+    lib.w4_abi_version.argtypes = []
+    lib.w4_status_string.restype = ctypes.c_char_p
+    lib.w4_status_string.argtypes = [I32]
+    lib.w4_last_error.restype = ctypes.c_char_p
+    lib.w4_last_error.argtypes = []
+    lib.w4_quantize_pack.restype = I32
+    lib.w4_quantize_pack.argtypes = [P, I32, I64, I64, I64, I32, P, P, P, P, P]
+    lib.w4_dequantize.restype = I32
+    lib.w4_dequantize.argtypes = [P, P, P, P, I64, I64, I64, I32, P, I32, P]
+    lib.w4_linear_workspace_bytes.restype = SZ
+    lib.w4_linear_workspace_bytes.argtypes = [I64, I64, I64, I64, I32, I32]
+    lib.w4_linear.restype = I32
+    lib.w4_linear.argtypes = [P, I64, P, P, P, P, I64, I64, I64, I32, P, P, P, SZ, P]
+    _LIB = lib
+    return lib
+
+
+def _check(lib, status: int) -> None:
+    if status != 0:
+        raise W4Error(status, lib.w4_last_error().decode())
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _dev(t: torch.Tensor, name: str, dtype, shape=None) -> None:
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+
+
+def _mode(mode) -> int:
+    if mode in (SYM, "sym"):
+        return SYM
+    if mode in (ASYM, "asym"):
+        return ASYM
+    raise ValueError("mode must be 'sym' or 'asym'")
+
+
+def _format_args(N, K, G, mode, codes, scales, zeros, g_idx):
+    NG = -(-K // G)
+    _dev(codes, "codes", torch.uint8, (N, (K + 1) // 2))
+    _dev(scales, "scales", torch.float32, (N, NG))
+    if mode == ASYM:
+        if zeros is None:
+            raise ValueError("zero-point mode needs zeros")
+        _dev(zeros, "zeros", torch.uint8, (N, NG))
+    elif zeros is not None:
+        raise ValueError("signed mode takes no zeros")
+    if g_idx is not None:
+        _dev(g_idx, "g_idx", torch.int32, (K,))
+
+
+def quantize_pack(w: torch.Tensor, G: int, mode="sym", g_idx: torch.Tensor | None = None, out=None):
+    """Quantize ``w`` [N, K] (fp32 or bf16, on the GPU) group-wise and pack it.
+    Returns ``(codes uint8 [N, ceil(K/2)], scales fp32 [N, ceil(K/G)],
+    zeros uint8 [N, ceil(K/G)] or None)``; ``out`` may hold that tuple
+    preallocated."""
+    lib = load()
+    mode = _mode(mode)
+    if w.dim() != 2:
+        raise ValueError("w must be a matrix")
+    if w.dtype not in (torch.float32, torch.bfloat16):
+        raise ValueError("w must be float32 or bfloat16")
+    _dev(w, "w", w.dtype)
+    N, K = w.shape
+    NG = -(-K // G) if G > 0 else 0
+    if out is None:
+        codes = torch.empty((N, (K + 1) // 2), dtype=torch.uint8, device=w.device)
+        scales = torch.empty((N, NG), dtype=torch.float32, device=w.device)
+        zeros = torch.empty((N, NG), dtype=torch.uint8, device=w.device) if mode == ASYM else None
+    else:
+        codes, scales, zeros = out
+    if G > 0:
+        _format_args(N, K, G, mode, codes, scales, zeros, None)
+    if g_idx is not None:
+        _dev(g_idx, "g_idx", torch.int32, (K,))
+    _check(lib, lib.w4_quantize_pack(_ptr(w), _BF16 if w.dtype == torch.bfloat16 else _F32,
+                                     N, K, G, mode, _ptr(g_idx), _ptr(codes), _ptr(scales),
+                                     _ptr(zeros), _stream(w.device)))
+    return codes, scales, zeros
+
+
+def dequantize(codes, scales, zeros, g_idx, K: int, G: int, mode="sym",
+               out_dtype=torch.bfloat16, out=None) -> torch.Tensor:
+    """Dense weight [N, K] (bf16 or fp32) from packed codes; ``out`` may be a
+    preallocated [N, K] tensor of ``out_dtype``."""
+    lib = load()
+    mode = _mode(mode)
+    N = codes.shape[0]
+    _format_args(N, K, G, mode, codes, scales, zeros, g_idx)
+    if out_dtype not in (torch.bfloat16, torch.float32):
+        raise ValueError("out_dtype must be bfloat16 or float32")
+    if out is None:
+        out = torch.empty((N, K), dtype=out_dtype, device=codes.device)
+    _dev(out, "out", out_dtype, (N, K))
+    _check(lib, lib.w4_dequantize(_ptr(codes), _ptr(scales), _ptr(zeros), _ptr(g_idx), N, K, G,
+                                  mode, _ptr(out), _BF16 if out_dtype == torch.bfloat16 else _F32,
+                                  _stream(codes.device)))
+    return out
+
+
+def linear_workspace_bytes(M: int, N: int, K: int, G: int, mode="sym", has_g_idx=False) -> int:
+    lib = load()
+    return int(lib.w4_linear_workspace_bytes(M, N, K, G, _mode(mode), int(bool(has_g_idx))))
+
+
+def linear(x, codes, scales, zeros, g_idx, K: int, G: int, mode="sym", bias=None,
+           out=None, workspace=None) -> torch.Tensor:
+    """``y = x . dequant(W)^T + bias`` with x bf16 [M, K]; returns bf16 [M, N].
+    ``out`` (bf16 [M, N]) and ``workspace`` (uint8, at least
+    ``linear_workspace_bytes`` bytes) may be passed in to avoid allocation."""
+    lib = load()
+    mode = _mode(mode)
+    N = codes.shape[0]
+    _format_args(N, K, G, mode, codes, scales, zeros, g_idx)
+    if x.dim() != 2 or x.shape[1] != K:
+        raise ValueError(f"x must be [M, {K}]")
+    _dev(x, "x", torch.bfloat16)
+    M = x.shape[0]
+    if bias is not None:
+        _dev(bias, "bias", torch.bfloat16, (N,))
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
+    _dev(out, "out", torch.bfloat16, (M, N))
+    need = int(lib.w4_linear_workspace_bytes(M, N, K, G, mode, int(g_idx is not None)))
+    if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
+        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib, lib.w4_linear(_ptr(x), M, _ptr(codes), _ptr(scales), _ptr(zeros), _ptr(g_idx),
+                              N, K, G, mode, _ptr(bias), _ptr(out), _ptr(workspace), ws_bytes,
+                              _stream(x.device)))
+    return out

@@ -1,0 +1,107 @@
+"""Host-side checks of the C ABI (no GPU needed): the library loads, exports
+every function include/w4.h declares, and rejects malformed requests on the
+host before any launch, returning a status and a message."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from int4_group_wise_amd import w4
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(w4.library_path()):
+        from int4_group_wise_amd import build
+        build.build()
+    return w4.load()
+
+
+def _declared_functions():
+    text = open(os.path.join(ROOT, "include", "w4.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[A-Za-z_0-9]+\s*\*?\s*(w4_[a-z_0-9]+)\s*\(", text, re.M)))
+
+
+def test_header_declares_the_entry_points():
+    names = _declared_functions()
+    for f in ("w4_quantize_pack", "w4_dequantize", "w4_linear", "w4_linear_workspace_bytes",
+              "w4_abi_version", "w4_status_string", "w4_last_error"):
+        assert f in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in _declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_library_has_gfx950_code_object():
+    data = open(w4.library_path(), "rb").read()
+    assert b"gfx950" in data
+
+
+def test_version_and_status_strings(lib):
+    assert lib.w4_abi_version() == 1
+    assert lib.w4_status_string(0) == b"ok"
+    assert lib.w4_status_string(1) == b"invalid argument"
+    assert lib.w4_status_string(2) == b"unsupported"
+    assert lib.w4_status_string(3) == b"HIP error"
+
+
+FAKE = ctypes.c_void_p(1 << 20)          # aligned, never dereferenced: calls fail before launch
+ODD = ctypes.c_void_p((1 << 20) + 2)
+
+
+@pytest.mark.parametrize("args,status,msg", [
+    # (w, dtype, N, K, G, mode, g_idx, codes, scales, zeros, stream)
+    ((FAKE, 0, 0, 16, 8, 0, None, FAKE, FAKE, None, None), 1, "N and K"),
+    ((FAKE, 0, 4, 0, 8, 0, None, FAKE, FAKE, None, None), 1, "N and K"),
+    ((FAKE, 0, 4, 16, 12, 0, None, FAKE, FAKE, None, None), 1, "group size"),
+    ((FAKE, 0, 4, 16, 0, 0, None, FAKE, FAKE, None, None), 1, "group size"),
+    ((FAKE, 0, 4, 16, 8, 7, None, FAKE, FAKE, None, None), 1, "mode"),
+    ((FAKE, 0, 4, 16, 8, 1, None, FAKE, FAKE, None, None), 1, "zero-points"),
+    ((FAKE, 0, 4, 16, 8, 0, None, FAKE, FAKE, FAKE, None), 1, "no zero-points"),
+    ((FAKE, 5, 4, 16, 8, 0, None, FAKE, FAKE, None, None), 1, "w_dtype"),
+    ((None, 0, 4, 16, 8, 0, None, FAKE, FAKE, None, None), 1, "non-NULL"),
+    ((ODD, 0, 4, 16, 8, 0, None, FAKE, FAKE, None, None), 1, "aligned"),
+    ((FAKE, 0, 4, 1 << 20, 8, 0, None, FAKE, FAKE, None, None), 2, "groups per row"),
+    ((FAKE, 0, 4, (1 << 30) + 1, 8, 0, None, FAKE, FAKE, None, None), 2, "2^30"),
+])
+def test_quantize_pack_rejects(lib, args, status, msg):
+    assert lib.w4_quantize_pack(*args) == status
+    assert msg in lib.w4_last_error().decode()
+
+
+def test_dequantize_rejects(lib):
+    assert lib.w4_dequantize(FAKE, FAKE, None, None, 4, 16, 8, 0, FAKE, 9, None) == 1
+    assert "out_dtype" in lib.w4_last_error().decode()
+    assert lib.w4_dequantize(FAKE, None, None, None, 4, 16, 8, 0, FAKE, 1, None) == 1
+    assert lib.w4_dequantize(FAKE, FAKE, None, ODD, 4, 16, 8, 0, FAKE, 1, None) == 1
+    assert "g_idx" in lib.w4_last_error().decode()
+
+
+def test_linear_rejects_and_workspace(lib):
+    # M = 0 is an empty batch: nothing to do, no launch
+    assert lib.w4_linear(FAKE, 0, FAKE, FAKE, None, None, 4, 16, 8, 0, None, FAKE, None, 0, None) == 0
+    assert lib.w4_last_error() == b""
+    assert lib.w4_linear(FAKE, -1, FAKE, FAKE, None, None, 4, 16, 8, 0, None, FAKE, None, 0, None) == 1
+    assert lib.w4_linear(None, 2, FAKE, FAKE, None, None, 4, 16, 8, 0, None, FAKE, None, 0, None) == 1
+    assert lib.w4_linear(FAKE, 2, FAKE, FAKE, None, None, 4, 16, 8, 0, ODD, FAKE, None, 0, None) == 1
+    # prefill sizes need the bf16 weight staged in a workspace
+    need = lib.w4_linear_workspace_bytes(64, 32, 128, 32, 0, 0)
+    assert need == 32 * 128 * 2
+    assert lib.w4_linear_workspace_bytes(16, 32, 128, 32, 0, 0) == 0
+    assert lib.w4_linear(FAKE, 64, FAKE, FAKE, None, None, 32, 128, 32, 0, None, FAKE, None, 0, None) == 1
+    assert "workspace" in lib.w4_last_error().decode()
+    assert lib.w4_linear(FAKE, 64, FAKE, FAKE, None, None, 32, 128, 32, 0, None, FAKE, FAKE, need - 1, None) == 1
+
+
+def test_binding_validates_before_calling():
+    import torch
+    with pytest.raises(ValueError):
+        w4.quantize_pack(torch.zeros(4, 8), 8)          # CPU tensor
+    with pytest.raises(ValueError):
+        w4._mode("int8")

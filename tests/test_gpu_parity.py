@@ -1,0 +1,238 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle.
+
+quantize_pack and dequantize must be bit-exact; the linear must reach
+normwise relative error <= 5e-3 and per-element error <= 2e-2 * max|y_ref|
+against the fp64 oracle, and must be exact on an identity activation (one
+non-zero product per output).  Full-size workloads compare sampled rows
+(weight rows and output features are independent), small shapes compare
+everything, including ragged tails and the degenerate cases.
+"""
+import numpy as np
+import pytest
+import torch
+
+from oracle import w4_oracle as O
+from int4_group_wise_amd import w4
+from int4_group_wise_amd.workloads import workload, generate, bf16_bits
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+NORM_TOL = 5e-3
+ELEM_TOL = 2e-2
+
+
+def _np_w(w: torch.Tensor) -> np.ndarray:
+    if w.dtype == torch.bfloat16:
+        return O.bf16_bits_to_f32(bf16_bits(w))
+    return w.numpy()
+
+
+def _bits(t: torch.Tensor) -> np.ndarray:
+    return t.contiguous().view(torch.int16).numpy().view(np.uint16)
+
+
+def _mode(m):
+    return O.SYM if m in ("sym", 0) else O.ASYM
+
+
+def _sample_rows(N, count=256, seed=0):
+    rng = np.random.default_rng(seed)
+    head = np.arange(min(N, 16))
+    tail = np.arange(max(0, N - 16), N)
+    rnd = rng.choice(N, size=min(N, count), replace=False)
+    return np.unique(np.concatenate([head, tail, rnd]))
+
+
+def _check_codec(w, G, mode, g_idx=None, rows=None, label=""):
+    """GPU quantize_pack + dequantize vs the oracle on `rows` (all if None)."""
+    N, K = w.shape
+    gi = None if g_idx is None else g_idx.to(DEV)
+    codes, scales, zeros = w4.quantize_pack(w.to(DEV), G, mode, gi)
+    torch.cuda.synchronize()
+    sel = np.arange(N) if rows is None else rows
+    tsel = torch.from_numpy(sel).to(DEV)
+    gnp = None if g_idx is None else g_idx.numpy()
+    oc, osc, oz = O.quantize_pack(_np_w(w[torch.from_numpy(sel)]), G, _mode(mode), gnp)
+    assert np.array_equal(codes[tsel].cpu().numpy(), oc), f"codes differ {label}"
+    assert np.array_equal(scales[tsel].cpu().numpy().view(np.uint32), osc.view(np.uint32)), f"scales differ {label}"
+    if oz is not None:
+        assert np.array_equal(zeros[tsel].cpu().numpy(), oz), f"zeros differ {label}"
+    for dt, kind in ((torch.bfloat16, "bf16"), (torch.float32, "f32")):
+        d = w4.dequantize(codes, scales, zeros, gi, K, G, mode, dt)
+        got = d[tsel].cpu()
+        ref = O.dequantize(oc, osc, oz, gnp, K, G, _mode(mode), kind)
+        if kind == "bf16":
+            assert np.array_equal(_bits(got), ref), f"bf16 dequant differs {label}"
+        else:
+            assert np.array_equal(got.numpy().view(np.uint32), ref.view(np.uint32)), f"f32 dequant differs {label}"
+        del d
+    return codes, scales, zeros, (oc, osc, oz, sel)
+
+
+def _check_linear(x, codes, scales, zeros, g_idx, K, G, mode, bias, oracle_rows, label=""):
+    oc, osc, oz, sel = oracle_rows
+    gi = None if g_idx is None else g_idx.to(DEV)
+    xb = x.to(DEV)
+    bb = None if bias is None else bias.to(DEV)
+    y = w4.linear(xb, codes, scales, zeros, gi, K, G, mode, bb)
+    y2 = w4.linear(xb, codes, scales, zeros, gi, K, G, mode, bb)
+    torch.cuda.synchronize()
+    assert torch.equal(y.view(torch.int16), y2.view(torch.int16)), f"linear not deterministic {label}"
+    yg = y[:, torch.from_numpy(sel).to(DEV)].float().cpu().numpy().astype(np.float64)
+    bsel = None if bias is None else _bits(bias)[sel]
+    gnp = None if g_idx is None else g_idx.numpy()
+    yr = O.linear(_bits(x), oc, osc, oz, gnp, K, G, _mode(mode), bsel)
+    err = yg - yr
+    scale = np.abs(yr).max()
+    nrm = np.linalg.norm(yr)
+    rel = np.linalg.norm(err) / nrm if nrm > 0 else np.linalg.norm(err)
+    assert rel <= NORM_TOL, f"normwise {rel:.3e} {label}"
+    assert np.abs(err).max() <= ELEM_TOL * max(scale, 1e-30), f"max err {np.abs(err).max():.3e} vs {scale:.3e} {label}"
+    return rel
+
+
+# ---------------------------------------------------------------------------
+# the five workloads at full size
+# ---------------------------------------------------------------------------
+def test_tiny_full():
+    wl = workload("tiny")
+    t = generate(wl)
+    c, s, z, orc = _check_codec(t["w"], wl.G, wl.mode, label="tiny")
+    _check_linear(t["x"], c, s, z, None, wl.K, wl.G, wl.mode, t["bias"], orc, "tiny")
+
+
+def test_decode_full_size_sampled():
+    wl = workload("decode")
+    t = generate(wl)
+    rows = _sample_rows(wl.N, 512, 1)
+    c, s, z, orc = _check_codec(t["w"], wl.G, wl.mode, rows=rows, label="decode")
+    _check_linear(t["x"], c, s, z, None, wl.K, wl.G, wl.mode, t["bias"], orc, "decode")
+
+
+def test_batched_decode_full_size_sampled():
+    wl = workload("batched_decode")
+    t = generate(wl)
+    rows = _sample_rows(wl.N, 384, 2)
+    c, s, z, orc = _check_codec(t["w"], wl.G, wl.mode, rows=rows, label="batched_decode")
+    _check_linear(t["x"], c, s, z, None, wl.K, wl.G, wl.mode, None, orc, "batched_decode")
+
+
+def test_prefill_full_size():
+    wl = workload("prefill")
+    t = generate(wl)
+    rows = _sample_rows(wl.N, 1024, 3)
+    c, s, z, orc = _check_codec(t["w"], wl.G, wl.mode, t["g_idx"], rows=rows, label="prefill")
+    _check_linear(t["x"], c, s, z, t["g_idx"], wl.K, wl.G, wl.mode, None, orc, "prefill")
+
+
+def test_codec_full_size_sampled():
+    wl = workload("codec")
+    t = generate(wl)
+    rows = _sample_rows(wl.N, 512, 4)
+    _check_codec(t["w"], wl.G, wl.mode, rows=rows, label="codec")
+    # the same codes also drive an odd-K skinny linear (x bf16 [1, 8191] ~ N(0, 1))
+    g = torch.Generator().manual_seed(0)
+    x = torch.randn(1, wl.K, generator=g).to(torch.bfloat16)
+    c, s, z, orc = _check_codec(t["w"][:2048], wl.G, wl.mode, rows=_sample_rows(2048, 256, 5), label="codec-head")
+    _check_linear(x, c, s, z, None, wl.K, wl.G, wl.mode, None, orc, "codec-linear")
+
+
+# ---------------------------------------------------------------------------
+# small shapes: every path, ragged tails, degenerate inputs
+# ---------------------------------------------------------------------------
+CASES = [
+    # M, N, K, G, mode, act_order, w_dtype, bias
+    (1, 1, 1, 8, "sym", False, "f32", "none"),
+    (3, 5, 7, 8, "asym", False, "f32", "randn"),
+    (1, 33, 96, 32, "sym", False, "f32", "randn"),      # decode kernel, row tail
+    (2, 64, 2080, 32, "asym", False, "f32", "none"),    # decode kernel, 65 slices per row
+    (4, 19, 4096, 128, "asym", False, "bf16", "randn"),
+    (5, 40, 256, 64, "sym", False, "f32", "none"),      # generic skinny
+    (16, 100, 512, 64, "sym", False, "f32", "randn"),
+    (1, 64, 512, 128, "asym", True, "f32", "none"),     # act-order decode
+    (16, 48, 1000, 40, "asym", True, "bf16", "none"),
+    (17, 130, 200, 8, "asym", False, "f32", "randn"),   # prefill, K % 64 != 0, N tail
+    (40, 70, 99, 16, "sym", False, "f32", "none"),      # prefill, K % 8 != 0
+    (300, 260, 1024, 128, "asym", True, "f32", "randn"),
+    (129, 128, 4096, 4096, "sym", False, "bf16", "none"),  # one group per row
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=lambda c: "M%d_N%d_K%d_G%d_%s%s" % (c[0], c[1], c[2], c[3], c[4], "_act" if c[5] else ""))
+def test_small_shapes(case):
+    M, N, K, G, mode, act, wdt, bias = case
+    wl = workload("tiny", M=M, N=N, K=K, G=G, mode=mode, act_order=act, w_dtype=wdt, bias=bias,
+                  bias_std=0.01, seed=K + N)
+    if act and K % G:
+        pytest.skip("act-order workloads use whole groups")
+    t = generate(wl)
+    c, s, z, orc = _check_codec(t["w"], G, mode, t["g_idx"], label=str(case))
+    _check_linear(t["x"], c, s, z, t["g_idx"], K, G, mode, t["bias"], orc, str(case))
+
+
+def test_codec_alignment_classes_and_long_rows():
+    g = torch.Generator().manual_seed(7)
+    for (N, K, G, dt) in [(37, 8191, 32, torch.bfloat16), (11, 8191, 32, torch.float32),
+                          (9, 20000, 64, torch.float32), (9, 20001, 64, torch.bfloat16),
+                          (8, 3, 8, torch.bfloat16)]:
+        w = (torch.randn(N, K, generator=g) * 0.02).to(dt)
+        for mode in ("sym", "asym"):
+            _check_codec(w, G, mode, label=f"{N}x{K} G{G} {dt} {mode}")
+
+
+def test_codec_degenerate_values():
+    """All-zero groups, one-signed groups, exact ties, tiny (subnormal-scale)
+    and large magnitudes."""
+    N, K, G = 8, 64, 16
+    w = torch.zeros(N, K)
+    w[1] = torch.linspace(0.01, 1.0, K)                       # all positive
+    w[2] = -torch.linspace(0.01, 1.0, K)                      # all negative
+    w[3, :G] = torch.tensor([7.0, -2.5, 1.5, 0.25, 3.5, -0.5, 0.5, 5.5] * 2)   # s = 1: ties
+    w[4] = torch.randn(K, generator=torch.Generator().manual_seed(1)) * 1e-39  # subnormal range
+    w[5] = torch.randn(K, generator=torch.Generator().manual_seed(2)) * 1e30
+    w[6, ::7] = 1.0                                           # sparse
+    w[7] = -0.0
+    for mode in ("sym", "asym"):
+        _check_codec(w, G, mode, label=f"degenerate {mode}")
+        _check_codec(w.to(torch.bfloat16), G, mode, label=f"degenerate bf16 {mode}")
+
+
+def test_act_order_with_unused_groups():
+    """A g_idx that leaves some groups empty: those keep scale 1 (zero-point 0)."""
+    N, K, G = 6, 64, 16
+    w = torch.randn(N, K, generator=torch.Generator().manual_seed(3)) * 0.02
+    g_idx = torch.tensor([0, 3] * (K // 2), dtype=torch.int32)
+    for mode in ("sym", "asym"):
+        _check_codec(w, G, mode, g_idx, label=f"unused groups {mode}")
+
+
+@pytest.mark.parametrize("M,K,G,mode", [(16, 256, 32, "asym"), (4, 512, 128, "sym"), (1, 96, 32, "asym"),
+                                        (7, 100, 8, "sym"), (256, 256, 64, "asym"), (96, 96, 32, "sym")])
+def test_identity_activation_is_exact(M, K, G, mode):
+    """x = rows of the identity: every output is a single product, so
+    y[i, n] must equal the bf16 dequantized weight Wd[n, k_i] bit for bit."""
+    N = 72
+    w = torch.randn(N, K, generator=torch.Generator().manual_seed(M + K)) * 0.02
+    cols = np.sort(np.random.default_rng(M).choice(K, size=min(M, K), replace=False))
+    x = torch.zeros(len(cols), K)
+    x[torch.arange(len(cols)), torch.from_numpy(cols)] = 1.0
+    codes, scales, zeros = w4.quantize_pack(w.to(DEV), G, mode)
+    y = w4.linear(x.to(torch.bfloat16).to(DEV), codes, scales, zeros, None, K, G, mode)
+    wd = w4.dequantize(codes, scales, zeros, None, K, G, mode, torch.bfloat16)
+    torch.cuda.synchronize()
+    oc, osc, oz = O.quantize_pack(w.numpy(), G, _mode(mode))
+    ref = O.dequantize(oc, osc, oz, None, K, G, _mode(mode), "bf16")[:, cols].T
+    assert np.array_equal(_bits(y.cpu()), ref)
+    assert np.array_equal(_bits(wd.cpu())[:, cols].T, ref)
+
+
+def test_empty_batch_and_errors():
+    wl = workload("tiny", N=16, K=64)
+    t = generate(wl)
+    codes, scales, zeros = w4.quantize_pack(t["w"].to(DEV), 32, "sym")
+    y = w4.linear(torch.empty(0, 64, dtype=torch.bfloat16, device=DEV), codes, scales, zeros, None, 64, 32, "sym")
+    assert y.shape == (0, 16)
+    with pytest.raises(w4.W4Error):
+        w4.quantize_pack(t["w"].to(DEV), 12, "sym")
+    with pytest.raises(ValueError):
+        w4.linear(torch.zeros(2, 64, dtype=torch.bfloat16, device=DEV), codes, scales, None, None, 64, 32, "asym")
