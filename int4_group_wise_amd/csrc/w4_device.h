@@ -8,6 +8,13 @@ namespace w4 {
 
 constexpr int kWave = 64;
 
+// Plain vector types (HIP's uint4 is a union-based struct whose copies can
+// defeat register promotion; these stay in registers).
+typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
+typedef __attribute__((ext_vector_type(4))) float f32x4_t;
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
+
 // bf16 <-> fp32.  bf16 is the upper half of an fp32; rounding to bf16 is to
 // the nearest value, ties to the even significand, done on the bit pattern so
 // that subnormals are kept (no flush) and the result is exactly reproducible.

@@ -15,9 +15,6 @@
 namespace w4 {
 namespace {
 
-typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
-typedef __attribute__((ext_vector_type(4))) float f32x4_t;
-
 constexpr int BM = 128, BN = 128, BK = 64;
 constexpr int kLdsStride = BK + 8;   // bf16 per LDS row: 144 bytes, rows stay 16-byte aligned
 constexpr int kThreads = 256;

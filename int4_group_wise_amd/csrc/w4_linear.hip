@@ -22,8 +22,6 @@
 namespace w4 {
 namespace {
 
-typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
-
 __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
   return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
                                          __builtin_bit_cast(bf16x2_t, b), c, false);
@@ -48,27 +46,141 @@ __device__ __forceinline__ void pair_x(const uint32_t a[4], uint32_t xp[4]) {
   xp[3] = perm(a[3], a[1], 0x07060302u);   // (x3, x7)
 }
 
+// (a & m) | e in one instruction.  The compiler does not form v_and_or_b32
+// from C (a VOP3 op may read only one scalar or literal operand here), so it
+// is written out; the nibble mask lives in a VGPR, the exponent pattern in an
+// SGPR.
+__device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t m, uint32_t e) {
+  uint32_t r;
+  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(m), "s"(e));
+  return r;
+}
+
+// The nibble-pair mask 0x000F000F held in a VGPR (see and_or).
+__device__ __forceinline__ uint32_t nibble_mask() {
+  uint32_t r;
+  asm volatile("v_mov_b32 %0, 0x000F000F" : "=v"(r));
+  return r;
+}
+
+constexpr uint32_t kMagic = 0x43004300u;   // bf16 pair (128, 128): 0x4300 | u == 128 + u
+
 // sum over 8 columns of x * (128 + u); d holds the 8 nibbles (column j at bits 4j).
-__device__ __forceinline__ float dot8(uint32_t d, const uint32_t xp[4], float acc) {
-  const uint32_t m = 0x000F000Fu, e = 0x43004300u;
-  acc = dot2_bf16((d & m) | e, xp[0], acc);
-  acc = dot2_bf16(((d >> 4) & m) | e, xp[1], acc);
-  acc = dot2_bf16(((d >> 8) & m) | e, xp[2], acc);
-  acc = dot2_bf16(((d >> 12) & m) | e, xp[3], acc);
+__device__ __forceinline__ float dot8(uint32_t d, uint32_t m, const uint32_t xp[4], float acc) {
+  acc = dot2_bf16(and_or(d, m, kMagic), xp[0], acc);
+  acc = dot2_bf16(and_or(d >> 4, m, kMagic), xp[1], acc);
+  acc = dot2_bf16(and_or(d >> 8, m, kMagic), xp[2], acc);
+  acc = dot2_bf16(and_or(d >> 12, m, kMagic), xp[3], acc);
   return acc;
 }
 
-template <int MT, bool ASYM>
-__global__ __launch_bounds__(kGemvWaves * kWave) void gemv_dot2_kernel(LinearArgs a) {
-  const int lane = lane_id();
-  const int64_t wave = static_cast<int64_t>(blockIdx.x) * kGemvWaves + (threadIdx.x >> 6);
-  const int64_t row0 = wave * kGemvRows;
-  if (row0 >= a.N) return;
-  const int K = static_cast<int>(a.K);
-  const int units = K / 32;                    // 32-column slices per row
+// One lane's share of one 2048-column chunk of its wave's rows: the 16 code
+// bytes (32 columns) of each row plus that slice's scale and offset
+// (128 + zero-point).
+struct Slice {
+  uint4 cw[kGemvRows];
+  float sc[kGemvRows];
+  uint32_t zb[kGemvRows];   // raw zero-point byte: converted where it is used, so
+                            // that no instruction waits for it right after its load
+};
+
+// Row bases are wave-uniform (scalar registers); each load adds one 32-bit
+// lane offset, so no per-load 64-bit address registers are needed.
+template <bool ASYM>
+__device__ __forceinline__ void load_slice(const LinearArgs& a, int64_t row0, int u, Slice& s) {
   const int64_t KB = a.K / 2;
+  const uint32_t g = (32u * static_cast<uint32_t>(u)) / static_cast<uint32_t>(a.G);
+  const uint32_t coff = 16u * static_cast<uint32_t>(u);
+#pragma unroll
+  for (int r = 0; r < kGemvRows; ++r) {
+    const int64_t n = min(row0 + r, a.N - 1);   // clamped rows are computed, not stored
+    const uint8_t* crow = a.codes + n * KB;
+    s.cw[r] = *reinterpret_cast<const uint4*>(crow + coff);
+    s.sc[r] = (a.scales + n * a.NG)[g];
+    s.zb[r] = ASYM ? (a.zeros + n * a.NG)[g] : 8u;
+  }
+}
+
+// Activations of one lane's 32 columns for MT rows, loaded raw and re-paired
+// in place (pair_x order), with their sum per row.
+template <int MT>
+struct XSlice {
+  uint4 q[MT][4];
+  float sum[MT];
+};
+
+template <int MT>
+__device__ __forceinline__ void load_x(const LinearArgs& a, int u, int M, XSlice<MT>& x) {
+  const uint32_t off = 64u * static_cast<uint32_t>(u);
+#pragma unroll
+  for (int m = 0; m < MT; ++m) {
+    const uint8_t* xrow = reinterpret_cast<const uint8_t*>(a.x + static_cast<int64_t>(min(m, M - 1)) * a.K);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) x.q[m][i] = *reinterpret_cast<const uint4*>(xrow + off + 16u * i);
+  }
+}
+
+template <int MT>
+__device__ __forceinline__ void pair_xslice(XSlice<MT>& x) {
+  const uint32_t ones = 0x3F803F80u;   // bf16 pair (1.0, 1.0)
+#pragma unroll
+  for (int m = 0; m < MT; ++m) {
+    float t = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t in[4] = {x.q[m][i].x, x.q[m][i].y, x.q[m][i].z, x.q[m][i].w};
+      uint32_t xp[4];
+      pair_x(in, xp);
+#pragma unroll
+      for (int p = 0; p < 4; ++p) t = dot2_bf16(xp[p], ones, t);
+      x.q[m][i] = make_uint4(xp[0], xp[1], xp[2], xp[3]);
+    }
+    x.sum[m] = t;
+  }
+}
+
+template <int MT, bool ASYM>
+__device__ __forceinline__ void use_slice(const Slice& s, const XSlice<MT>& x, bool valid, uint32_t mask,
+                                          float (&tot)[kGemvRows][MT]) {
+#pragma unroll
+  for (int r = 0; r < kGemvRows; ++r) {
+    const uint32_t flip = ASYM ? 0u : 0x88888888u;
+    const uint32_t d[4] = {s.cw[r].x ^ flip, s.cw[r].y ^ flip, s.cw[r].z ^ flip, s.cw[r].w ^ flip};
+#pragma unroll
+    for (int m = 0; m < MT; ++m) {
+      float acc = 0.0f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t xp[4] = {x.q[m][i].x, x.q[m][i].y, x.q[m][i].z, x.q[m][i].w};
+        acc = dot8(d[i], mask, xp, acc);
+      }
+      const float zo = 128.0f + static_cast<float>(s.zb[r]);
+      const float v = s.sc[r] * (acc - zo * x.sum[m]);
+      tot[r][m] += valid ? v : 0.0f;
+    }
+  }
+}
+
+// Work split: a workgroup's 4 waves form 4 / KS row groups of kGemvRows rows;
+// the KS waves of a row group take alternate 2048-column chunks of K, and
+// their partial row sums are added through LDS at the end.  Per chunk a lane
+// first issues the loads of its activations (L2-resident), then the code
+// words, scales and zero-points; loads retire in order, so re-pairing the
+// activations waits only for them.  The next chunk's loads are issued before
+// the current chunk's arithmetic.
+template <int MT, bool ASYM, int KS>
+__global__ __launch_bounds__(kGemvWaves * kWave) void gemv_dot2_kernel(LinearArgs a) {
+  __shared__ float red[kGemvWaves][kGemvRows][MT];
+  const int lane = lane_id();
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int rg = w / KS, part = w % KS;
+  const int64_t row0 = (static_cast<int64_t>(blockIdx.x) * (kGemvWaves / KS) + rg) * kGemvRows;
+  const bool active = row0 < a.N;                  // idle waves still reach the barrier
+  const int units = static_cast<int>(a.K / 32);    // 32-column slices per row
+  const int nchunks = (units + kWave - 1) / kWave;
   const int M = static_cast<int>(a.M);
-  const uint32_t ones = 0x3F803F80u;           // bf16 pair (1.0, 1.0)
+  const uint32_t mask = nibble_mask();
+  const int64_t rbase = active ? row0 : 0;
 
   float tot[kGemvRows][MT];
 #pragma unroll
@@ -76,67 +188,554 @@ __global__ __launch_bounds__(kGemvWaves * kWave) void gemv_dot2_kernel(LinearArg
 #pragma unroll
     for (int m = 0; m < MT; ++m) tot[r][m] = 0.0f;
 
-  for (int u0 = 0; u0 < units; u0 += kWave) {
-    const int u = u0 + lane;
-    if (u < units) {
-      // code words of this lane's 32 columns for every row of the wave
-      uint4 cw[kGemvRows];
-      float sc[kGemvRows];
-      float zo[kGemvRows];
-      const int g = (32 * u) / static_cast<int>(a.G);
+  // Slices past the row end (K not a multiple of 2048) load the last slice
+  // again and are discarded, so the loads need no branches: a branch would
+  // end the basic block and force an early wait for all outstanding loads.
+  int c = part;
+  XSlice<MT> xa;
+  Slice sa;
+  if (c < nchunks) {
+    const int ca = min(c * kWave + lane, units - 1);
+    load_x<MT>(a, ca, M, xa);
+    __builtin_amdgcn_sched_barrier(0);
+    load_slice<ASYM>(a, rbase, ca, sa);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  for (; c < nchunks; c += KS) {
+    const int ua = c * kWave + lane;
+    const int cn = c + KS;
+    XSlice<MT> xb;
+    Slice sb;
+    if (cn < nchunks) {                              // prefetch the next chunk
+      const int cb = min(cn * kWave + lane, units - 1);
+      load_x<MT>(a, cb, M, xb);
+      __builtin_amdgcn_sched_barrier(0);
+      load_slice<ASYM>(a, rbase, cb, sb);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    pair_xslice<MT>(xa);
+    use_slice<MT, ASYM>(sa, xa, ua < units, mask, tot);
+    xa = xb;
+    sa = sb;
+  }
+
 #pragma unroll
-      for (int r = 0; r < kGemvRows; ++r) {
-        const int64_t n = min(row0 + r, a.N - 1);   // clamped rows are computed, not stored
-        cw[r] = *reinterpret_cast<const uint4*>(a.codes + n * KB + 16 * u);
-        sc[r] = a.scales[n * a.NG + g];
-        zo[r] = ASYM ? 128.0f + static_cast<float>(a.zeros[n * a.NG + g]) : 136.0f;
-      }
-      // activations of the same 32 columns
-      uint32_t xp[MT][4][4];
-      float xs[MT];
+  for (int r = 0; r < kGemvRows; ++r)
 #pragma unroll
-      for (int m = 0; m < MT; ++m) {
-        const int mm = min(m, M - 1);
-        const uint4* xr = reinterpret_cast<const uint4*>(a.x + static_cast<int64_t>(mm) * a.K + 32 * u);
-        float s = 0.0f;
+    for (int m = 0; m < MT; ++m) {
+      const float v = wave_sum(tot[r][m]);
+      if (KS > 1 && lane == 0) red[w][r][m] = v;
+      tot[r][m] = v;
+    }
+  if constexpr (KS > 1) __syncthreads();
+  if (!active || part != 0 || lane != 0) return;
+#pragma unroll
+  for (int r = 0; r < kGemvRows; ++r) {
+    const int64_t n = row0 + r;
+    if (n >= a.N) continue;
+    const float b = a.bias ? bf16_to_f32(a.bias[n]) : 0.0f;
+#pragma unroll
+    for (int m = 0; m < MT; ++m) {
+      if (m >= M) continue;
+      float v = tot[r][m];
+#pragma unroll
+      for (int p = 1; p < KS; ++p) v += red[w + p][r][m];
+      a.y[static_cast<int64_t>(m) * a.N + n] = static_cast<uint16_t>(f32_to_bf16(v + b));
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Matrix-core decode kernel (M <= 4): v_mfma_f32_16x16x32_bf16 with the
+// activations as the 16-row A operand (rows m >= M are padding) and 16 weight
+// rows as the B operand.  The only per-weight VALU work is the nibble -> bf16
+// decode (7 instructions per 8 weights); the multiply-adds run on the matrix
+// cores.
+//
+// Operand layout: lane l serves weight row n = l % 16 and column quarter
+// q = l / 16.  Per 128-column block it holds 16 code bytes (32 columns) of its
+// row; dword i feeds MFMA i.  Without transposition MFMA i sums columns
+// {kb + 32q + 8i + e}, spanning the whole block (fine for G >= 128).  For
+// G = 32 or 64 the four dwords are transposed across the lane quarters
+// (v_permlane32_swap + v_permlane16_swap), after which MFMA i sums the 32
+// contiguous columns kb + 32i .. kb + 32i + 31, a single group.
+//
+// Memory access: in that layout the four lanes of a row are 16 apart, so a
+// load would touch a different cache line in every lane.  Instead lanes
+// 4r..4r+3 load the 64 contiguous bytes of row r (16 rows per instruction,
+// one line per lane quad), and each block is re-laid out through a 1 KB
+// wave-private LDS scratch.  Scales and zero-points of the wave's 16 rows are
+// loaded the same way (consecutive lanes, consecutive groups) into an LDS
+// table.
+//
+// Workgroup = 4 waves on one 16-row tile, each wave a quarter of K; the
+// partial tiles are summed in LDS at the end.  The activations (re-paired to
+// the decode's slot order, plus their sums per 32 columns) are staged once in
+// LDS.  Load order is activations, scale/zero tables, code words: loads retire
+// in order, so the staging waits only for the first two, and the barrier
+// before the arithmetic does not wait for outstanding global loads.
+// ---------------------------------------------------------------------------
+
+constexpr int kTileWaves = 4;
+constexpr int kMfmaKR = 8;           // k-blocks (128 columns) per round
+
+// 8 nibbles (column j at bits 4j) -> 8 bf16 values 128 + u in slot order
+// (c0, c4, c1, c5, c2, c6, c3, c7), matching pair_x on the activation side.
+__device__ __forceinline__ bf16x8_t decode_word(uint32_t d, uint32_t m) {
+  const u32x4 v = {and_or(d, m, kMagic), and_or(d >> 4, m, kMagic), and_or(d >> 8, m, kMagic),
+                   and_or(d >> 12, m, kMagic)};
+  return __builtin_bit_cast(bf16x8_t, v);
+}
+
+// Register i of lane quarter q <- register q of lane quarter i (4 x 4
+// transpose across the quarters of the wave).
+__device__ __forceinline__ void transpose_quarters(uint32_t (&d)[4]) {
+  auto r02 = __builtin_amdgcn_permlane32_swap(d[0], d[2], false, false);
+  auto r13 = __builtin_amdgcn_permlane32_swap(d[1], d[3], false, false);
+  auto r01 = __builtin_amdgcn_permlane16_swap(r02[0], r13[0], false, false);
+  auto r23 = __builtin_amdgcn_permlane16_swap(r02[1], r13[1], false, false);
+  d[0] = r01[0]; d[1] = r01[1]; d[2] = r23[0]; d[3] = r23[1];
+}
+
+// Groups one wave's round can touch in a row: KR blocks of 128 columns hold
+// KR * 128 / G groups for G <= 128, at most KR + 1 for G > 128.
+constexpr int kMaxTileGroups = 4 * kMfmaKR;
+
+// LDS layout (bytes) for a K of `kc` columns and MT activation rows:
+//   x      paired activation chunks, row m at m * xrow, chunk c at + 16 c,
+//          xrow = 2 kc + 16 (the pad spreads rows over the banks);
+//   xs     float sums per row and 32-column unit, [MT][kc / 32];
+//   xsb    float sums per row and 128-column block, [MT][kc / 128];
+//   wave   per wave: 1 KB code scratch, scale table [16][kMaxTileGroups]
+//          floats, zero table [16][kMaxTileGroups] bytes;
+//   red    cross-wave reduction [kTileWaves][MT][16] floats.
+struct XLayout {
+  uint32_t xrow, xs_off, xsb_off, wave_off, wave_bytes, red_off, bytes;
+};
+
+__host__ __device__ inline XLayout x_layout(int MT, int64_t kc) {
+  XLayout L;
+  L.xrow = static_cast<uint32_t>(2 * kc + 16);
+  L.xs_off = MT * L.xrow;
+  L.xsb_off = L.xs_off + static_cast<uint32_t>(MT * (kc / 32) * 4);
+  L.wave_off = (L.xsb_off + static_cast<uint32_t>(MT * (kc / 128) * 4) + 15u) & ~15u;
+  L.wave_bytes = 1024 + 16 * kMaxTileGroups * 4 + 16 * kMaxTileGroups;
+  L.red_off = L.wave_off + kTileWaves * L.wave_bytes;
+  L.bytes = L.red_off + kTileWaves * MT * 16 * 4;
+  return L;
+}
+
+template <int MT, bool ASYM, bool TR, int GU>
+__global__ __launch_bounds__(kTileWaves * kWave, 4) void skinny_mfma_kernel(LinearArgs a, int kpw) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  constexpr int KR = kMfmaKR;
+  const int K = static_cast<int>(a.K);
+  const int M = static_cast<int>(a.M);
+  const XLayout L = x_layout(MT, K);
+  const int lane = lane_id();
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int n = lane & 15, q = lane >> 4;
+  const int64_t n0 = static_cast<int64_t>(blockIdx.x) * 16;   // rows past N are clamped: computed, not stored
+  const int nkb = K / 128;
+  const int kb0 = min(nkb, w * kpw), kb1 = min(nkb, kb0 + kpw);
+  const int64_t KB = a.K / 2;
+  const uint32_t G = static_cast<uint32_t>(a.G);
+  uint8_t* wave_lds = smem + L.wave_off + w * L.wave_bytes;
+  u32x4* scratch = reinterpret_cast<u32x4*>(wave_lds);
+  float* stab = reinterpret_cast<float*>(wave_lds + 1024);
+  uint8_t* ztab = wave_lds + 1024 + 16 * kMaxTileGroups * 4;
+
+  // 1. activations: 32-column units (64 bytes of one row), MT per thread per
+  //    batch.  All batches but the last are staged at once; the last one is
+  //    loaded, then the other loads are issued, then it is staged.
+  const int units = K / 32;
+  const int xu_total = MT * units;
+  const int nbatch = (xu_total + 256 * MT - 1) / (256 * MT);
+  u32x4 xr[MT][4];
+  auto load_x_batch = [&](int bt) {
+#pragma unroll
+    for (int j = 0; j < MT; ++j) {
+      const int t = min(bt * 256 * MT + static_cast<int>(threadIdx.x) + 256 * j, xu_total - 1);
+      const int m = t / units, u = t % units;
+      const uint8_t* src = reinterpret_cast<const uint8_t*>(a.x + static_cast<int64_t>(min(m, M - 1)) * a.K) + 64u * u;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) xr[j][i] = *reinterpret_cast<const u32x4*>(src + 16 * i);
+    }
+  };
+  auto stage_x_batch = [&](int bt) {
+#pragma unroll
+    for (int j = 0; j < MT; ++j) {
+      const int t = bt * 256 * MT + static_cast<int>(threadIdx.x) + 256 * j;
+      if (t < xu_total) {
+        const int m = t / units, u = t % units;
+        const bool live = m < M;
+        const uint32_t ones = 0x3F803F80u;
+        float sum = 0.0f;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const uint4 q = xr[i];
-          const uint32_t t[4] = {q.x, q.y, q.z, q.w};
-          pair_x(t, xp[m][i]);
+          const uint32_t in[4] = {xr[j][i][0], xr[j][i][1], xr[j][i][2], xr[j][i][3]};
+          uint32_t xp[4];
+          pair_x(in, xp);
 #pragma unroll
-          for (int p = 0; p < 4; ++p) s = dot2_bf16(xp[m][i][p], ones, s);
+          for (int p = 0; p < 4; ++p) sum = dot2_bf16(xp[p], ones, sum);
+          const u32x4 pv = {xp[0], xp[1], xp[2], xp[3]};
+          *reinterpret_cast<u32x4*>(smem + m * L.xrow + 64u * u + 16 * i) = live ? pv : u32x4{0u, 0u, 0u, 0u};
         }
-        xs[m] = s;
+        reinterpret_cast<float*>(smem + L.xs_off)[t] = live ? sum : 0.0f;
       }
+    }
+  };
+  for (int bt = 0; bt + 1 < nbatch; ++bt) {
+    load_x_batch(bt);
+    stage_x_batch(bt);
+  }
+  load_x_batch(nbatch - 1);
+
+  // 2. per round: the scale/zero table of the wave's 16 rows (consecutive
+  //    lanes read consecutive groups of a row), then the code words: load j
+  //    brings k-block j, lane quad r holding the 64 bytes of row r.
+  const uint32_t rq = static_cast<uint32_t>(lane >> 2), cq = static_cast<uint32_t>(lane & 3);
+  const uint32_t rload = static_cast<uint32_t>(min(static_cast<int64_t>(rq), a.N - 1 - n0));
+  const uint8_t* cbase = a.codes + n0 * KB;
+  const float* sbase = a.scales + n0 * a.NG;
+  const uint8_t* zbase = ASYM ? a.zeros + n0 * a.NG : nullptr;
+  u32x4 cw[KR];
+  // table loads: lane quad r covers row r, lane cq takes groups cq, cq + 4, ...
+  constexpr int kTG = GU == 1 ? KR + 1 : KR * GU;     // groups per row per round, at most
+  constexpr int kTabLoads = (kTG + 3) / 4;
+  float tabs[kTabLoads];
+  uint32_t tabz[kTabLoads];
+  int g_first = 0, ngt = 1;
+  auto issue = [&](int kbs) {
+    const int kbl = min(kbs + KR, kb1) - 1;          // last k-block of the round
+    g_first = static_cast<int>((128u * kbs) / G);
+    ngt = static_cast<int>((128u * kbl + 127u) / G) - g_first + 1;
+    const uint32_t trow = rload * static_cast<uint32_t>(a.NG) + static_cast<uint32_t>(g_first);
 #pragma unroll
-      for (int r = 0; r < kGemvRows; ++r) {
-        uint32_t d[4] = {cw[r].x, cw[r].y, cw[r].z, cw[r].w};
+    for (int j = 0; j < kTabLoads; ++j) {
+      const uint32_t gg = static_cast<uint32_t>(min(4 * j + static_cast<int>(cq), ngt - 1));
+      tabs[j] = sbase[trow + gg];
+      tabz[j] = ASYM ? zbase[trow + gg] : 8u;
+    }
+#pragma unroll
+    for (int j = 0; j < KR; ++j) {
+      const uint32_t kb = static_cast<uint32_t>(min(kbs + j, nkb - 1));
+      cw[j] = *reinterpret_cast<const u32x4*>(cbase + rload * static_cast<uint32_t>(KB) + 64u * kb + 16u * cq);
+    }
+  };
+  auto store_tab = [&]() {
+#pragma unroll
+    for (int j = 0; j < kTabLoads; ++j) {
+      const int gg = 4 * j + static_cast<int>(cq);
+      if (gg < ngt) {
+        stab[rq * kMaxTileGroups + gg] = tabs[j];
+        ztab[rq * kMaxTileGroups + gg] = static_cast<uint8_t>(tabz[j]);
+      }
+    }
+  };
+  issue(kb0);
+  __builtin_amdgcn_sched_barrier(0);
+
+  // 3. stage the last activation batch and the first table, sums per block
+  stage_x_batch(nbatch - 1);
+  store_tab();
+  __syncthreads();
+  for (int t = threadIdx.x; t < MT * (K / 128); t += kTileWaves * kWave) {
+    const float* xs4 = reinterpret_cast<const float*>(smem + L.xs_off) + 4 * t;
+    reinterpret_cast<float*>(smem + L.xsb_off)[t] = (xs4[0] + xs4[1]) + (xs4[2] + xs4[3]);
+  }
+  __syncthreads();
+
+  // 4. arithmetic.  A-operand row of this lane: output rows are independent,
+  //    so lanes whose activation row is absent (m >= MT) may read any staged
+  //    row; their output rows are discarded.
+  const uint32_t a_base = (n < MT ? n : 0) * L.xrow;
+  const uint32_t mask = nibble_mask();
+  const float* xs = reinterpret_cast<const float*>(smem + L.xs_off);
+  const float* xsb = reinterpret_cast<const float*>(smem + L.xsb_off);
+  float out[MT];
+#pragma unroll
+  for (int t = 0; t < MT; ++t) out[t] = 0.0f;
+  const f32x4_t zero4 = {0.0f, 0.0f, 0.0f, 0.0f};
+
+  for (int kbs = kb0; kbs < kb1; kbs += KR) {
+#pragma unroll
+    for (int j = 0; j < KR; ++j) {
+      const int kb = kbs + j;
+      if (kb < kb1) {
+        // re-lay the block out: row-major in, operand layout out
+        scratch[rq * 4 + cq] = cw[j];
+        __builtin_amdgcn_s_waitcnt(0xc07f);          // lgkmcnt(0): the wave's own LDS writes
+        const u32x4 v = scratch[n * 4 + q];
+        uint32_t d[4] = {v[0], v[1], v[2], v[3]};
         if constexpr (!ASYM) {
 #pragma unroll
           for (int i = 0; i < 4; ++i) d[i] ^= 0x88888888u;
         }
+        if constexpr (TR) transpose_quarters(d);
+        f32x4_t acc[GU];
 #pragma unroll
-        for (int m = 0; m < MT; ++m) {
-          float acc = 0.0f;
+        for (int i = 0; i < 4; ++i) {
+          const uint32_t chunk = TR ? (16u * kb + 4u * i + q) : (16u * kb + 4u * q + i);
+          const bf16x8_t av = *reinterpret_cast<const bf16x8_t*>(smem + a_base + 16u * chunk);
+          const int gi = i / (4 / GU);
+          acc[gi] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, decode_word(d[i], mask),
+                                                            (i % (4 / GU)) == 0 ? zero4 : acc[gi], 0, 0, 0);
+        }
+        // group correction: out += s * (acc - (128 + z) * sum_x); output rows
+        // 4 (l / 16) + t, so for M <= 4 only the first quarter's t < M matter
 #pragma unroll
-          for (int i = 0; i < 4; ++i) acc = dot8(d[i], xp[m][i], acc);
-          tot[r][m] += sc[r] * (acc - zo[r] * xs[m]);
+        for (int gi = 0; gi < GU; ++gi) {
+          const int col = 128 * kb + (128 / GU) * gi;
+          const int gg = col / static_cast<int>(G) - g_first;
+          const float sc = stab[n * kMaxTileGroups + gg];
+          const float zo = 128.0f + static_cast<float>(ztab[n * kMaxTileGroups + gg]);
+#pragma unroll
+          for (int t = 0; t < MT; ++t) {
+            const float sx = GU == 1 ? xsb[t * (K / 128) + kb] : 0.0f;
+            float sxu = 0.0f;
+            if constexpr (GU > 1) {
+#pragma unroll
+              for (int uu = 0; uu < 4 / GU; ++uu) sxu += xs[t * units + 4 * kb + gi * (4 / GU) + uu];
+            }
+            out[t] += sc * (acc[gi][t] - zo * (GU == 1 ? sx : sxu));
+          }
         }
       }
+      __builtin_amdgcn_sched_barrier(0);   // bound register use: one k-block in flight
+    }
+    if (kbs + KR < kb1) {
+      issue(kbs + KR);
+      store_tab();
     }
   }
 
+  // 5. sum the four K quarters and store
+  float* red = reinterpret_cast<float*>(smem + L.red_off);
+  if (lane < 16) {
 #pragma unroll
-  for (int r = 0; r < kGemvRows; ++r) {
+    for (int t = 0; t < MT; ++t) red[(w * MT + t) * 16 + n] = out[t];
+  }
+  __syncthreads();
+  if (w == 0 && lane < 16 && n0 + n < a.N) {
+    const float b = a.bias ? bf16_to_f32(a.bias[n0 + n]) : 0.0f;
 #pragma unroll
-    for (int m = 0; m < MT; ++m) {
-      const float v = wave_sum(tot[r][m]);
-      const int64_t n = row0 + r;
-      if (lane == 0 && n < a.N && m < M) {
-        const float b = a.bias ? bf16_to_f32(a.bias[n]) : 0.0f;
-        a.y[static_cast<int64_t>(m) * a.N + n] = static_cast<uint16_t>(f32_to_bf16(v + b));
+    for (int t = 0; t < MT; ++t) {
+      if (t < M) {
+        float v = 0.0f;
+#pragma unroll
+        for (int ww = 0; ww < kTileWaves; ++ww) v += red[(ww * MT + t) * 16 + n];
+        a.y[static_cast<int64_t>(t) * a.N + n0 + n] = static_cast<uint16_t>(f32_to_bf16(v + b));
       }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Matrix-core batched-decode kernel (4 < M <= 16).  The same operand scheme
+// as skinny_mfma_kernel (activations = 16-row A operand, 16 weight rows = B
+// operand, nibbles decoded to 128 + u, per-group correction), organised for
+// activation reuse: a workgroup's 4 waves own 4 different 16-row tiles and
+// walk K together in batches of kRowsKB blocks of 128 columns; each batch's
+// activations [16 rows x 512 columns] are staged once in LDS (re-paired, with
+// sums per 32 columns) and read by all 4 waves.  Batches are double-buffered:
+// batch b + 1 is loaded (activations, scale/zero tables, code words, in that
+// order) while batch b is computed.  Code words are loaded by lane quads
+// (64 contiguous bytes of a row) and re-laid out through a 1 KB wave-private
+// LDS scratch, as in the decode kernel.
+// ---------------------------------------------------------------------------
+constexpr int kRowsWaves = 4;
+constexpr int kRowsKB = 4;                      // 128-column blocks per batch
+constexpr int kRowsTG = 16;                     // table groups per row per batch, at most
+
+struct RowsLayout {
+  uint32_t xrow, xbuf, xs_off, xsbuf, wave_off, wave_bytes, bytes;
+};
+
+__host__ __device__ inline RowsLayout rows_layout() {
+  RowsLayout L;
+  L.xrow = kRowsKB * 128 * 2 + 16;              // one activation row of a batch (+ bank pad)
+  L.xbuf = 16 * L.xrow;
+  L.xs_off = 2 * L.xbuf;
+  L.xsbuf = 16 * kRowsKB * 4 * 4;               // [16 rows][kRowsKB * 4 units] floats
+  L.wave_off = L.xs_off + 2 * L.xsbuf;
+  L.wave_bytes = 1024 + 16 * kRowsTG * 4 + 16 * kRowsTG;
+  L.bytes = L.wave_off + kRowsWaves * L.wave_bytes;
+  return L;
+}
+
+struct RowsRegs {
+  u32x4 x[4];          // this thread's staged activation unit (64 bytes)
+  u32x4 cw[kRowsKB];   // code words, load j = block j of the batch
+  float ts[4];         // scale table entries
+  uint32_t tz[4];      // zero-point table entries
+};
+
+template <bool ASYM>
+__device__ __forceinline__ void rows_issue(const LinearArgs& a, int b, int nkb, int64_t n0,
+                                           int lane, RowsRegs& R) {
+  const int M = static_cast<int>(a.M);
+  const int K = static_cast<int>(a.K);
+  const uint32_t G = static_cast<uint32_t>(a.G);
+  // activations: thread t stages row t / 16, unit t % 16 of the batch
+  const int t = threadIdx.x;
+  const int xm = min(t >> 4, M - 1);
+  const int col = min(b * kRowsKB * 128 + 32 * (t & 15), K - 32);
+  const uint8_t* xs = reinterpret_cast<const uint8_t*>(a.x + static_cast<int64_t>(xm) * a.K + col);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) R.x[i] = *reinterpret_cast<const u32x4*>(xs + 16 * i);
+  __builtin_amdgcn_sched_barrier(0);
+  // scale / zero-point table: lane quad r = row r, lane cq takes groups cq + 4 i
+  const uint32_t rq = static_cast<uint32_t>(lane >> 2), cq = static_cast<uint32_t>(lane & 3);
+  const uint32_t rload = static_cast<uint32_t>(min(static_cast<int64_t>(rq), a.N - 1 - n0));
+  const int kbf = b * kRowsKB, kbl = min(kbf + kRowsKB, nkb) - 1;
+  const int g_first = static_cast<int>((128u * kbf) / G);
+  const int ngt = static_cast<int>((128u * kbl + 127u) / G) - g_first + 1;
+  const uint32_t trow = (static_cast<uint32_t>(n0) + rload) * static_cast<uint32_t>(a.NG) + static_cast<uint32_t>(g_first);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t gg = static_cast<uint32_t>(min(4 * i + static_cast<int>(cq), ngt - 1));
+    R.ts[i] = a.scales[trow + gg];
+    R.tz[i] = ASYM ? a.zeros[trow + gg] : 8u;
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  // code words
+  const uint8_t* crow = a.codes + (n0 + rload) * (a.K / 2);
+#pragma unroll
+  for (int j = 0; j < kRowsKB; ++j) {
+    const uint32_t kb = static_cast<uint32_t>(min(kbf + j, nkb - 1));
+    R.cw[j] = *reinterpret_cast<const u32x4*>(crow + 64u * kb + 16u * cq);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// Stage batch b's activations into buffer b % 2 and this wave's tables.
+__device__ __forceinline__ void rows_stage(const LinearArgs& a, int b, int lane, const RowsRegs& R,
+                                           uint8_t* smem, const RowsLayout& L, uint8_t* wave_lds) {
+  const int M = static_cast<int>(a.M);
+  const int K = static_cast<int>(a.K);
+  const int t = threadIdx.x;
+  const int m = t >> 4, uu = t & 15;
+  const bool live = m < M && b * kRowsKB * 128 + 32 * uu < K;
+  const uint32_t ones = 0x3F803F80u;
+  uint8_t* xb = smem + (b & 1) * L.xbuf + m * L.xrow + 64 * uu;
+  float sum = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t in[4] = {R.x[i][0], R.x[i][1], R.x[i][2], R.x[i][3]};
+    uint32_t xp[4];
+    pair_x(in, xp);
+#pragma unroll
+    for (int p = 0; p < 4; ++p) sum = dot2_bf16(xp[p], ones, sum);
+    *reinterpret_cast<u32x4*>(xb + 16 * i) = live ? u32x4{xp[0], xp[1], xp[2], xp[3]} : u32x4{0u, 0u, 0u, 0u};
+  }
+  reinterpret_cast<float*>(smem + L.xs_off + (b & 1) * L.xsbuf)[m * (kRowsKB * 4) + uu] = live ? sum : 0.0f;
+  const int rq = lane >> 2, cq = lane & 3;
+  float* stab = reinterpret_cast<float*>(wave_lds + 1024);
+  uint8_t* ztab = wave_lds + 1024 + 16 * kRowsTG * 4;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    stab[rq * kRowsTG + 4 * i + cq] = R.ts[i];
+    ztab[rq * kRowsTG + 4 * i + cq] = static_cast<uint8_t>(R.tz[i]);
+  }
+}
+
+template <bool ASYM, bool TR, int GU>
+__device__ __forceinline__ void rows_compute(const LinearArgs& a, int b, int nkb, int lane, uint32_t mask,
+                                             const RowsRegs& R, const uint8_t* smem, const RowsLayout& L,
+                                             uint8_t* wave_lds, float (&out)[4]) {
+  const uint32_t G = static_cast<uint32_t>(a.G);
+  const int n = lane & 15, q = lane >> 4;
+  const int rq = lane >> 2, cq = lane & 3;
+  u32x4* scratch = reinterpret_cast<u32x4*>(wave_lds);
+  const float* stab = reinterpret_cast<const float*>(wave_lds + 1024);
+  const uint8_t* ztab = wave_lds + 1024 + 16 * kRowsTG * 4;
+  const uint8_t* xa = smem + (b & 1) * L.xbuf + n * L.xrow;          // A row n (zero rows for m >= M)
+  const float* xs = reinterpret_cast<const float*>(smem + L.xs_off + (b & 1) * L.xsbuf);
+  const int kbf = b * kRowsKB;
+  const int g_first = static_cast<int>((128u * kbf) / G);
+  const f32x4_t zero4 = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+  for (int j = 0; j < kRowsKB; ++j) {
+    if (kbf + j < nkb) {
+      scratch[rq * 4 + cq] = R.cw[j];
+      __builtin_amdgcn_s_waitcnt(0xc07f);            // lgkmcnt(0): the wave's own LDS writes
+      const u32x4 v = scratch[n * 4 + q];
+      uint32_t d[4] = {v[0], v[1], v[2], v[3]};
+      if constexpr (!ASYM) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) d[i] ^= 0x88888888u;
+      }
+      if constexpr (TR) transpose_quarters(d);
+      f32x4_t acc[GU];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t chunk = TR ? (16u * j + 4u * i + q) : (16u * j + 4u * q + i);
+        const bf16x8_t av = *reinterpret_cast<const bf16x8_t*>(xa + 16u * chunk);
+        const int gi = i / (4 / GU);
+        acc[gi] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, decode_word(d[i], mask),
+                                                          (i % (4 / GU)) == 0 ? zero4 : acc[gi], 0, 0, 0);
+      }
+#pragma unroll
+      for (int gi = 0; gi < GU; ++gi) {
+        const int col = 128 * (kbf + j) + (128 / GU) * gi;
+        const int gg = col / static_cast<int>(G) - g_first;
+        const float sc = stab[n * kRowsTG + gg];
+        const float zo = 128.0f + static_cast<float>(ztab[n * kRowsTG + gg]);
+        const int u0 = 4 * j + gi * (4 / GU);
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const int m = 4 * q + t;                    // output row of acc[gi][t]
+          float sx = 0.0f;
+#pragma unroll
+          for (int uu = 0; uu < 4 / GU; ++uu) sx += xs[m * (kRowsKB * 4) + u0 + uu];
+          out[t] += sc * (acc[gi][t] - zo * sx);
+        }
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+template <bool ASYM, bool TR, int GU>
+__global__ __launch_bounds__(kRowsWaves * kWave, 2) void skinny_rows_kernel(LinearArgs a) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  const RowsLayout L = rows_layout();
+  const int lane = lane_id();
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int64_t n0 = static_cast<int64_t>(blockIdx.x) * (16 * kRowsWaves) + 16 * w;  // rows past N are clamped
+  const int64_t n0c = min(n0, a.N - 1);
+  uint8_t* wave_lds = smem + L.wave_off + w * L.wave_bytes;
+  const int nkb = static_cast<int>(a.K / 128);
+  const int nbat = (nkb + kRowsKB - 1) / kRowsKB;
+  const uint32_t mask = nibble_mask();
+  float out[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+
+  RowsRegs ra, rb;
+  rows_issue<ASYM>(a, 0, nkb, n0c, lane, ra);
+  rows_stage(a, 0, lane, ra, smem, L, wave_lds);
+  __syncthreads();
+  for (int b = 0; b < nbat; b += 2) {
+    if (b + 1 < nbat) rows_issue<ASYM>(a, b + 1, nkb, n0c, lane, rb);
+    rows_compute<ASYM, TR, GU>(a, b, nkb, lane, mask, ra, smem, L, wave_lds, out);
+    if (b + 1 >= nbat) break;
+    rows_stage(a, b + 1, lane, rb, smem, L, wave_lds);
+    __syncthreads();
+    if (b + 2 < nbat) rows_issue<ASYM>(a, b + 2, nkb, n0c, lane, ra);
+    rows_compute<ASYM, TR, GU>(a, b + 1, nkb, lane, mask, rb, smem, L, wave_lds, out);
+    if (b + 2 >= nbat) break;
+    rows_stage(a, b + 2, lane, ra, smem, L, wave_lds);
+    __syncthreads();
+  }
+
+  // lane holds output rows m = 4 q + t of weight row n0 + n
+  const int n = lane & 15, q = lane >> 4;
+  if (n0 + n < a.N) {
+    const float bias = a.bias ? bf16_to_f32(a.bias[n0 + n]) : 0.0f;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const int m = 4 * q + t;
+      if (m < a.M) a.y[static_cast<int64_t>(m) * a.N + n0 + n] = static_cast<uint16_t>(f32_to_bf16(out[t] + bias));
     }
   }
 }
@@ -185,16 +784,77 @@ __global__ __launch_bounds__(kGemvWaves * kWave) void gemv_generic_kernel(Linear
   }
 }
 
-template <int MT>
-hipError_t launch_dot2(const LinearArgs& a, hipStream_t s) {
-  const int64_t waves = (a.N + kGemvRows - 1) / kGemvRows;
-  const dim3 grid(static_cast<uint32_t>((waves + kGemvWaves - 1) / kGemvWaves));
+template <int MT, int KS>
+hipError_t launch_dot2_ks(const LinearArgs& a, hipStream_t s) {
+  const int64_t groups = (a.N + kGemvRows - 1) / kGemvRows;
+  const dim3 grid(static_cast<uint32_t>((groups + kGemvWaves / KS - 1) / (kGemvWaves / KS)));
   const dim3 block(kGemvWaves * kWave);
   if (a.asym)
-    gemv_dot2_kernel<MT, true><<<grid, block, 0, s>>>(a);
+    gemv_dot2_kernel<MT, true, KS><<<grid, block, 0, s>>>(a);
   else
-    gemv_dot2_kernel<MT, false><<<grid, block, 0, s>>>(a);
+    gemv_dot2_kernel<MT, false, KS><<<grid, block, 0, s>>>(a);
   return hipGetLastError();
+}
+
+// K is split over two waves per row group when a row has at least two
+// 2048-column chunks.
+template <int MT>
+hipError_t launch_dot2(const LinearArgs& a, hipStream_t s) {
+  return a.K > 2048 ? launch_dot2_ks<MT, 2>(a, s) : launch_dot2_ks<MT, 1>(a, s);
+}
+
+template <int MT, bool ASYM, bool TR, int GU>
+hipError_t launch_mfma4(const LinearArgs& a, hipStream_t s) {
+  const int nkb = static_cast<int>(a.K / 128);
+  const int kpw = (nkb + kTileWaves - 1) / kTileWaves;
+  const XLayout L = x_layout(MT, a.K);
+  const dim3 grid(static_cast<uint32_t>((a.N + 15) / 16)), block(kTileWaves * kWave);
+  skinny_mfma_kernel<MT, ASYM, TR, GU><<<grid, block, L.bytes, s>>>(a, kpw);
+  return hipGetLastError();
+}
+
+template <int MT, bool ASYM>
+hipError_t launch_mfma3(const LinearArgs& a, hipStream_t s) {
+  if (a.G == 32) return launch_mfma4<MT, ASYM, true, 4>(a, s);
+  if (a.G == 64) return launch_mfma4<MT, ASYM, true, 2>(a, s);
+  return launch_mfma4<MT, ASYM, false, 1>(a, s);
+}
+
+template <int MT>
+hipError_t launch_mfma2(const LinearArgs& a, hipStream_t s) {
+  return a.asym ? launch_mfma3<MT, true>(a, s) : launch_mfma3<MT, false>(a, s);
+}
+
+// The matrix-core decode kernel covers contiguous groups of 32, 64 or a
+// multiple of 128 columns, K a multiple of 128, M <= 4, and activations that
+// fit the 64 KB LDS staging area.
+bool mfma_ok(const LinearArgs& a) {
+  if (a.g_idx != nullptr || a.K % 128 != 0 || a.M > 4) return false;
+  if (!(a.G == 32 || a.G == 64 || a.G % 128 == 0)) return false;
+  const int MT = a.M == 1 ? 1 : a.M == 2 ? 2 : 4;
+  return x_layout(MT, a.K).bytes <= 65536;
+}
+
+template <bool ASYM, bool TR, int GU>
+hipError_t launch_rows3(const LinearArgs& a, hipStream_t s) {
+  const RowsLayout L = rows_layout();
+  const dim3 grid(static_cast<uint32_t>((a.N + 16 * kRowsWaves - 1) / (16 * kRowsWaves)));
+  skinny_rows_kernel<ASYM, TR, GU><<<grid, dim3(kRowsWaves * kWave), L.bytes, s>>>(a);
+  return hipGetLastError();
+}
+
+template <bool ASYM>
+hipError_t launch_rows2(const LinearArgs& a, hipStream_t s) {
+  if (a.G == 32) return launch_rows3<ASYM, true, 4>(a, s);
+  if (a.G == 64) return launch_rows3<ASYM, true, 2>(a, s);
+  return launch_rows3<ASYM, false, 1>(a, s);
+}
+
+// Batched decode on the matrix cores: contiguous groups of 32, 64 or a
+// multiple of 128 columns, K a multiple of 128, 4 < M <= 16.
+bool rows_ok(const LinearArgs& a) {
+  return a.g_idx == nullptr && a.K % 128 == 0 && a.M > 4 && a.M <= 16 &&
+         (a.G == 32 || a.G == 64 || a.G % 128 == 0);
 }
 
 bool dot2_ok(const LinearArgs& a) {
@@ -207,6 +867,12 @@ bool skinny_supported(const LinearArgs& a) { return a.M >= 1 && a.M <= 16; }
 
 hipError_t launch_linear_skinny(const LinearArgs& a, hipStream_t s) {
   if (!skinny_supported(a)) return hipErrorInvalidValue;
+  if (rows_ok(a)) return a.asym ? launch_rows2<true>(a, s) : launch_rows2<false>(a, s);
+  if (mfma_ok(a)) {
+    if (a.M == 1) return launch_mfma2<1>(a, s);
+    if (a.M == 2) return launch_mfma2<2>(a, s);
+    return launch_mfma2<4>(a, s);
+  }
   if (dot2_ok(a)) {
     if (a.M == 1) return launch_dot2<1>(a, s);
     if (a.M == 2) return launch_dot2<2>(a, s);

@@ -143,12 +143,20 @@ def test_codec_full_size_sampled():
 CASES = [
     # M, N, K, G, mode, act_order, w_dtype, bias
     (1, 1, 1, 8, "sym", False, "f32", "none"),
+    (1, 33, 128, 128, "asym", False, "f32", "randn"),   # matrix-core decode: one k-block, row tail
+    (3, 50, 1024, 64, "sym", False, "f32", "none"),     # matrix-core decode, transposed quarters
+    (2, 40, 640, 32, "asym", False, "bf16", "randn"),
+    (1, 24, 14336, 128, "sym", False, "f32", "none"),   # long K: activations staged in two batches
+    (4, 16, 2048, 256, "asym", False, "f32", "randn"),
     (3, 5, 7, 8, "asym", False, "f32", "randn"),
     (1, 33, 96, 32, "sym", False, "f32", "randn"),      # decode kernel, row tail
     (2, 64, 2080, 32, "asym", False, "f32", "none"),    # decode kernel, 65 slices per row
     (4, 19, 4096, 128, "asym", False, "bf16", "randn"),
     (5, 40, 256, 64, "sym", False, "f32", "none"),      # generic skinny
-    (16, 100, 512, 64, "sym", False, "f32", "randn"),
+    (16, 100, 512, 64, "sym", False, "f32", "randn"),   # matrix-core batched decode
+    (5, 70, 640, 32, "asym", False, "f32", "randn"),     # batch tail (5 blocks of 128 columns)
+    (12, 200, 1024, 256, "sym", False, "bf16", "none"),
+    (16, 64, 8192, 64, "sym", False, "f32", "none"),
     (1, 64, 512, 128, "asym", True, "f32", "none"),     # act-order decode
     (16, 48, 1000, 40, "asym", True, "bf16", "none"),
     (17, 130, 200, 8, "asym", False, "f32", "randn"),   # prefill, K % 64 != 0, N tail
