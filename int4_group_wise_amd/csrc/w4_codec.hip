@@ -225,13 +225,31 @@ __global__ __launch_bounds__(kQThreads) void quantize_pack_kernel(QuantArgs a) {
   }
 }
 
-// Dequantize: one thread per 8 consecutive columns of one row.
-template <bool OUT_BF16, bool ASYM, bool GIDX>
+// Largest row table (scales + zero-points) the act-order dequantizer stages
+// in LDS; rows with more groups gather from global memory instead.
+constexpr int64_t kDequantLdsGroups = 8192;
+
+// Dequantize: one thread per 8 consecutive columns of one row.  GIDX: 0 =
+// contiguous groups, 1 = act-order with the row's scale / zero-point table
+// staged in LDS (g_idx read 8 entries at a time), 2 = act-order gathering the
+// table entries from global memory.
+template <bool OUT_BF16, bool ASYM, int GIDX>
 __global__ __launch_bounds__(kDThreads) void dequantize_kernel(DequantArgs a, int chunk_blocks) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t dsm[];
   const int64_t n = blockIdx.x / chunk_blocks;
   const int j = (blockIdx.x % chunk_blocks) * kDThreads + threadIdx.x;
   const int K = static_cast<int>(a.K);
   const int nchunks = (K + 7) / 8;
+  const int NG = static_cast<int>(a.NG);
+  float* st = reinterpret_cast<float*>(dsm);
+  uint8_t* zt = dsm + 4 * NG;
+  if constexpr (GIDX == 1) {
+    for (int g = threadIdx.x; g < NG; g += kDThreads) {
+      st[g] = a.scales[n * a.NG + g];
+      if constexpr (ASYM) zt[g] = a.zeros[n * a.NG + g];
+    }
+    __syncthreads();
+  }
   if (j >= nchunks) return;
   const int64_t KB = (a.K + 1) / 2;
   const int k0 = 8 * j, cnt = min(8, K - k0);
@@ -248,7 +266,7 @@ __global__ __launch_bounds__(kDThreads) void dequantize_kernel(DequantArgs a, in
   float o[8];
   const float* srow = a.scales + n * a.NG;
   const uint8_t* zrow = ASYM ? a.zeros + n * a.NG : nullptr;
-  if constexpr (!GIDX) {
+  if constexpr (GIDX == 0) {
     const int g = k0 / static_cast<int>(a.G);
     const float s = srow[g];
     const int z = ASYM ? static_cast<int>(zrow[g]) : 0;
@@ -258,12 +276,30 @@ __global__ __launch_bounds__(kDThreads) void dequantize_kernel(DequantArgs a, in
       const int val = ASYM ? nib - z : (nib ^ 8) - 8;
       o[e] = static_cast<float>(val) * s;
     }
+  } else if constexpr (GIDX == 1) {
+    int gv[8];
+    if (cnt == 8) {
+      const u32x4 g0 = *reinterpret_cast<const u32x4*>(a.g_idx + k0);
+      const u32x4 g1 = *reinterpret_cast<const u32x4*>(a.g_idx + k0 + 4);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) { gv[e] = static_cast<int>(g0[e]); gv[4 + e] = static_cast<int>(g1[e]); }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) gv[e] = e < cnt ? a.g_idx[k0 + e] : 0;
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int g = min(max(gv[e], 0), NG - 1);
+      const int nib = static_cast<int>((d >> (4 * e)) & 15u);
+      const int val = ASYM ? nib - static_cast<int>(zt[g]) : (nib ^ 8) - 8;
+      o[e] = static_cast<float>(val) * st[g];
+    }
   } else {
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       o[e] = 0.0f;
       if (e < cnt) {
-        const int g = gid_at(a.g_idx, k0 + e, static_cast<int>(a.NG));
+        const int g = gid_at(a.g_idx, k0 + e, NG);
         const int nib = static_cast<int>((d >> (4 * e)) & 15u);
         const int val = ASYM ? nib - static_cast<int>(zrow[g]) : (nib ^ 8) - 8;
         o[e] = static_cast<float>(val) * srow[g];
@@ -322,18 +358,21 @@ hipError_t launch_q2(const QuantArgs& a, hipStream_t s) {
   return a.g_idx ? launch_q3<BF16, ASYM, true>(a, s) : launch_q3<BF16, ASYM, false>(a, s);
 }
 
-template <bool OUT_BF16, bool ASYM, bool GIDX>
+template <bool OUT_BF16, bool ASYM, int GIDX>
 hipError_t launch_d3(const DequantArgs& a, hipStream_t s) {
   const int64_t nchunks = (a.K + 7) / 8;
   const int cb = static_cast<int>((nchunks + kDThreads - 1) / kDThreads);
   const dim3 grid(static_cast<uint32_t>(a.N * cb)), block(kDThreads);
-  dequantize_kernel<OUT_BF16, ASYM, GIDX><<<grid, block, 0, s>>>(a, cb);
+  const size_t lds = GIDX == 1 ? static_cast<size_t>((a.NG * 5 + 15) / 16 * 16) : 0;
+  dequantize_kernel<OUT_BF16, ASYM, GIDX><<<grid, block, lds, s>>>(a, cb);
   return hipGetLastError();
 }
 
 template <bool OUT_BF16, bool ASYM>
 hipError_t launch_d2(const DequantArgs& a, hipStream_t s) {
-  return a.g_idx ? launch_d3<OUT_BF16, ASYM, true>(a, s) : launch_d3<OUT_BF16, ASYM, false>(a, s);
+  if (!a.g_idx) return launch_d3<OUT_BF16, ASYM, 0>(a, s);
+  if (a.NG <= kDequantLdsGroups) return launch_d3<OUT_BF16, ASYM, 1>(a, s);
+  return launch_d3<OUT_BF16, ASYM, 2>(a, s);
 }
 
 }  // namespace

@@ -40,7 +40,7 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_nt_kernel(
 
   // A K-step of either operand is 128 rows x 64 columns = 1024 chunks of
   // 8 bf16 (16 bytes); thread t moves chunks t, t+256, t+512, t+768.
-  uint4 ra[4], rb[4];
+  u32x4 ra[4], rb[4];
   auto gload = [&](int k0) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -48,9 +48,9 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_nt_kernel(
       const int r = c >> 3, kc = (c & 7) * 8;
       const int gk = k0 + kc;
       const int gm = m0 + r, gn = n0 + r;
-      const uint4 zero = {0u, 0u, 0u, 0u};
-      ra[i] = (gm < M && gk < K) ? *reinterpret_cast<const uint4*>(x + static_cast<int64_t>(gm) * K + gk) : zero;
-      rb[i] = (gn < N && gk < K) ? *reinterpret_cast<const uint4*>(wd + static_cast<int64_t>(gn) * K + gk) : zero;
+      const u32x4 zero = {0u, 0u, 0u, 0u};
+      ra[i] = (gm < M && gk < K) ? *reinterpret_cast<const u32x4*>(x + static_cast<int64_t>(gm) * K + gk) : zero;
+      rb[i] = (gn < N && gk < K) ? *reinterpret_cast<const u32x4*>(wd + static_cast<int64_t>(gn) * K + gk) : zero;
     }
   };
   auto sstore = [&]() {
@@ -58,8 +58,8 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_nt_kernel(
     for (int i = 0; i < 4; ++i) {
       const int c = tid + kThreads * i;
       const int r = c >> 3, kc = (c & 7) * 8;
-      *reinterpret_cast<uint4*>(&As[r * kLdsStride + kc]) = ra[i];
-      *reinterpret_cast<uint4*>(&Bs[r * kLdsStride + kc]) = rb[i];
+      *reinterpret_cast<u32x4*>(&As[r * kLdsStride + kc]) = ra[i];
+      *reinterpret_cast<u32x4*>(&Bs[r * kLdsStride + kc]) = rb[i];
     }
   };
 
@@ -105,6 +105,135 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_nt_kernel(
   }
 }
 
+// ---------------------------------------------------------------------------
+// Pipelined GEMM for K % 64 == 0: 256 x 128 output tile per 256-thread
+// workgroup (2 x 2 waves of 128 x 64, i.e. 8 x 4 MFMA tiles of 16 x 16 per
+// wave), K stepped by 64 through a 3-stage LDS ring filled by direct
+// global -> LDS loads (global_load_lds_dwordx4), so two K-steps are in flight
+// while one is consumed without staging registers.
+//
+// LDS layout of a stage: A rows (256) then B rows (128), 128 bytes each (64
+// bf16), split in 8 chunks of 16 bytes; chunk c of row r is stored at slot
+// c ^ (r & 7), so the 16 rows a fragment read touches hit distinct banks.  A
+// load instruction fills 1 KB of consecutive slots (8 rows): lane i writes
+// slot i, so lane i fetches the global chunk that belongs there.
+// ---------------------------------------------------------------------------
+constexpr int PM = 256, PN = 128, PK = 64, PSTAGES = 3;
+constexpr int kPStageBytes = (PM + PN) * PK * 2;          // 48 KB
+constexpr int kPLdsBytes = PSTAGES * kPStageBytes;       // 144 KB
+
+__device__ __forceinline__ void lds_dma16(const void* gsrc, void* ldst) {
+  __builtin_amdgcn_global_load_lds(gsrc, reinterpret_cast<__attribute__((address_space(3))) void*>(
+                                       reinterpret_cast<uintptr_t>(ldst)), 16, 0, 0);
+}
+
+__global__ __launch_bounds__(kThreads) void gemm_bf16_pipe_kernel(
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ wd,
+    const uint16_t* __restrict__ bias, uint16_t* __restrict__ y,
+    int M, int N, int K) {
+  extern __shared__ __attribute__((aligned(1024))) uint8_t psm[];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wid >> 1, wn = wid & 1;
+  const int tiles_n = (N + PN - 1) / PN;
+  const int m0 = (blockIdx.x / tiles_n) * PM;
+  const int n0 = (blockIdx.x % tiles_n) * PN;
+
+  // loads: wave wid fills A rows [64 wid, 64 wid + 64) (8 instructions of 8
+  // rows) and B rows [32 wid, 32 wid + 32) (4 instructions); lane i of an
+  // instruction covering rows r0..r0+7 writes slot i = (row r0 + i / 8,
+  // slot i % 8) and fetches chunk (i % 8) ^ (row & 7) of that row.  Rows past
+  // M or N fetch a valid row instead: their outputs are never stored.
+  const int lr = lane >> 3, ls = lane & 7;
+  const uint16_t* asrc[8];
+  const uint16_t* bsrc[4];
+#pragma unroll
+  for (int p = 0; p < 8; ++p) {
+    const int r = 64 * wid + 8 * p + lr;
+    const int gm = min(m0 + r, M - 1);
+    asrc[p] = x + static_cast<int64_t>(gm) * K + 8 * (ls ^ (r & 7));
+  }
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    const int r = 32 * wid + 8 * p + lr;
+    const int gn = min(n0 + r, N - 1);
+    bsrc[p] = wd + static_cast<int64_t>(gn) * K + 8 * (ls ^ (r & 7));
+  }
+  auto issue = [&](int kt) {
+    uint8_t* st = psm + (kt % PSTAGES) * kPStageBytes;
+    const int k0 = kt * PK;
+#pragma unroll
+    for (int p = 0; p < 8; ++p) lds_dma16(asrc[p] + k0, st + (64 * wid + 8 * p) * 128);
+#pragma unroll
+    for (int p = 0; p < 4; ++p) lds_dma16(bsrc[p] + k0, st + PM * 128 + (32 * wid + 8 * p) * 128);
+  };
+
+  f32x4_t acc[8][4];
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+
+  const int nk = K / PK;
+  issue(0);
+  if (nk > 1) issue(1);
+  const int fr = lane & 15, fq = lane >> 4;
+  for (int kt = 0; kt < nk; ++kt) {
+    // this thread's loads of stage kt are done once at most the next stage's
+    // 12 loads are outstanding; the barrier then covers every thread's
+    // s_waitcnt encodes vmcnt in bits 3:0 and 15:14, lgkmcnt in 11:8, expcnt
+    // in 6:4; 0x0F7C = vmcnt(12), 0x0F70 = vmcnt(0), the others not waited on.
+    if (kt + 1 < nk) __builtin_amdgcn_s_waitcnt(0x0F7C);
+    else __builtin_amdgcn_s_waitcnt(0x0F70);
+    // a bare barrier: __syncthreads would also wait for the next stage's
+    // loads.  The empty asm keeps the compiler from moving LDS reads across.
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    if (kt + 2 < nk) issue(kt + 2);
+    const uint8_t* st = psm + (kt % PSTAGES) * kPStageBytes;
+    const uint8_t* sa = st + (wm * 128) * 128;
+    const uint8_t* sb = st + PM * 128 + (wn * 64) * 128;
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      const int chunk = 4 * kk + fq;
+      bf16x8_t af[8], bfr[4];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int r = 16 * i + fr;
+        af[i] = *reinterpret_cast<const bf16x8_t*>(sa + r * 128 + 16 * (chunk ^ (r & 7)));
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int r = 16 * j + fr;
+        bfr[j] = *reinterpret_cast<const bf16x8_t*>(sb + r * 128 + 16 * (chunk ^ (r & 7)));
+      }
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+    }
+  }
+
+  // 16 x 16 accumulator layout: lane holds rows 4 (lane / 16) + t, column lane % 16
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int n = n0 + wn * 64 + j * 16 + fr;
+    if (n >= N) continue;
+    const float b = bias ? bf16_to_f32(bias[n]) : 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const int m = m0 + wm * 128 + i * 16 + 4 * fq + t;
+        if (m < M) y[static_cast<int64_t>(m) * N + n] = static_cast<uint16_t>(f32_to_bf16(acc[i][j][t] + b));
+      }
+    }
+  }
+}
+
 // Any K (rows not 16-byte aligned): one thread per output, fp32 accumulation.
 __global__ __launch_bounds__(256) void gemm_bf16_nt_simple_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ wd,
@@ -123,7 +252,18 @@ __global__ __launch_bounds__(256) void gemm_bf16_nt_simple_kernel(
 
 hipError_t launch_gemm_bf16(const uint16_t* x, const uint16_t* wd, const uint16_t* bias,
                             uint16_t* y, int64_t M, int64_t N, int64_t K, hipStream_t s) {
-  if (K % 8 == 0 && M <= INT32_MAX && N <= INT32_MAX && K <= INT32_MAX) {
+  if (K % PK == 0 && M <= INT32_MAX && N <= INT32_MAX && K <= INT32_MAX) {
+    static bool attr_set = false;   // once per process: allow the 144 KB LDS ring
+    if (!attr_set) {
+      hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(gemm_bf16_pipe_kernel),
+                                         hipFuncAttributeMaxDynamicSharedMemorySize, kPLdsBytes);
+      if (e != hipSuccess) return e;
+      attr_set = true;
+    }
+    const int64_t tiles = ((M + PM - 1) / PM) * ((N + PN - 1) / PN);
+    gemm_bf16_pipe_kernel<<<dim3(static_cast<uint32_t>(tiles)), dim3(kThreads), kPLdsBytes, s>>>(
+        x, wd, bias, y, static_cast<int>(M), static_cast<int>(N), static_cast<int>(K));
+  } else if (K % 8 == 0 && M <= INT32_MAX && N <= INT32_MAX && K <= INT32_MAX) {
     const int64_t tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
     gemm_bf16_nt_kernel<<<dim3(static_cast<uint32_t>(tiles)), dim3(kThreads), 0, s>>>(
         x, wd, bias, y, static_cast<int>(M), static_cast<int>(N), static_cast<int>(K));

@@ -868,8 +868,9 @@ bool skinny_supported(const LinearArgs& a) { return a.M >= 1 && a.M <= 16; }
 hipError_t launch_linear_skinny(const LinearArgs& a, hipStream_t s) {
   if (!skinny_supported(a)) return hipErrorInvalidValue;
   if (rows_ok(a)) return a.asym ? launch_rows2<true>(a, s) : launch_rows2<false>(a, s);
-  if (mfma_ok(a)) {
-    if (a.M == 1) return launch_mfma2<1>(a, s);
+  // M = 1: the dot-product kernel streams rows fastest; M = 2..4: the
+  // matrix-core kernel, whose cost does not grow with M.
+  if (a.M >= 2 && mfma_ok(a)) {
     if (a.M == 2) return launch_mfma2<2>(a, s);
     return launch_mfma2<4>(a, s);
   }
@@ -878,6 +879,7 @@ hipError_t launch_linear_skinny(const LinearArgs& a, hipStream_t s) {
     if (a.M == 2) return launch_dot2<2>(a, s);
     return launch_dot2<4>(a, s);
   }
+  if (mfma_ok(a)) return launch_mfma2<1>(a, s);
   const dim3 grid(static_cast<uint32_t>((a.N + kGemvWaves - 1) / kGemvWaves));
   const dim3 block(kGemvWaves * kWave);
   if (a.asym) {
