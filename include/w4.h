@@ -79,9 +79,11 @@ const char* w4_last_error(void);
  * w4_quantize_pack — quantize W group-wise and pack the codes.
  *   (LoopQ packed_weight.py page: pack_weight; keras dense.py diff page:
  *    Dense.quantize, int4 branch with block_size.)
- *   w        [N, K] weights, fp32 (w_dtype = W4_F32) or bf16 (W4_BF16).
+ *   w        [N, K] finite weights, fp32 (w_dtype = W4_F32) or bf16 (W4_BF16);
+ *            codes of non-finite weights are unspecified.
  *   N, K     >= 1 (an empty matrix is rejected, as pack_weight rejects it).
- *   G        group size, 8 <= G <= 4096 and G % 8 == 0.
+ *   G        group size, 8 <= G <= 4096 and G % 8 == 0; at most 4096 groups
+ *            per row, ceil(K/G) <= 4096 (else W4_ERR_UNSUPPORTED).
  *   mode     W4_SYM or W4_ASYM.
  *   g_idx    int32 [K] or NULL (contiguous groups).  Group statistics run over
  *            the columns mapped to each group; a group no column maps to gets

@@ -335,6 +335,218 @@ __global__ __launch_bounds__(kDThreads) void dequantize_kernel(DequantArgs a, in
   }
 }
 
+// ---------------------------------------------------------------------------
+// Row quantizer for contiguous groups, G a power of two in [8, 512], rows of
+// 64 .. 8 * 8 * kQThreads columns.  One 256-thread workgroup per row; thread
+// t holds chunks t, t + 256, ... (eight columns each) in registers, so a
+// group is G / 8 consecutive lanes of one wave and its statistics are a lane
+// reduction (no LDS, no barrier).
+//
+// Loads.  A row starts OB = (n K es) mod 16 bytes past a 16-byte boundary.
+// OB is the same for the whole workgroup and selects a straight-line variant
+// that reads aligned 16-byte segments and shifts them into place.  A chunk's
+// segments can reach up to 48 bytes into the next row, so the last row of
+// the matrix is read element by element instead.
+//
+// Division.  Only rint(fp32(w / s)) is needed.  With r = rcp(s) (relative
+// error <= 2^-23) and t = fp32(w r): |w / s| <= 15 (1 + 2^-23), hence
+// |t - w / s| < 2^-18.4, and fp32(w / s) is within 2^-20 of w / s, so
+// |t - fp32(w / s)| < 2^-18.  When t is farther than 2^-16 from the nearest
+// half-integer, rint(t) == rint(fp32(w / s)); otherwise, and whenever r is
+// not finite, the chunk is redone with the IEEE division.  The codes are
+// therefore exactly those of the plain division (weights are finite).
+// ---------------------------------------------------------------------------
+constexpr float kTieMargin = 0.5f - 0x1p-16f;
+
+// max over the lanes of an aligned block of `lpg` lanes (a power of two <= 64)
+__device__ __forceinline__ float group_max(float m, int lpg) {
+  if (lpg > 1) m = fmaxf(m, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(m), 0xB1, 0xF, 0xF, false)));
+  if (lpg > 2) m = fmaxf(m, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(m), 0x4E, 0xF, 0xF, false)));
+  if (lpg > 4) m = fmaxf(m, __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(m), 0x1F | (4 << 10))));
+  if (lpg > 8) m = fmaxf(m, __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(m), 0x1F | (8 << 10))));
+  if (lpg > 16) m = fmaxf(m, __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(m), 0x1F | (16 << 10))));
+  if (lpg > 32) m = fmaxf(m, __shfl_xor(m, 32, kWave));
+  return m;
+}
+
+// The eight weights of chunk j (columns 8j .. 8j+7) of a row whose first byte
+// sits OB bytes past the 16-byte aligned pointer `rowA`.  OB < 0: element
+// loads from `row` (cnt valid columns).
+template <bool BF16, int OB>
+struct ChunkLoader {
+  static constexpr int kCB = BF16 ? 16 : 32;                 // bytes per chunk
+  static constexpr int kNS = kCB / 16 + (OB > 0 ? 1 : 0);    // aligned segments
+  u32x4 seg[kNS];
+  __device__ __forceinline__ void issue(const uint8_t* __restrict__ rowA, int j) {
+#pragma unroll
+    for (int s = 0; s < kNS; ++s) seg[s] = *reinterpret_cast<const u32x4*>(rowA + kCB * j + 16 * s);
+  }
+  __device__ __forceinline__ void unpack(float v[8]) const {
+    uint32_t d[4 * kNS];
+#pragma unroll
+    for (int s = 0; s < kNS; ++s)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) d[4 * s + i] = seg[s][i];
+    constexpr int q = (OB > 0 ? OB : 0) / 4, r = (OB > 0 ? OB : 0) % 4;
+    uint32_t w[kCB / 4];
+#pragma unroll
+    for (int k = 0; k < kCB / 4; ++k) w[k] = r == 0 ? d[q + k] : __builtin_amdgcn_alignbyte(d[q + k + 1], d[q + k], r);
+    if constexpr (BF16) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        v[2 * i] = __uint_as_float(w[i] << 16);
+        v[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v[i] = __uint_as_float(w[i]);
+    }
+  }
+};
+
+template <bool BF16, bool ASYM, int CH, int OB>
+__device__ __forceinline__ void quantize_row(const QuantArgs& a, int64_t n, int lpg) {
+  constexpr int kEs = BF16 ? 2 : 4;
+  const int K = static_cast<int>(a.K);
+  const int nchunks = (K + 7) / 8;
+  const int lane = lane_id();
+
+  // phase 1: every load of the thread in flight before any use
+  float v[CH][8];
+  if constexpr (OB >= 0) {
+    const uint8_t* rowA = static_cast<const uint8_t*>(a.w) + n * a.K * kEs - OB;
+    ChunkLoader<BF16, OB> ld[CH];
+#pragma unroll
+    for (int c = 0; c < CH; ++c) ld[c].issue(rowA, min(static_cast<int>(threadIdx.x) + c * kQThreads, nchunks - 1));
+#pragma unroll
+    for (int c = 0; c < CH; ++c) ld[c].unpack(v[c]);
+  } else {
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+      const int k0 = 8 * min(static_cast<int>(threadIdx.x) + c * kQThreads, nchunks - 1);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int k = min(k0 + e, K - 1);
+        v[c][e] = BF16 ? bf16_to_f32(static_cast<const uint16_t*>(a.w)[n * a.K + k])
+                       : static_cast<const float*>(a.w)[n * a.K + k];
+      }
+    }
+  }
+
+  const int64_t KB = (a.K + 1) / 2;
+#pragma unroll
+  for (int c = 0; c < CH; ++c) {
+    const int j = static_cast<int>(threadIdx.x) + c * kQThreads;
+    const int cnt = K - 8 * j;                 // valid columns of the chunk (> 8: all)
+    if (cnt < 8) {                             // row tail and idle lanes hold zeros
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[c][e] = e < cnt ? v[c][e] : 0.0f;
+    }
+    // group statistics: hi = max(0, max w), nl = max(0, max -w)  (signed: max |w|)
+    float m1 = 0.0f, m2 = 0.0f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      if constexpr (ASYM) {
+        m1 = fmaxf(m1, v[c][e]);
+        m2 = fmaxf(m2, -v[c][e]);
+      } else {
+        m1 = fmaxf(m1, fabsf(v[c][e]));
+      }
+    }
+    m1 = group_max(m1, lpg);
+    if constexpr (ASYM) m2 = group_max(m2, lpg);
+    float sc, zf = 8.0f;
+    if constexpr (ASYM) {
+      sc = (m1 + m2) / 15.0f;
+      if (sc == 0.0f) sc = 1.0f;
+      zf = fminf(fmaxf(rintf(m2 / sc), 0.0f), 15.0f);
+    } else {
+      sc = m1 / 7.0f;
+      if (sc == 0.0f) sc = 1.0f;
+    }
+    if (cnt <= 0) continue;
+    const float rc = __builtin_amdgcn_rcpf(sc);
+    float qf[8];
+    float dmax = 0.0f;                         // largest |t - rint(t)| over the chunk
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float t = v[c][e] * rc;
+      qf[e] = rintf(t);
+      dmax = fmaxf(dmax, fabsf(t - qf[e]));
+    }
+    // redo with the IEEE division the quotients that lie near a half-integer
+    // (about 1 weight in 300 for bf16 weights), or all of them when rc is not
+    // finite (s subnormal)
+    if (!(dmax < kTieMargin) || !(rc < __builtin_inff())) {
+      const bool all = !(rc < __builtin_inff());
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float t = v[c][e] * rc;
+        if (all || !(fabsf(t - qf[e]) < kTieMargin)) qf[e] = rintf(v[c][e] / sc);
+      }
+    }
+    // unsigned nibbles as bytes: q + z (zero-point), or q + 8 for signed codes
+    // (|w| <= 7 s there, so q is already in [-7, 7]; flipped back below)
+    uint32_t ev = 0, od = 0;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float x = ASYM ? fminf(fmaxf(qf[e] + zf, 0.0f), 15.0f) : qf[e] + 8.0f;
+      if (e & 1) od = __builtin_amdgcn_cvt_pk_u8_f32(x, e >> 1, od);
+      else ev = __builtin_amdgcn_cvt_pk_u8_f32(x, e >> 1, ev);
+    }
+    uint32_t packed = ev | (od << 4);
+    if constexpr (!ASYM) packed ^= 0x88888888u;
+    if (cnt < 8) packed &= (1u << (4 * cnt)) - 1u;   // the nibble past the row end stays 0
+    const int g = j / lpg;
+    if ((lane & (lpg - 1)) == 0) {
+      a.scales[n * a.NG + g] = sc;
+      if constexpr (ASYM) a.zeros[n * a.NG + g] = static_cast<uint8_t>(zf);
+    }
+    store_code_word(a.codes, n * KB + 4 * j, min(4, static_cast<int>(KB) - 4 * j), packed);
+  }
+}
+
+template <bool BF16, bool ASYM, int CH>
+__global__ __launch_bounds__(kQThreads) void quantize_rows_kernel(QuantArgs a, int lpg) {
+  const int64_t n = blockIdx.x;
+  if (n == a.N - 1) {
+    quantize_row<BF16, ASYM, CH, -1>(a, n, lpg);
+    return;
+  }
+  const int ob = static_cast<int>((n * a.K * (BF16 ? 2 : 4)) & 15);
+  if constexpr (BF16) {
+    switch (ob) {
+      case 0: quantize_row<BF16, ASYM, CH, 0>(a, n, lpg); break;
+      case 2: quantize_row<BF16, ASYM, CH, 2>(a, n, lpg); break;
+      case 4: quantize_row<BF16, ASYM, CH, 4>(a, n, lpg); break;
+      case 6: quantize_row<BF16, ASYM, CH, 6>(a, n, lpg); break;
+      case 8: quantize_row<BF16, ASYM, CH, 8>(a, n, lpg); break;
+      case 10: quantize_row<BF16, ASYM, CH, 10>(a, n, lpg); break;
+      case 12: quantize_row<BF16, ASYM, CH, 12>(a, n, lpg); break;
+      default: quantize_row<BF16, ASYM, CH, 14>(a, n, lpg); break;
+    }
+  } else {
+    switch (ob) {
+      case 0: quantize_row<BF16, ASYM, CH, 0>(a, n, lpg); break;
+      case 4: quantize_row<BF16, ASYM, CH, 4>(a, n, lpg); break;
+      case 8: quantize_row<BF16, ASYM, CH, 8>(a, n, lpg); break;
+      default: quantize_row<BF16, ASYM, CH, 12>(a, n, lpg); break;
+    }
+  }
+}
+
+template <bool BF16, bool ASYM>
+hipError_t launch_qrows(const QuantArgs& a, hipStream_t s) {
+  const int lpg = static_cast<int>(a.G / 8);
+  const int64_t nchunks = (a.K + 7) / 8;
+  const dim3 grid(static_cast<uint32_t>(a.N)), block(kQThreads);
+  if (nchunks <= 1 * kQThreads) quantize_rows_kernel<BF16, ASYM, 1><<<grid, block, 0, s>>>(a, lpg);
+  else if (nchunks <= 2 * kQThreads) quantize_rows_kernel<BF16, ASYM, 2><<<grid, block, 0, s>>>(a, lpg);
+  else if (nchunks <= 4 * kQThreads) quantize_rows_kernel<BF16, ASYM, 4><<<grid, block, 0, s>>>(a, lpg);
+  else quantize_rows_kernel<BF16, ASYM, 8><<<grid, block, 0, s>>>(a, lpg);
+  return hipGetLastError();
+}
+
 template <bool BF16, bool ASYM, bool GIDX>
 hipError_t launch_q3(const QuantArgs& a, hipStream_t s) {
   const size_t lds = static_cast<size_t>(a.NG) * 4 * sizeof(uint32_t);
@@ -355,7 +567,155 @@ hipError_t launch_q3(const QuantArgs& a, hipStream_t s) {
 
 template <bool BF16, bool ASYM>
 hipError_t launch_q2(const QuantArgs& a, hipStream_t s) {
-  return a.g_idx ? launch_q3<BF16, ASYM, true>(a, s) : launch_q3<BF16, ASYM, false>(a, s);
+  if (a.g_idx) return launch_q3<BF16, ASYM, true>(a, s);
+  // fast path: contiguous power-of-two groups of at most 512 columns, rows
+  // of at most 2048 * 8 columns
+  const bool pow2 = (a.G & (a.G - 1)) == 0;
+  if (pow2 && a.G >= 8 && a.G <= 512 && a.K >= 64 && a.K <= 8 * 8 * kQThreads) return launch_qrows<BF16, ASYM>(a, s);
+  return launch_q3<BF16, ASYM, false>(a, s);
+}
+
+// ---------------------------------------------------------------------------
+// Row dequantizer for contiguous power-of-two groups and rows of at least
+// 1024 columns; one workgroup per row.  Lane l of a wave decodes column chunk
+// i = B + l - 1 (eight columns from a multiple of 8: one code dword, one
+// group).  The output is written in the 16-byte chunks of the flattened
+// [N, K] array: output chunk i of the row holds its last SFT columns of
+// column chunk i - 1 and the first 8 - SFT of chunk i, SFT = (n K) mod 8 being
+// the same for the whole row, so each lane takes the words it needs from its
+// left neighbour (one-lane wave shift) and funnel-shifts them into place.
+// Lane 0 only feeds lane 1: a wave step writes 63 output chunks.  The first
+// and last output chunks of a row are shared with the neighbouring rows and
+// are written element by element (each row writes only its own elements).
+// ---------------------------------------------------------------------------
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+  return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(static_cast<int>(v), static_cast<int>(v), CTRL, 0xF, 0xF, false));
+}
+constexpr int kWaveShr1 = 0x138;   // lane l receives lane l - 1
+
+template <bool OUT_BF16, bool ASYM, int SFT>
+__device__ __forceinline__ void dequantize_row(const DequantArgs& a, int64_t n, int lg) {
+  const int K = static_cast<int>(a.K);
+  const int nch = (K + 7) / 8;                       // column chunks of the row
+  const int J = (K - 1 + SFT) / 8 + 1;              // output chunks touching the row
+  const int64_t e0 = n * a.K;
+  const int64_t f0 = e0 >> 3;
+  const int64_t KB = (a.K + 1) / 2;
+  const int64_t cb = n * KB;                         // row's first code byte
+  const int cadj = static_cast<int>(cb & 3);
+  const uint8_t* cbase = a.codes + (cb - cadj);
+  const int64_t total = a.N * KB;
+  const bool last = n == a.N - 1;
+  const float* srow = a.scales + n * a.NG;
+  const uint8_t* zrow = ASYM ? a.zeros + n * a.NG : nullptr;
+  const int lane = lane_id();
+  const int wave = threadIdx.x / kWave;
+  constexpr int kWaves = kDThreads / kWave;
+
+  for (int B = 63 * wave; B < J; B += 63 * kWaves) {
+    const int i = B + lane - 1;
+    const int ic = min(max(i, 0), nch - 1);
+    // the chunk's code word (bytes 4 ic .. 4 ic + 3 of the row)
+    uint32_t d;
+    if (!last) {
+      const uint32_t d0 = *reinterpret_cast<const uint32_t*>(cbase + 4 * ic);
+      d = d0;
+      if (cadj) d = __builtin_amdgcn_alignbyte(*reinterpret_cast<const uint32_t*>(cbase + 4 * ic + 4), d0, cadj);
+    } else {                                         // stay inside the buffer
+      d = 0;
+#pragma unroll
+      for (int b = 0; b < 4; ++b)
+        d |= static_cast<uint32_t>(a.codes[min(cb + 4 * ic + b, total - 1)]) << (8 * b);
+    }
+    const int g = (8 * ic) >> lg;
+    const float s = srow[g];
+    float o[8];
+    if constexpr (ASYM) {
+      const float z = static_cast<float>(zrow[g]);
+      const uint32_t lo = d & 0x0F0F0F0Fu, hi = (d >> 4) & 0x0F0F0F0Fu;
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        o[e] = (static_cast<float>((((e & 1) ? hi : lo) >> (8 * (e >> 1))) & 0xFFu) - z) * s;
+    } else {
+      // u = q + 8 in [0, 15]; fma(u, s, -8 s) rounds (u - 8) s once, as the
+      // plain product does (-8 s is exact unless it overflows)
+      d ^= 0x88888888u;
+      const uint32_t lo = d & 0x0F0F0F0Fu, hi = (d >> 4) & 0x0F0F0F0Fu;
+      const float m8 = -8.0f * s;
+      if (fabsf(m8) < __builtin_inff()) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          o[e] = __builtin_fmaf(static_cast<float>((((e & 1) ? hi : lo) >> (8 * (e >> 1))) & 0xFFu), s, m8);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          o[e] = (static_cast<float>((((e & 1) ? hi : lo) >> (8 * (e >> 1))) & 0xFFu) - 8.0f) * s;
+      }
+    }
+
+    // words of column chunk i, then those of chunk i - 1 from the left lane
+    constexpr int kW = OUT_BF16 ? 4 : 8;             // 32-bit words per chunk
+    uint32_t P[kW], C[2 * kW];
+    if constexpr (OUT_BF16) {
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const bf16x2_t p = {static_cast<__bf16>(o[2 * k]), static_cast<__bf16>(o[2 * k + 1])};
+        P[k] = __builtin_bit_cast(uint32_t, p);
+      }
+    } else {
+#pragma unroll
+      for (int k = 0; k < 8; ++k) P[k] = __float_as_uint(o[k]);
+    }
+    // output element m = concatenated element (8 - SFT + m) of [chunk i-1 | chunk i]
+    constexpr int kByte = (8 - SFT) * (OUT_BF16 ? 2 : 4);   // byte offset into the 2 kW words
+    constexpr int kW0 = kByte / 4, kR = kByte % 4;
+#pragma unroll
+    for (int k = 0; k < kW; ++k) C[kW + k] = P[k];
+#pragma unroll
+    for (int k = 0; k < kW; ++k) C[k] = k >= kW0 ? dpp_u32<kWaveShr1>(P[k]) : 0u;
+    uint32_t out[kW];
+#pragma unroll
+    for (int k = 0; k < kW; ++k)
+      out[k] = kR == 0 ? C[kW0 + k] : __builtin_amdgcn_alignbyte(C[kW0 + k + 1], C[kW0 + k], kR);
+
+    const int j = i;                                 // output chunk written by this lane
+    if (lane == 0 || j >= J) continue;
+    const int c0 = 8 * j - SFT;                      // column of its element 0
+    if (c0 >= 0 && c0 + 8 <= K) {
+      if constexpr (OUT_BF16) {
+        *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(a.out) + 8 * (f0 + j)) = u32x4{out[0], out[1], out[2], out[3]};
+      } else {
+        u32x4* dst = reinterpret_cast<u32x4*>(static_cast<float*>(a.out) + 8 * (f0 + j));
+        dst[0] = u32x4{out[0], out[1], out[2], out[3]};
+        dst[1] = u32x4{out[4], out[5], out[6], out[7]};
+      }
+    } else {
+#pragma unroll
+      for (int m = 0; m < 8; ++m) {
+        const int col = c0 + m;
+        if (col >= 0 && col < K) {
+          if constexpr (OUT_BF16) static_cast<uint16_t*>(a.out)[e0 + col] = static_cast<uint16_t>(out[m / 2] >> (16 * (m & 1)));
+          else static_cast<uint32_t*>(a.out)[e0 + col] = out[m];
+        }
+      }
+    }
+  }
+}
+
+template <bool OUT_BF16, bool ASYM>
+__global__ __launch_bounds__(kDThreads) void dequantize_rows_kernel(DequantArgs a, int lg) {
+  const int64_t n = blockIdx.x;
+  switch (static_cast<int>((n * a.K) & 7)) {
+    case 0: dequantize_row<OUT_BF16, ASYM, 0>(a, n, lg); break;
+    case 1: dequantize_row<OUT_BF16, ASYM, 1>(a, n, lg); break;
+    case 2: dequantize_row<OUT_BF16, ASYM, 2>(a, n, lg); break;
+    case 3: dequantize_row<OUT_BF16, ASYM, 3>(a, n, lg); break;
+    case 4: dequantize_row<OUT_BF16, ASYM, 4>(a, n, lg); break;
+    case 5: dequantize_row<OUT_BF16, ASYM, 5>(a, n, lg); break;
+    case 6: dequantize_row<OUT_BF16, ASYM, 6>(a, n, lg); break;
+    default: dequantize_row<OUT_BF16, ASYM, 7>(a, n, lg); break;
+  }
 }
 
 template <bool OUT_BF16, bool ASYM, int GIDX>
@@ -370,7 +730,15 @@ hipError_t launch_d3(const DequantArgs& a, hipStream_t s) {
 
 template <bool OUT_BF16, bool ASYM>
 hipError_t launch_d2(const DequantArgs& a, hipStream_t s) {
-  if (!a.g_idx) return launch_d3<OUT_BF16, ASYM, 0>(a, s);
+  if (!a.g_idx) {
+    if ((a.G & (a.G - 1)) == 0 && a.K >= 1024) {
+      int lg = 0;
+      while ((int64_t{1} << lg) < a.G) ++lg;
+      dequantize_rows_kernel<OUT_BF16, ASYM><<<dim3(static_cast<uint32_t>(a.N)), dim3(kDThreads), 0, s>>>(a, lg);
+      return hipGetLastError();
+    }
+    return launch_d3<OUT_BF16, ASYM, 0>(a, s);
+  }
   if (a.NG <= kDequantLdsGroups) return launch_d3<OUT_BF16, ASYM, 1>(a, s);
   return launch_d3<OUT_BF16, ASYM, 2>(a, s);
 }

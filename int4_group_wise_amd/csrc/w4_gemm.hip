@@ -169,16 +169,20 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_pipe_kernel(
     for (int p = 0; p < 4; ++p) lds_dma16(bsrc[p] + k0, st + PM * 128 + (32 * wid + 8 * p) * 128);
   };
 
-  f32x4_t acc[8][4];
+  // wave tile 128 x 64 = 4 x 2 tiles of 32 x 32 (v_mfma_f32_32x32x16_bf16,
+  // which sustains a higher rate than 16 x 16 x 32 with one wave per SIMD)
+  f32x16_t acc[4][2];
 #pragma unroll
-  for (int i = 0; i < 8; ++i)
+  for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
 
   const int nk = K / PK;
   issue(0);
   if (nk > 1) issue(1);
-  const int fr = lane & 15, fq = lane >> 4;
+  const int fr = lane & 31, fh = lane >> 5;
   for (int kt = 0; kt < nk; ++kt) {
     // this thread's loads of stage kt are done once at most the next stage's
     // 12 loads are outstanding; the barrier then covers every thread's
@@ -195,40 +199,46 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_pipe_kernel(
     const uint8_t* st = psm + (kt % PSTAGES) * kPStageBytes;
     const uint8_t* sa = st + (wm * 128) * 128;
     const uint8_t* sb = st + PM * 128 + (wn * 64) * 128;
+    // Fragments of all four 16-column sub-steps are read up front, so later
+    // sub-steps' reads are in flight while earlier MFMAs run.  32 x 32 x 16
+    // operand layout: lane l holds row (or column) l % 32, k = 8 (l / 32) + e.
+    bf16x8_t af[4][4], bfr[4][2];
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-      const int chunk = 4 * kk + fq;
-      bf16x8_t af[8], bfr[4];
+    for (int ks = 0; ks < 4; ++ks) {
+      const int chunk = 2 * ks + fh;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int r = 16 * i + fr;
-        af[i] = *reinterpret_cast<const bf16x8_t*>(sa + r * 128 + 16 * (chunk ^ (r & 7)));
+      for (int j = 0; j < 2; ++j) {
+        const int r = 32 * j + fr;
+        bfr[ks][j] = *reinterpret_cast<const bf16x8_t*>(sb + r * 128 + 16 * (chunk ^ (r & 7)));
       }
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int r = 16 * j + fr;
-        bfr[j] = *reinterpret_cast<const bf16x8_t*>(sb + r * 128 + 16 * (chunk ^ (r & 7)));
+      for (int i = 0; i < 4; ++i) {
+        const int r = 32 * i + fr;
+        af[ks][i] = *reinterpret_cast<const bf16x8_t*>(sa + r * 128 + 16 * (chunk ^ (r & 7)));
       }
-#pragma unroll
-      for (int i = 0; i < 8; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
     }
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[ks][i], bfr[ks][j], acc[i][j], 0, 0, 0);
   }
 
-  // 16 x 16 accumulator layout: lane holds rows 4 (lane / 16) + t, column lane % 16
+  // 32 x 32 accumulator layout: register v of lane l holds row
+  // 8 (v / 4) + 4 (l / 32) + v % 4, column l % 32.
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int n = n0 + wn * 64 + j * 16 + fr;
+  for (int j = 0; j < 2; ++j) {
+    const int n = n0 + wn * 64 + j * 32 + fr;
     if (n >= N) continue;
     const float b = bias ? bf16_to_f32(bias[n]) : 0.0f;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < 4; ++i) {
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const int m = m0 + wm * 128 + i * 16 + 4 * fq + t;
-        if (m < M) y[static_cast<int64_t>(m) * N + n] = static_cast<uint16_t>(f32_to_bf16(acc[i][j][t] + b));
+      for (int v = 0; v < 16; ++v) {
+        const int m = m0 + wm * 128 + i * 32 + 8 * (v / 4) + 4 * fh + (v % 4);
+        if (m < M) y[static_cast<int64_t>(m) * N + n] = static_cast<uint16_t>(f32_to_bf16(acc[i][j][v] + b));
       }
     }
   }

@@ -188,6 +188,64 @@ def test_codec_alignment_classes_and_long_rows():
             _check_codec(w, G, mode, label=f"{N}x{K} G{G} {dt} {mode}")
 
 
+CODEC_SHAPES = [
+    # N, K, G, weight dtype: row-register quantizer (power-of-two G <= 512,
+    # K <= 16384) and flat dequantizer (K >= 2048) around their edges
+    (5, 2048, 8, torch.float32), (7, 2049, 32, torch.bfloat16), (3, 2050, 512, torch.float32),
+    (6, 4100, 128, torch.bfloat16), (4, 3000, 256, torch.float32), (3, 16384, 512, torch.bfloat16),
+    (2, 16383, 8, torch.float32), (3, 16385, 64, torch.bfloat16), (9, 2047, 16, torch.bfloat16),
+    (13, 2111, 64, torch.float32), (3, 6000, 48, torch.bfloat16),
+]
+
+
+@pytest.mark.parametrize("shape", CODEC_SHAPES, ids=lambda c: "N%d_K%d_G%d_%s" % (c[0], c[1], c[2], str(c[3])[6:]))
+def test_codec_fast_paths(shape):
+    N, K, G, dt = shape
+    g = torch.Generator().manual_seed(K + G)
+    w = (torch.randn(N, K, generator=g) * 0.05).to(dt)
+    for mode in ("sym", "asym"):
+        _check_codec(w, G, mode, label=f"{N}x{K} G{G} {dt} {mode}")
+
+
+def test_codec_near_rounding_ties():
+    """Weights at and a few ulps either side of (q + 1/2) times the scale,
+    where the last bit of the quotient decides the code.  Scales have short
+    significands so that each group's range pins them exactly."""
+    N, K, G = 6, 4096, 32
+    NG = K // G
+    rng = np.random.default_rng(11)
+    s = (rng.integers(2 ** 12, 2 ** 16, size=(N, NG)) * 2.0 ** rng.integers(-40, 0, size=(N, NG))).astype(np.float32)
+    sk = np.repeat(s, G, axis=1).astype(np.float64)
+    for mode, lo, hi in (("sym", -7, 6), ("asym", -8, 6)):
+        q = rng.integers(lo, hi + 1, size=(N, K)).astype(np.float64) + 0.5
+        w = (q * sk).astype(np.float32)
+        step = rng.integers(-2, 3, size=(N, K)).astype(np.int32)
+        w = (w.view(np.int32) + step).view(np.float32)
+        w[:, ::G] = 7.0 * s                      # max: 7 s
+        w[:, 1::G] = -7.0 * s if mode == "sym" else -8.0 * s
+        for dt in (torch.float32, torch.bfloat16):
+            _check_codec(torch.from_numpy(w).to(dt), G, mode, label=f"ties {mode} {dt}")
+
+
+def test_dequantize_act_order_large_group_table():
+    """More groups per row than the staged act-order table holds (G = 8,
+    8200 groups): the dequantizer gathers scales from global memory."""
+    N, K, G = 3, 65600, 8
+    rng = np.random.default_rng(12)
+    gnp = (rng.permutation(K) // G).astype(np.int32)
+    w = rng.standard_normal((N, K)).astype(np.float32) * 0.02
+    for mode in (O.SYM, O.ASYM):
+        # w4_quantize_pack takes at most 4096 groups per row; these codes come from the oracle
+        oc, osc, oz = O.quantize_pack(w, G, mode, gnp)
+        zeros = None if oz is None else torch.from_numpy(oz).to(DEV)
+        for dt, kind in ((torch.bfloat16, "bf16"), (torch.float32, "f32")):
+            d = w4.dequantize(torch.from_numpy(oc).to(DEV), torch.from_numpy(osc).to(DEV), zeros,
+                              torch.from_numpy(gnp).to(DEV), K, G, mode, dt).cpu()
+            ref = O.dequantize(oc, osc, oz, gnp, K, G, mode, kind)
+            got = _bits(d) if kind == "bf16" else d.numpy().view(np.uint32)
+            assert np.array_equal(got, ref if kind == "bf16" else ref.view(np.uint32)), f"{mode} {kind}"
+
+
 def test_codec_degenerate_values():
     """All-zero groups, one-signed groups, exact ties, tiny (subnormal-scale)
     and large magnitudes."""
@@ -200,9 +258,11 @@ def test_codec_degenerate_values():
     w[5] = torch.randn(K, generator=torch.Generator().manual_seed(2)) * 1e30
     w[6, ::7] = 1.0                                           # sparse
     w[7] = -0.0
+    wide = w.repeat(1, 2048 // K)                             # the same rows at K = 2048
     for mode in ("sym", "asym"):
-        _check_codec(w, G, mode, label=f"degenerate {mode}")
-        _check_codec(w.to(torch.bfloat16), G, mode, label=f"degenerate bf16 {mode}")
+        for x, lab in ((w, ""), (wide, " wide")):
+            _check_codec(x, G, mode, label=f"degenerate{lab} {mode}")
+            _check_codec(x.to(torch.bfloat16), G, mode, label=f"degenerate{lab} bf16 {mode}")
 
 
 def test_act_order_with_unused_groups():
