@@ -161,26 +161,21 @@ __device__ __forceinline__ void use_slice(const Slice& s, const XSlice<MT>& x, b
   }
 }
 
-// Work split: a workgroup's 4 waves form 4 / KS row groups of kGemvRows rows;
-// the KS waves of a row group take alternate 2048-column chunks of K, and
-// their partial row sums are added through LDS at the end.  Per chunk a lane
-// first issues the loads of its activations (L2-resident), then the code
-// words, scales and zero-points; loads retire in order, so re-pairing the
-// activations waits only for them.  The next chunk's loads are issued before
-// the current chunk's arithmetic.
-template <int MT, bool ASYM, int KS>
+// Each round covers two 2048-column chunks.  A lane first issues the loads of
+// its activations (L2-resident), then the code words, scales and zero-points
+// of both chunks (HBM); loads retire in order, so re-pairing the activations
+// waits only for them, and the arithmetic of the first chunk overlaps the
+// second chunk's transfer.
+template <int MT, bool ASYM>
 __global__ __launch_bounds__(kGemvWaves * kWave) void gemv_dot2_kernel(LinearArgs a) {
-  __shared__ float red[kGemvWaves][kGemvRows][MT];
   const int lane = lane_id();
-  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int rg = w / KS, part = w % KS;
-  const int64_t row0 = (static_cast<int64_t>(blockIdx.x) * (kGemvWaves / KS) + rg) * kGemvRows;
-  const bool active = row0 < a.N;                  // idle waves still reach the barrier
-  const int units = static_cast<int>(a.K / 32);    // 32-column slices per row
-  const int nchunks = (units + kWave - 1) / kWave;
+  const int64_t wave = static_cast<int64_t>(blockIdx.x) * kGemvWaves +
+                       __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int64_t row0 = wave * kGemvRows;
+  if (row0 >= a.N) return;
+  const int units = static_cast<int>(a.K / 32);   // 32-column slices per row
   const int M = static_cast<int>(a.M);
   const uint32_t mask = nibble_mask();
-  const int64_t rbase = active ? row0 : 0;
 
   float tot[kGemvRows][MT];
 #pragma unroll
@@ -188,59 +183,39 @@ __global__ __launch_bounds__(kGemvWaves * kWave) void gemv_dot2_kernel(LinearArg
 #pragma unroll
     for (int m = 0; m < MT; ++m) tot[r][m] = 0.0f;
 
-  // Slices past the row end (K not a multiple of 2048) load the last slice
+  // Slices past the row end (K not a multiple of 4096) load the last slice
   // again and are discarded, so the loads need no branches: a branch would
   // end the basic block and force an early wait for all outstanding loads.
-  int c = part;
-  XSlice<MT> xa;
-  Slice sa;
-  if (c < nchunks) {
-    const int ca = min(c * kWave + lane, units - 1);
+  for (int u0 = 0; u0 < units; u0 += 2 * kWave) {
+    const int ua = u0 + lane, ub = u0 + kWave + lane;
+    const int ca = min(ua, units - 1), cb = min(ub, units - 1);
+    XSlice<MT> xa, xb;
+    Slice sa, sb;
+    // Issue order = use order (loads retire in order); the scheduling
+    // barriers keep the compiler from regrouping them.
     load_x<MT>(a, ca, M, xa);
+    load_x<MT>(a, cb, M, xb);
     __builtin_amdgcn_sched_barrier(0);
-    load_slice<ASYM>(a, rbase, ca, sa);
+    load_slice<ASYM>(a, row0, ca, sa);
     __builtin_amdgcn_sched_barrier(0);
-  }
-  for (; c < nchunks; c += KS) {
-    const int ua = c * kWave + lane;
-    const int cn = c + KS;
-    XSlice<MT> xb;
-    Slice sb;
-    if (cn < nchunks) {                              // prefetch the next chunk
-      const int cb = min(cn * kWave + lane, units - 1);
-      load_x<MT>(a, cb, M, xb);
-      __builtin_amdgcn_sched_barrier(0);
-      load_slice<ASYM>(a, rbase, cb, sb);
-      __builtin_amdgcn_sched_barrier(0);
-    }
+    load_slice<ASYM>(a, row0, cb, sb);
+    __builtin_amdgcn_sched_barrier(0);
     pair_xslice<MT>(xa);
     use_slice<MT, ASYM>(sa, xa, ua < units, mask, tot);
-    xa = xb;
-    sa = sb;
+    pair_xslice<MT>(xb);
+    use_slice<MT, ASYM>(sb, xb, ub < units, mask, tot);
   }
 
 #pragma unroll
-  for (int r = 0; r < kGemvRows; ++r)
+  for (int r = 0; r < kGemvRows; ++r) {
 #pragma unroll
     for (int m = 0; m < MT; ++m) {
       const float v = wave_sum(tot[r][m]);
-      if (KS > 1 && lane == 0) red[w][r][m] = v;
-      tot[r][m] = v;
-    }
-  if constexpr (KS > 1) __syncthreads();
-  if (!active || part != 0 || lane != 0) return;
-#pragma unroll
-  for (int r = 0; r < kGemvRows; ++r) {
-    const int64_t n = row0 + r;
-    if (n >= a.N) continue;
-    const float b = a.bias ? bf16_to_f32(a.bias[n]) : 0.0f;
-#pragma unroll
-    for (int m = 0; m < MT; ++m) {
-      if (m >= M) continue;
-      float v = tot[r][m];
-#pragma unroll
-      for (int p = 1; p < KS; ++p) v += red[w + p][r][m];
-      a.y[static_cast<int64_t>(m) * a.N + n] = static_cast<uint16_t>(f32_to_bf16(v + b));
+      const int64_t n = row0 + r;
+      if (lane == 0 && n < a.N && m < M) {
+        const float b = a.bias ? bf16_to_f32(a.bias[n]) : 0.0f;
+        a.y[static_cast<int64_t>(m) * a.N + n] = static_cast<uint16_t>(f32_to_bf16(v + b));
+      }
     }
   }
 }
@@ -784,23 +759,16 @@ __global__ __launch_bounds__(kGemvWaves * kWave) void gemv_generic_kernel(Linear
   }
 }
 
-template <int MT, int KS>
-hipError_t launch_dot2_ks(const LinearArgs& a, hipStream_t s) {
-  const int64_t groups = (a.N + kGemvRows - 1) / kGemvRows;
-  const dim3 grid(static_cast<uint32_t>((groups + kGemvWaves / KS - 1) / (kGemvWaves / KS)));
-  const dim3 block(kGemvWaves * kWave);
-  if (a.asym)
-    gemv_dot2_kernel<MT, true, KS><<<grid, block, 0, s>>>(a);
-  else
-    gemv_dot2_kernel<MT, false, KS><<<grid, block, 0, s>>>(a);
-  return hipGetLastError();
-}
-
-// K is split over two waves per row group when a row has at least two
-// 2048-column chunks.
 template <int MT>
 hipError_t launch_dot2(const LinearArgs& a, hipStream_t s) {
-  return a.K > 2048 ? launch_dot2_ks<MT, 2>(a, s) : launch_dot2_ks<MT, 1>(a, s);
+  const int64_t waves = (a.N + kGemvRows - 1) / kGemvRows;
+  const dim3 grid(static_cast<uint32_t>((waves + kGemvWaves - 1) / kGemvWaves));
+  const dim3 block(kGemvWaves * kWave);
+  if (a.asym)
+    gemv_dot2_kernel<MT, true><<<grid, block, 0, s>>>(a);
+  else
+    gemv_dot2_kernel<MT, false><<<grid, block, 0, s>>>(a);
+  return hipGetLastError();
 }
 
 template <int MT, bool ASYM, bool TR, int GU>
