@@ -94,7 +94,9 @@ def f32_to_bf16_bits(x) -> np.ndarray:
     Written as the definition: the two bf16 neighbours are the fp32 value
     truncated to 16 bits (toward zero) and the next bf16 away from zero; pick
     the nearer one, and on a tie the one whose last significand bit is 0.
-    Distances are exact in fp64.
+    Distances are exact in fp64.  As IEEE 754 rounds as if the exponent range
+    were unbounded, the neighbour past the largest finite bf16 counts as
+    2^128 and a value rounding to it becomes infinity.
     """
     x = np.ascontiguousarray(x, dtype=F32)
     u = x.view(np.uint32)
@@ -104,6 +106,7 @@ def f32_to_bf16_bits(x) -> np.ndarray:
     lo = np.abs(toward_zero.view(F32).astype(np.float64))
     with np.errstate(over="ignore", invalid="ignore"):
         hi = np.abs(away.view(F32).astype(np.float64))
+        hi = np.where(np.isinf(hi), 2.0 ** 128, hi)
         d_lo = mag - lo
         d_hi = hi - mag
     even_lo = ((toward_zero >> np.uint32(16)) & np.uint32(1)) == 0

@@ -80,6 +80,9 @@ def test_bf16_rounding_matches_torch():
         (rng.standard_normal(50000) * 1e-39).astype(F32),     # fp32 subnormals
         (rng.standard_normal(50000) * 1e30).astype(F32),
         np.array([0.0, -0.0, 1.0, -1.0, 3.0e38, -3.0e38], F32),
+        # largest bf16 and the values that round past it to infinity
+        np.array([0x7F7F0000, 0x7F7F7FFF, 0x7F7F8000, 0x7F7FFFFF,
+                  0xFF7F7FFF, 0xFF7F8000, 0xFF7FFFFF], np.uint32).view(F32),
     ]
     # exact ties: low 16 bits = 0x8000, both parities of bit 16
     u = rng.integers(0, 2**32, 100000, dtype=np.uint64).astype(np.uint32)
