@@ -157,6 +157,10 @@ CASES = [
     (5, 70, 640, 32, "asym", False, "f32", "randn"),     # batch tail (5 blocks of 128 columns)
     (12, 200, 1024, 256, "sym", False, "bf16", "none"),
     (16, 64, 8192, 64, "sym", False, "f32", "none"),
+    (1, 37, 2048, 64, "asym", False, "f32", "randn"),   # staged decode, row tail
+    (1, 50, 4096, 256, "sym", False, "bf16", "none"),   # staged decode, signed
+    (1, 24, 16384, 256, "asym", False, "f32", "randn"), # staged decode, longest row, 64 groups
+    (1, 8, 640, 32, "sym", False, "f32", "randn"),      # staged decode, partial round
     (1, 64, 512, 128, "asym", True, "f32", "none"),     # act-order decode
     (16, 48, 1000, 40, "asym", True, "bf16", "none"),
     (17, 130, 200, 8, "asym", False, "f32", "randn"),   # prefill, K % 64 != 0, N tail
