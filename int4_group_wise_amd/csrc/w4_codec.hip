@@ -718,6 +718,135 @@ __global__ __launch_bounds__(kDThreads) void dequantize_rows_kernel(DequantArgs 
   }
 }
 
+// ---------------------------------------------------------------------------
+// Act-order dequantizer.  A workgroup owns kActRows rows x 2048 columns.  It
+// first builds, for each (row, group), the 16 possible outputs of that group
+// (value(u) * s rounded to the output type) as a table in LDS; then each
+// thread takes 8 columns, loads their 8 group indices once, and for each of
+// the rows turns every nibble into one table lookup.  The group indices are
+// read once per 16 rows instead of once per row, and the per-weight work is a
+// shift, a mask and an LDS read.
+// ---------------------------------------------------------------------------
+constexpr int kActRows = 8;
+
+template <bool OUT_BF16>
+__host__ __device__ constexpr int act_entry_bytes() { return OUT_BF16 ? 2 : 4; }
+
+// rows of table a workgroup can hold for NG groups in 64 KB of LDS (0: none)
+template <bool OUT_BF16>
+__host__ __device__ inline int act_rows(int64_t NG) {
+  const int64_t per_row = NG * 16 * act_entry_bytes<OUT_BF16>();
+  const int64_t r = 65536 / per_row;
+  return static_cast<int>(r >= kActRows ? kActRows : r);
+}
+
+template <bool OUT_BF16, bool ASYM>
+__global__ __launch_bounds__(kDThreads) void dequantize_act_kernel(DequantArgs a, int rows) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t tsm[];
+  constexpr int kEB = act_entry_bytes<OUT_BF16>();
+  const int NG = static_cast<int>(a.NG);
+  const int K = static_cast<int>(a.K);
+  const int64_t row0 = static_cast<int64_t>(blockIdx.y) * rows;
+  const int nrows = static_cast<int>(min(static_cast<int64_t>(rows), a.N - row0));
+
+  // 1. this thread's 8 columns (chunk j): group offsets and every row's code
+  //    word, loaded before the table is built so that both latencies overlap
+  const int j = blockIdx.x * kDThreads + threadIdx.x;
+  const int k0 = 8 * j;
+  const bool live = k0 < K;
+  const int cnt = live ? min(8, K - k0) : 0;
+  // byte offset of each column's group inside a row's table
+  uint32_t goff[8];
+  if (!live) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) goff[e] = 0;
+  } else if (cnt == 8) {
+    const u32x4 g0 = *reinterpret_cast<const u32x4*>(a.g_idx + k0);
+    const u32x4 g1 = *reinterpret_cast<const u32x4*>(a.g_idx + k0 + 4);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      goff[e] = static_cast<uint32_t>(min(max(static_cast<int>(g0[e]), 0), NG - 1)) * 16 * kEB;
+      goff[4 + e] = static_cast<uint32_t>(min(max(static_cast<int>(g1[e]), 0), NG - 1)) * 16 * kEB;
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      goff[e] = static_cast<uint32_t>(min(max(a.g_idx[min(k0 + e, K - 1)], 0), NG - 1)) * 16 * kEB;
+  }
+
+  const int64_t KB = (a.K + 1) / 2;
+  // every row's code word first (in flight together), then the lookups
+  uint32_t dw[kActRows];
+  if (cnt == 8 && (KB & 3) == 0) {               // aligned words; rows past the end reload the last
+#pragma unroll
+    for (int r = 0; r < kActRows; ++r)
+      dw[r] = *reinterpret_cast<const uint32_t*>(a.codes + (row0 + min(r, nrows - 1)) * KB + 4 * j);
+  } else {
+#pragma unroll
+    for (int r = 0; r < kActRows; ++r) {
+      dw[r] = 0;
+      if (live && r < nrows) {
+        const int64_t off = (row0 + r) * KB + 4 * j;
+        for (int b = 0; b < (cnt + 1) / 2; ++b) dw[r] |= static_cast<uint32_t>(a.codes[off + b]) << (8 * b);
+      }
+    }
+  }
+  // 2. table: entry (r, g, u) at byte ((r * NG + g) * 16 + u) * kEB
+  for (int p = threadIdx.x; p < nrows * NG; p += kDThreads) {
+    const int64_t gi = (row0 + p / NG) * a.NG + p % NG;
+    const float s = a.scales[gi];
+    const float z = ASYM ? static_cast<float>(a.zeros[gi]) : 8.0f;
+    uint32_t wv[16 * kEB / 4];
+#pragma unroll
+    for (int u = 0; u < 16; u += 2) {
+      // signed codes: nibble u holds q with u = q & 15, value (u ^ 8) - 8
+      const float v0 = (static_cast<float>(ASYM ? u : (u ^ 8)) - z) * s;
+      const float v1 = (static_cast<float>(ASYM ? u + 1 : ((u + 1) ^ 8)) - z) * s;
+      if constexpr (OUT_BF16) {
+        wv[u / 2] = f32_to_bf16(v0) | (f32_to_bf16(v1) << 16);
+      } else {
+        wv[u] = __float_as_uint(v0);
+        wv[u + 1] = __float_as_uint(v1);
+      }
+    }
+    u32x4* dst = reinterpret_cast<u32x4*>(tsm + static_cast<size_t>(p) * 16 * kEB);
+#pragma unroll
+    for (int q = 0; q < 16 * kEB / 16; ++q) dst[q] = u32x4{wv[4 * q], wv[4 * q + 1], wv[4 * q + 2], wv[4 * q + 3]};
+  }
+  __syncthreads();
+
+  if (!live) return;
+#pragma unroll
+  for (int r = 0; r < kActRows; ++r) {
+    if (r >= nrows) break;
+    const uint8_t* trow = tsm + static_cast<size_t>(r) * NG * 16 * kEB;
+    const int64_t e0 = (row0 + r) * a.K + k0;
+    uint32_t o[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const uint32_t u = (dw[r] >> (4 * e)) & 15u;
+      o[e] = OUT_BF16 ? *reinterpret_cast<const uint16_t*>(trow + goff[e] + 2 * u)
+                      : *reinterpret_cast<const uint32_t*>(trow + goff[e] + 4 * u);
+    }
+    if constexpr (OUT_BF16) {
+      uint16_t* out = static_cast<uint16_t*>(a.out) + e0;
+      if (cnt == 8 && (e0 & 7) == 0) {
+        *reinterpret_cast<u32x4*>(out) = u32x4{o[0] | (o[1] << 16), o[2] | (o[3] << 16), o[4] | (o[5] << 16), o[6] | (o[7] << 16)};
+      } else {
+        for (int e = 0; e < cnt; ++e) out[e] = static_cast<uint16_t>(o[e]);
+      }
+    } else {
+      uint32_t* out = static_cast<uint32_t*>(a.out) + e0;
+      if (cnt == 8 && (e0 & 3) == 0) {
+        reinterpret_cast<u32x4*>(out)[0] = u32x4{o[0], o[1], o[2], o[3]};
+        reinterpret_cast<u32x4*>(out)[1] = u32x4{o[4], o[5], o[6], o[7]};
+      } else {
+        for (int e = 0; e < cnt; ++e) out[e] = o[e];
+      }
+    }
+  }
+}
+
 template <bool OUT_BF16, bool ASYM, int GIDX>
 hipError_t launch_d3(const DequantArgs& a, hipStream_t s) {
   const int64_t nchunks = (a.K + 7) / 8;
@@ -738,6 +867,16 @@ hipError_t launch_d2(const DequantArgs& a, hipStream_t s) {
       return hipGetLastError();
     }
     return launch_d3<OUT_BF16, ASYM, 0>(a, s);
+  }
+  if (a.K >= 512) {
+    const int rows = act_rows<OUT_BF16>(a.NG);
+    if (rows >= 4 && (a.N + rows - 1) / rows <= 65535) {
+      const dim3 grid(static_cast<uint32_t>((a.K + 8 * kDThreads - 1) / (8 * kDThreads)),
+                      static_cast<uint32_t>((a.N + rows - 1) / rows));
+      const size_t lds = static_cast<size_t>(rows) * a.NG * 16 * act_entry_bytes<OUT_BF16>();
+      dequantize_act_kernel<OUT_BF16, ASYM><<<grid, dim3(kDThreads), lds, s>>>(a, rows);
+      return hipGetLastError();
+    }
   }
   if (a.NG <= kDequantLdsGroups) return launch_d3<OUT_BF16, ASYM, 1>(a, s);
   return launch_d3<OUT_BF16, ASYM, 2>(a, s);
