@@ -522,6 +522,16 @@ __global__ __launch_bounds__(kTileWaves * kWave, 4) void skinny_mfma_kernel(Line
 constexpr int kRowsWaves = 4;
 constexpr int kRowsKB = 4;                      // 128-column blocks per batch
 constexpr int kRowsTG = 16;                     // table groups per row per batch, at most
+constexpr int kRowsTS = kRowsTG + 1;            // table row stride (odd: rows on distinct banks)
+// staged activations: chunk c (16 bytes) of a batch row is stored at chunk
+// x_swz(c) = c with its low two bits rotated by bits 3..4, so the 16 lanes
+// that stage one row (64-byte units) write distinct banks
+__host__ __device__ constexpr uint32_t x_swz(uint32_t c) {
+  return (c & ~3u) | (((c & 3u) + ((c >> 3) & 3u)) & 3u);
+}
+// activation sums: row m, unit u at m * (kRowsKB * 4) + (u ^ xs_swz(m)); the XOR keeps
+// aligned groups of 4 together and puts the 4 lane quarters' rows on distinct banks
+__device__ __forceinline__ int xs_swz(int m) { return 4 * ((m >> 2) & 3); }
 
 struct RowsLayout {
   uint32_t xrow, xbuf, xs_off, xsbuf, wave_off, wave_bytes, bytes;
@@ -534,7 +544,7 @@ __host__ __device__ inline RowsLayout rows_layout() {
   L.xs_off = 2 * L.xbuf;
   L.xsbuf = 16 * kRowsKB * 4 * 4;               // [16 rows][kRowsKB * 4 units] floats
   L.wave_off = L.xs_off + 2 * L.xsbuf;
-  L.wave_bytes = 1024 + 16 * kRowsTG * 4 + 16 * kRowsTG;
+  L.wave_bytes = 2048 + ((16 * kRowsTS * 4 + 16 * kRowsTS + 15) & ~15);
   L.bytes = L.wave_off + kRowsWaves * L.wave_bytes;
   return L;
 }
@@ -602,16 +612,17 @@ __device__ __forceinline__ void rows_stage(const LinearArgs& a, int b, int lane,
     pair_x(in, xp);
 #pragma unroll
     for (int p = 0; p < 4; ++p) sum = dot2_bf16(xp[p], ones, sum);
-    *reinterpret_cast<u32x4*>(xb + 16 * i) = live ? u32x4{xp[0], xp[1], xp[2], xp[3]} : u32x4{0u, 0u, 0u, 0u};
+    *reinterpret_cast<u32x4*>(xb - 64 * uu + 16 * x_swz(4 * uu + i)) =
+        live ? u32x4{xp[0], xp[1], xp[2], xp[3]} : u32x4{0u, 0u, 0u, 0u};
   }
-  reinterpret_cast<float*>(smem + L.xs_off + (b & 1) * L.xsbuf)[m * (kRowsKB * 4) + uu] = live ? sum : 0.0f;
+  reinterpret_cast<float*>(smem + L.xs_off + (b & 1) * L.xsbuf)[m * (kRowsKB * 4) + (uu ^ xs_swz(m))] = live ? sum : 0.0f;
   const int rq = lane >> 2, cq = lane & 3;
-  float* stab = reinterpret_cast<float*>(wave_lds + 1024);
-  uint8_t* ztab = wave_lds + 1024 + 16 * kRowsTG * 4;
+  float* stab = reinterpret_cast<float*>(wave_lds + 2048);
+  uint8_t* ztab = wave_lds + 2048 + 16 * kRowsTS * 4;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    stab[rq * kRowsTG + 4 * i + cq] = R.ts[i];
-    ztab[rq * kRowsTG + 4 * i + cq] = static_cast<uint8_t>(R.tz[i]);
+    stab[rq * kRowsTS + 4 * i + cq] = R.ts[i];
+    ztab[rq * kRowsTS + 4 * i + cq] = static_cast<uint8_t>(R.tz[i]);
   }
 }
 
@@ -623,8 +634,8 @@ __device__ __forceinline__ void rows_compute(const LinearArgs& a, int b, int nkb
   const int n = lane & 15, q = lane >> 4;
   const int rq = lane >> 2, cq = lane & 3;
   u32x4* scratch = reinterpret_cast<u32x4*>(wave_lds);
-  const float* stab = reinterpret_cast<const float*>(wave_lds + 1024);
-  const uint8_t* ztab = wave_lds + 1024 + 16 * kRowsTG * 4;
+  const float* stab = reinterpret_cast<const float*>(wave_lds + 2048);
+  const uint8_t* ztab = wave_lds + 2048 + 16 * kRowsTS * 4;
   const uint8_t* xa = smem + (b & 1) * L.xbuf + n * L.xrow;          // A row n (zero rows for m >= M)
   const float* xs = reinterpret_cast<const float*>(smem + L.xs_off + (b & 1) * L.xsbuf);
   const int kbf = b * kRowsKB;
@@ -633,9 +644,13 @@ __device__ __forceinline__ void rows_compute(const LinearArgs& a, int b, int nkb
 #pragma unroll
   for (int j = 0; j < kRowsKB; ++j) {
     if (kbf + j < nkb) {
-      scratch[rq * 4 + cq] = R.cw[j];
-      __builtin_amdgcn_s_waitcnt(0xc07f);            // lgkmcnt(0): the wave's own LDS writes
-      const u32x4 v = scratch[n * 4 + q];
+      // the wave's LDS operations complete in order, so the read sees the
+      // write; alternating halves let consecutive blocks overlap
+      // (chunk c of row r sits at slot 4 r + (c ^ ((r >> 1) & 3)), so that
+      // both the write and the transposed read hit distinct banks)
+      u32x4* sc2 = scratch + 64 * (j & 1);
+      sc2[rq * 4 + (cq ^ ((rq >> 1) & 3))] = R.cw[j];
+      const u32x4 v = sc2[n * 4 + (q ^ ((n >> 1) & 3))];
       uint32_t d[4] = {v[0], v[1], v[2], v[3]};
       if constexpr (!ASYM) {
 #pragma unroll
@@ -646,7 +661,7 @@ __device__ __forceinline__ void rows_compute(const LinearArgs& a, int b, int nkb
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const uint32_t chunk = TR ? (16u * j + 4u * i + q) : (16u * j + 4u * q + i);
-        const bf16x8_t av = *reinterpret_cast<const bf16x8_t*>(xa + 16u * chunk);
+        const bf16x8_t av = *reinterpret_cast<const bf16x8_t*>(xa + 16u * x_swz(chunk));
         const int gi = i / (4 / GU);
         acc[gi] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, decode_word(d[i], mask),
                                                           (i % (4 / GU)) == 0 ? zero4 : acc[gi], 0, 0, 0);
@@ -655,20 +670,19 @@ __device__ __forceinline__ void rows_compute(const LinearArgs& a, int b, int nkb
       for (int gi = 0; gi < GU; ++gi) {
         const int col = 128 * (kbf + j) + (128 / GU) * gi;
         const int gg = col / static_cast<int>(G) - g_first;
-        const float sc = stab[n * kRowsTG + gg];
-        const float zo = 128.0f + static_cast<float>(ztab[n * kRowsTG + gg]);
+        const float sc = stab[n * kRowsTS + gg];
+        const float zo = 128.0f + static_cast<float>(ztab[n * kRowsTS + gg]);
         const int u0 = 4 * j + gi * (4 / GU);
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
           const int m = 4 * q + t;                    // output row of acc[gi][t]
           float sx = 0.0f;
 #pragma unroll
-          for (int uu = 0; uu < 4 / GU; ++uu) sx += xs[m * (kRowsKB * 4) + u0 + uu];
+          for (int uu = 0; uu < 4 / GU; ++uu) sx += xs[m * (kRowsKB * 4) + ((u0 + uu) ^ xs_swz(m))];
           out[t] += sc * (acc[gi][t] - zo * sx);
         }
       }
     }
-    __builtin_amdgcn_sched_barrier(0);
   }
 }
 
