@@ -379,7 +379,8 @@ struct ChunkLoader {
   u32x4 seg[kNS];
   __device__ __forceinline__ void issue(const uint8_t* __restrict__ rowA, int j) {
 #pragma unroll
-    for (int s = 0; s < kNS; ++s) seg[s] = *reinterpret_cast<const u32x4*>(rowA + kCB * j + 16 * s);
+    for (int s = 0; s < kNS; ++s)   // weights are read once: non-temporal
+      seg[s] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(rowA + kCB * j + 16 * s));
   }
   __device__ __forceinline__ void unpack(float v[8]) const {
     uint32_t d[4 * kNS];
@@ -619,7 +620,7 @@ __device__ __forceinline__ void dequantize_row(const DequantArgs& a, int64_t n, 
     // the chunk's code word (bytes 4 ic .. 4 ic + 3 of the row)
     uint32_t d;
     if (!last) {
-      const uint32_t d0 = *reinterpret_cast<const uint32_t*>(cbase + 4 * ic);
+      const uint32_t d0 = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(cbase + 4 * ic));
       d = d0;
       if (cadj) d = __builtin_amdgcn_alignbyte(*reinterpret_cast<const uint32_t*>(cbase + 4 * ic + 4), d0, cadj);
     } else {                                         // stay inside the buffer
@@ -684,7 +685,8 @@ __device__ __forceinline__ void dequantize_row(const DequantArgs& a, int64_t n, 
     const int c0 = 8 * j - SFT;                      // column of its element 0
     if (c0 >= 0 && c0 + 8 <= K) {
       if constexpr (OUT_BF16) {
-        *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(a.out) + 8 * (f0 + j)) = u32x4{out[0], out[1], out[2], out[3]};
+        __builtin_nontemporal_store(u32x4{out[0], out[1], out[2], out[3]},   // streamed out once
+                                    reinterpret_cast<u32x4*>(static_cast<uint16_t*>(a.out) + 8 * (f0 + j)));
       } else {
         u32x4* dst = reinterpret_cast<u32x4*>(static_cast<float*>(a.out) + 8 * (f0 + j));
         dst[0] = u32x4{out[0], out[1], out[2], out[3]};

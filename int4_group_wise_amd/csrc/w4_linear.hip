@@ -95,7 +95,9 @@ __device__ __forceinline__ void load_slice(const LinearArgs& a, int64_t row0, in
   for (int r = 0; r < kGemvRows; ++r) {
     const int64_t n = min(row0 + r, a.N - 1);   // clamped rows are computed, not stored
     const uint8_t* crow = a.codes + n * KB;
-    s.cw[r] = *reinterpret_cast<const uint4*>(crow + coff);
+    // code words are read once: non-temporal, so they do not displace x
+    const u32x4 t = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(crow + coff));
+    s.cw[r] = make_uint4(t[0], t[1], t[2], t[3]);
     s.sc[r] = (a.scales + n * a.NG)[g];
     s.zb[r] = ASYM ? (a.zeros + n * a.NG)[g] : 8u;
   }
