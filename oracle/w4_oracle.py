@@ -52,7 +52,7 @@ ASYM = "asym"   # unsigned nibbles with a per-group zero-point
 __all__ = [
     "SYM", "ASYM", "n_groups", "group_of_columns", "bf16_bits_to_f32",
     "f32_to_bf16_bits", "quantize", "pack_nibbles", "unpack_nibbles",
-    "decode", "dequantize", "quantize_pack", "linear", "validate_packed",
+    "decode", "dequantize", "quantize_pack", "linear", "linear_grad_input", "validate_packed",
     "payload_bytes",
 ]
 
@@ -249,6 +249,28 @@ def linear(x_bits, codes, scales, zeros, g_idx, K: int, G: int, mode: str,
     if bias_bits is not None:
         y += bf16_bits_to_f32(bias_bits).astype(np.float64)[None, :]
     return y
+
+
+def linear_grad_input(dy_bits, codes, scales, zeros, g_idx, K: int, G: int, mode: str,
+                      row_chunk: int = 4096) -> np.ndarray:
+    """Input gradient of the linear: ``dx[m, k] = sum_n dy[m, n] * Wd[n, k]``
+    in fp64, with the same bf16-rounded dequantized weight Wd as the forward
+    (R7).  ([Keras] the custom gradient of the sub-channel int4 matmul: the
+    upstream gradient times the dequantized kernel cast to the compute dtype;
+    [Paddle] ``QuantizationLinearFunc`` backward: the output gradient times
+    the dequantized weight.)  ``dy_bits`` uint16 [M, N] bf16 bit patterns.
+    Returns fp64 [M, K]."""
+    dy = bf16_bits_to_f32(dy_bits).astype(np.float64)
+    codes = np.asarray(codes)
+    N = codes.shape[0]
+    dx = np.zeros((dy.shape[0], K), dtype=np.float64)
+    for n0 in range(0, N, row_chunk):
+        n1 = min(N, n0 + row_chunk)
+        z = None if zeros is None else np.asarray(zeros)[n0:n1]
+        wd = bf16_bits_to_f32(dequantize(codes[n0:n1], np.asarray(scales)[n0:n1],
+                                         z, g_idx, K, G, mode, "bf16"))
+        dx += dy[:, n0:n1] @ wd.astype(np.float64)
+    return dx
 
 
 # ---------------------------------------------------------------------------

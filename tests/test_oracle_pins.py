@@ -271,6 +271,72 @@ def _brute_linear(xf, wd, b):
     return np.array(y)
 
 
+def _hand_dequant(codes, s, z, g_idx, N, K, G, mode):
+    """bf16-rounded dequantized weight decoded by hand, element by element."""
+    gid = np.arange(K) // G if g_idx is None else g_idx
+    wd = np.zeros((N, K))
+    for n in range(N):
+        for k in range(K):
+            byte = int(codes[n, k // 2])
+            nib = (byte >> 4) if (k & 1) else (byte & 15)
+            val = (nib - 16 if nib >= 8 else nib) if mode == O.SYM else nib - int(z[n, gid[k]])
+            prod = np.float32(np.float32(val) * s[n, gid[k]])
+            wd[n, k] = torch.tensor(float(prod), dtype=torch.float32).to(torch.bfloat16).item()
+    return wd
+
+
+@pytest.mark.parametrize("mode,g_act", [(O.SYM, False), (O.ASYM, True)])
+def test_linear_grad_input_brute_force(mode, g_act):
+    """dx[m, k] = sum_n dy[m, n] Wd[n, k], summed by explicit loops."""
+    rng = np.random.default_rng(19)
+    M, N, K, G = 3, 6, 29, 8
+    w = (rng.standard_normal((N, K)) * 0.02).astype(F32)
+    g_idx = (rng.permutation(K) % O.n_groups(K, G)).astype(np.int32) if g_act else None
+    codes, s, z = O.quantize_pack(w, G, mode, g_idx)
+    dyb = O.f32_to_bf16_bits(rng.standard_normal((M, N)).astype(F32))
+    dx = O.linear_grad_input(dyb, codes, s, z, g_idx, K, G, mode, row_chunk=4)
+    wd = _hand_dequant(codes, s, z, g_idx, N, K, G, mode)
+    dyf = torch.from_numpy(dyb.view(np.int16).copy()).view(torch.bfloat16).double().numpy()
+    ref = np.zeros((M, K))
+    for m in range(M):
+        for k in range(K):
+            acc = 0.0
+            for n in range(N):
+                acc += dyf[m, n] * wd[n, k]
+            ref[m, k] = acc
+    np.testing.assert_allclose(dx, ref, rtol=1e-12, atol=1e-15)
+
+
+@pytest.mark.parametrize("mode", [O.SYM, O.ASYM])
+def test_linear_grad_input_is_the_adjoint(mode):
+    """<x Wd^T, dy> = <x, dy Wd> for any x, dy: the gradient is the transpose
+    of the forward map (a dropped or transposed index breaks the identity)."""
+    rng = np.random.default_rng(20)
+    M, N, K, G = 4, 33, 64, 16
+    w = (rng.standard_normal((N, K)) * 0.02).astype(F32)
+    g_idx = (rng.permutation(K) // G).astype(np.int32)
+    codes, s, z = O.quantize_pack(w, G, mode, g_idx)
+    xb = O.f32_to_bf16_bits(rng.standard_normal((M, K)).astype(F32))
+    dyb = O.f32_to_bf16_bits(rng.standard_normal((M, N)).astype(F32))
+    y = O.linear(xb, codes, s, z, g_idx, K, G, mode, None)
+    dx = O.linear_grad_input(dyb, codes, s, z, g_idx, K, G, mode)
+    lhs = float(np.sum(y * O.bf16_bits_to_f32(dyb).astype(np.float64)))
+    rhs = float(np.sum(O.bf16_bits_to_f32(xb).astype(np.float64) * dx))
+    assert abs(lhs - rhs) <= 1e-12 * max(1.0, abs(lhs))
+
+
+def test_linear_grad_input_unit_rows_return_weight_rows():
+    """dy = unit rows e_n gives the bf16 dequantized rows of W exactly."""
+    rng = np.random.default_rng(21)
+    N, K, G = 7, 48, 16
+    w = (rng.standard_normal((N, K)) * 0.02).astype(F32)
+    codes, s, z = O.quantize_pack(w, G, O.ASYM)
+    dyb = O.f32_to_bf16_bits(np.eye(N, dtype=F32))
+    dx = O.linear_grad_input(dyb, codes, s, z, None, K, G, O.ASYM)
+    wd = O.bf16_bits_to_f32(O.dequantize(codes, s, z, None, K, G, O.ASYM, "bf16"))
+    assert np.array_equal(dx, wd.astype(np.float64))
+
+
 @pytest.mark.parametrize("mode,g_act", [(O.SYM, False), (O.ASYM, True)])
 def test_linear_brute_force(mode, g_act):
     rng = np.random.default_rng(9)
