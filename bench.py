@@ -10,7 +10,8 @@ model with many layers.  The JSON line reports whole-job HBM GB/s of the
 algorithmic bytes, the decode kernel's roofline (its average launch duration
 measured with HIP events on the launch stream), and the CPU oracle on a
 bounded sample.  Secondary entries cover the prefill GEMM (TFLOP/s), the
-batched decode and the codec round trip.
+batched decode, the input gradient (decode and prefill shapes) and the codec
+round trip.
 """
 from __future__ import annotations
 
@@ -221,6 +222,52 @@ def bench_secondary(w4):
                              "config": {"workload": "batched_decode", "M": wl.M, "N": wl.N, "K": wl.K,
                                         "G": wl.G, "mode": wl.mode}}
     del rot, x, y
+
+    # input gradient dx = dy . Wd at the decode layer's shape (M = 1) and the
+    # prefill shape (M = 2048, act-order)
+    wl = workload("decode")
+    t = generate(wl)
+    c, s, z = w4.quantize_pack(t["w"].to(dev), wl.G, wl.mode)
+    del t
+    dy = torch.randn(1, wl.N, generator=torch.Generator().manual_seed(1)).to(torch.bfloat16).to(dev)
+    rot = Rotation([c, s, z], 2 * MALL_BYTES)
+    del c, s, z
+    dx = torch.empty(1, wl.K, dtype=torch.bfloat16, device=dev)
+    gws = torch.empty(w4.linear_grad_input_workspace_bytes(1, wl.N, wl.K, wl.G, wl.mode), dtype=torch.uint8, device=dev)
+    steps = 2000
+
+    def call_g(i):
+        cc, ss, zz = rot.sets[i]
+        w4.linear_grad_input(dy, cc, ss, zz, None, wl.K, wl.G, wl.mode, out=dx, workspace=gws)
+
+    ev_ms, _ = time_graph(call_g, rot.count * 4, steps, rot.count * 4, rot.count)
+    nb = algorithmic_bytes_linear(1, wl.N, wl.K, wl.G, True, False)   # same operands, dy/dx for x/y
+    gbs = nb * steps / (ev_ms * 1e-3) / 1e9
+    out["grad_input_decode"] = {"metric": "W4A16 input gradient HBM GB/s M=1", "value": round(gbs, 1), "unit": "GB/s",
+                                "us_per_call": round(ev_ms * 1e3 / steps, 2),
+                                "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
+                                             "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4)},
+                                "config": {"workload": "decode", "M": 1, "N": wl.N, "K": wl.K, "G": wl.G, "mode": wl.mode}}
+    del rot, dx, gws, dy
+    wl = workload("prefill")
+    t = generate(wl)
+    gi = t["g_idx"].to(dev)
+    c, s, z = w4.quantize_pack(t["w"].to(dev), wl.G, wl.mode, gi)
+    dy = torch.randn(wl.M, wl.N, generator=torch.Generator().manual_seed(2)).to(torch.bfloat16).to(dev)
+    del t
+    dx = torch.empty(wl.M, wl.K, dtype=torch.bfloat16, device=dev)
+    gws = torch.empty(w4.linear_grad_input_workspace_bytes(wl.M, wl.N, wl.K, wl.G, wl.mode, True), dtype=torch.uint8, device=dev)
+    steps = 200
+    ev_ms, _ = time_graph(lambda i: w4.linear_grad_input(dy, c, s, z, gi, wl.K, wl.G, wl.mode, out=dx, workspace=gws),
+                          20, steps, 20, 1)
+    tfs = 2.0 * wl.M * wl.N * wl.K * steps / (ev_ms * 1e-3) / 1e12
+    out["grad_input_prefill"] = {"metric": "W4A16 input gradient TFLOP/s M=2048", "value": round(tfs, 2), "unit": "TFLOP/s",
+                                 "us_per_call": round(ev_ms * 1e3 / steps, 2),
+                                 "roofline": {"bound": "mfma", "achieved": round(tfs, 2), "peak": BF16_MFMA_PEAK_TFS,
+                                              "unit": "TFLOP/s", "frac": round(tfs / BF16_MFMA_PEAK_TFS, 4)},
+                                 "config": {"workload": "prefill", "M": wl.M, "N": wl.N, "K": wl.K, "G": wl.G,
+                                            "mode": wl.mode, "act_order": True}}
+    del c, s, z, gi, dy, dx, gws
 
     # codec: bf16 W [28672, 8191] -> quantize_pack -> dequantize (bf16)
     wl = workload("codec")

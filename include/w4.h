@@ -142,6 +142,37 @@ w4_status w4_linear(const void* x, int64_t M,
                     const void* bias, void* y,
                     void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * w4_linear_grad_input_workspace_bytes — device scratch w4_linear_grad_input
+ * needs for this shape: fp32 partial sums of row slices for M <= 16, the
+ * transposed bf16 dequantized weight [K, N] for M > 16.
+ */
+size_t w4_linear_grad_input_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t G,
+                                            int mode, int has_g_idx);
+
+/*
+ * w4_linear_grad_input — input gradient of w4_linear:
+ *   dx[m, k] = sum_n dy[m, n] * Wd[n, k].
+ *   (keras dense.py diff page: the custom gradient of the sub-channel int4
+ *    matmul, the upstream gradient times the dequantized kernel cast to the
+ *    compute dtype; PaddleNLP quantization_linear.py page:
+ *    QuantizationLinearFunc.backward, the output gradient times the
+ *    dequantized weight.)
+ *   dy       bf16 [M, N] upstream gradient.
+ *   M        >= 0 (M = 0 returns W4_OK and launches nothing).
+ *   codes, scales, zeros, g_idx, N, K, G, mode  as in w4_linear.
+ *   dx       out bf16 [M, K]; products accumulate in fp32 in a fixed order
+ *            (the same inputs give the same bits), one rounding to bf16.
+ *   workspace, workspace_bytes  device scratch of at least
+ *            w4_linear_grad_input_workspace_bytes(...) bytes (never NULL).
+ */
+w4_status w4_linear_grad_input(const void* dy, int64_t M,
+                               const uint8_t* codes, const float* scales,
+                               const uint8_t* zeros, const int32_t* g_idx,
+                               int64_t N, int64_t K, int64_t G, int mode,
+                               void* dx, void* workspace, size_t workspace_bytes,
+                               void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -6,7 +6,8 @@ Its names are re-exported here on first access, so importing the package (or
 its ``workloads`` module) does not load the library.
 """
 _EXPORTS = ("SYM", "ASYM", "W4Error", "library_path", "load", "quantize_pack",
-            "dequantize", "linear", "linear_workspace_bytes")
+            "dequantize", "linear", "linear_workspace_bytes", "linear_grad_input",
+            "linear_grad_input_workspace_bytes")
 
 
 def __getattr__(name):

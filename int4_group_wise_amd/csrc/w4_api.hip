@@ -136,4 +136,44 @@ w4_status w4_linear(const void* x, int64_t M, const uint8_t* codes, const float*
   return hip_status(w4::launch_gemm_bf16(a.x, static_cast<const uint16_t*>(workspace), a.bias, a.y, M, N, K, s), fn);
 }
 
+size_t w4_linear_grad_input_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t G, int mode,
+                                            int has_g_idx) {
+  (void)mode;
+  if (M < 1 || N < 1 || K < 1 || G < 1) return 0;
+  return w4::grad_plan(M, N, K, G, has_g_idx != 0).workspace;
+}
+
+w4_status w4_linear_grad_input(const void* dy, int64_t M, const uint8_t* codes, const float* scales,
+                               const uint8_t* zeros, const int32_t* g_idx, int64_t N, int64_t K,
+                               int64_t G, int mode, void* dx, void* workspace, size_t workspace_bytes,
+                               void* stream) {
+  g_last_error.clear();
+  const char* fn = "w4_linear_grad_input";
+  if (w4_status st = check_format(N, K, G, mode, zeros, g_idx, fn)) return st;
+  if (M < 0) return fail(W4_ERR_INVALID_ARG, "%s: M must be >= 0", fn);
+  if (M > kMaxDim) return fail(W4_ERR_UNSUPPORTED, "%s: M must be <= 2^30", fn);
+  if (M == 0) return W4_OK;
+  if (!dy || !codes || !scales || !dx) return fail(W4_ERR_INVALID_ARG, "%s: dy, codes, scales and dx must be non-NULL", fn);
+  if (!aligned16(dy) || !aligned16(codes) || !aligned16(scales) || !aligned16(dx))
+    return fail(W4_ERR_INVALID_ARG, "%s: dy, codes, scales and dx must be 16-byte aligned", fn);
+  const size_t need = w4_linear_grad_input_workspace_bytes(M, N, K, G, mode, g_idx != nullptr);
+  if (workspace_bytes < need || !workspace)
+    return fail(W4_ERR_INVALID_ARG, "%s: workspace of %zu bytes needed (got %zu)", fn, need, workspace_bytes);
+  if (!aligned16(workspace)) return fail(W4_ERR_INVALID_ARG, "%s: workspace must be 16-byte aligned", fn);
+  const w4::GradPlan plan = w4::grad_plan(M, N, K, G, g_idx != nullptr);
+  if (M <= w4::kGradSkinnyMax) {
+    const int64_t cb = ((K + 7) / 8 + 255) / 256;
+    if (cb > kMaxGrid || plan.slices > 65535 || (M * K + 255) / 256 > kMaxGrid)
+      return fail(W4_ERR_UNSUPPORTED, "%s: matrix too large for one launch", fn);
+  } else {
+    const int64_t gemm_blocks = N % 8 == 0 ? ((M + 127) / 128) * ((K + 127) / 128) : (M * K + 255) / 256;
+    if ((K + 63) / 64 > kMaxGrid || (N + 63) / 64 > 65535 || gemm_blocks > kMaxGrid)
+      return fail(W4_ERR_UNSUPPORTED, "%s: matrix too large for one launch", fn);
+  }
+  const int64_t NG = (K + G - 1) / G;
+  w4::GradArgs a{static_cast<const uint16_t*>(dy), M, codes, scales, zeros, g_idx, N, K, G, NG,
+                 mode == W4_ASYM, static_cast<uint16_t*>(dx), static_cast<float*>(workspace)};
+  return hip_status(w4::launch_grad_input(a, static_cast<hipStream_t>(stream)), fn);
+}
+
 }  // extern "C"

@@ -1,0 +1,362 @@
+// Input gradient of the W4A16 linear: dx[m, k] = sum_n dy[m, n] * Wd[n, k]
+// (keras dense.py diff page: the custom gradient of the sub-channel int4
+// matmul; PaddleNLP quantization_linear.py page: QuantizationLinearFunc
+// backward).
+//
+// M <= 16: the reduction runs over the rows of W, so the N rows are split
+// into P slices.  A workgroup of 4 waves takes 64 * CPT columns of dx and one
+// slice; a lane owns CPT consecutive columns (32, one 16-byte code load per
+// row, when groups are contiguous and a multiple of 32 wide and M <= 4; else
+// 8, one dword), streams the code words of its wave's rows (coalesced across
+// the wave) and accumulates dy[m, n] * w[n, k] in fp32, the dy values being
+// uniform loads.  Each slice writes its fp32 partial [M, K] to the workspace
+// and a second kernel adds the P partials in a fixed order (the result does
+// not depend on scheduling).  The group size is a multiple of 8, so an
+// 8-column piece lies in one group.
+//
+// M > 16: the weight is dequantized transposed, Wd^T [K, N] bf16, into the
+// workspace, and the bf16 GEMM computes dx = dy . (Wd^T)^T.
+
+#include "w4_device.h"
+#include "w4_internal.h"
+
+#include <algorithm>
+
+namespace w4 {
+namespace {
+
+constexpr int kGThreads = 256;
+constexpr int kGWaves = kGThreads / kWave;
+constexpr int kGUnroll = 8;               // rows of a wave whose loads are issued together
+
+// Columns per lane: 32 (one 16-byte code load per row) for contiguous groups
+// of a multiple of 32 columns and at most 4 dy rows, else 8 (one dword).
+template <int MT, bool WIDE>
+constexpr int grad_cpt() { return WIDE && MT <= 4 ? 32 : 8; }
+
+// One workgroup: 64 * CPT columns of dx (lane l owns columns CPT l ..), one
+// slice of rows of W; wave w takes rows w, w + 4, ... of the slice.  The 4
+// waves' sums are added through LDS and wave 0 writes the slice's partial.
+template <bool ASYM, bool GIDX, int MT, int CPT>
+__global__ __launch_bounds__(kGThreads) void grad_split_kernel(GradArgs a, int rows_per) {
+  extern __shared__ __attribute__((aligned(16))) float gsm[];
+  constexpr int kW = CPT / 8;                         // code dwords per row
+  const int lane = lane_id();
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int K = static_cast<int>(a.K);
+  const int k0 = blockIdx.x * (kWave * CPT) + CPT * lane;
+  const int M = static_cast<int>(a.M);
+  const int64_t nb = static_cast<int64_t>(blockIdx.y) * rows_per;
+  const int64_t ne = min(a.N, nb + rows_per);
+  const bool live = k0 < K;
+  const int cnt = live ? min(CPT, K - k0) : 0;
+  const int64_t KB = (a.K + 1) / 2;
+  const int NG = static_cast<int>(a.NG);
+  const int kc = min(k0, K - 1);
+
+  // group of the lane's columns (contiguous: one, the chunk lies in one
+  // group) or of each of its 8 columns (act-order)
+  constexpr int kNGrp = GIDX ? 8 : 1;
+  int g[kNGrp];
+#pragma unroll
+  for (int e = 0; e < kNGrp; ++e)
+    g[e] = GIDX ? min(max(a.g_idx[min(kc + e, K - 1)], 0), NG - 1) : kc / static_cast<int>(a.G);
+  const bool aligned = cnt == CPT && (KB & 3) == 0;
+
+  float acc[MT][CPT];
+#pragma unroll
+  for (int m = 0; m < MT; ++m)
+#pragma unroll
+    for (int e = 0; e < CPT; ++e) acc[m][e] = 0.0f;
+
+  for (int64_t n0 = nb + w; n0 < ne; n0 += kGUnroll * kGWaves) {
+    uint32_t d[kGUnroll][kW];
+    float s[kGUnroll][kNGrp];
+    float z[kGUnroll][kNGrp];
+    // loads of this wave's next kGUnroll rows first (past the slice: reload the last)
+#pragma unroll
+    for (int u = 0; u < kGUnroll; ++u) {
+      const int64_t n = min(n0 + u * kGWaves, ne - 1);
+      const uint8_t* crow = a.codes + n * KB + CPT / 2 * (k0 / CPT);
+      if (aligned) {
+        if constexpr (kW == 4) {
+          const u32x4 q = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(crow));
+#pragma unroll
+          for (int i = 0; i < 4; ++i) d[u][i] = q[i];
+        } else {
+          d[u][0] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(crow));
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < kW; ++i) d[u][i] = 0;
+        for (int b = 0; b < (cnt + 1) / 2; ++b) d[u][b >> 2] |= static_cast<uint32_t>(crow[b]) << (8 * (b & 3));
+      }
+#pragma unroll
+      for (int e = 0; e < kNGrp; ++e) {
+        s[u][e] = a.scales[n * NG + g[e]];
+        z[u][e] = ASYM ? static_cast<float>(a.zeros[n * NG + g[e]]) : 8.0f;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kGUnroll; ++u) {
+      const int64_t n = n0 + u * kGWaves;
+      if (n >= ne) break;
+      float dm[MT];
+#pragma unroll
+      for (int m = 0; m < MT; ++m) {   // rows m >= M read row M - 1 and add nothing
+        const float dv = bf16_to_f32(a.dy[static_cast<int64_t>(min(m, M - 1)) * a.N + n]);
+        dm[m] = m < M ? dv : 0.0f;
+      }
+#pragma unroll
+      for (int i = 0; i < kW; ++i) {
+        const uint32_t dd = ASYM ? d[u][i] : (d[u][i] ^ 0x88888888u);   // signed q -> q + 8
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int ge = GIDX ? e : 0;
+          const float wv = (static_cast<float>((dd >> (4 * e)) & 15u) - z[u][ge]) * s[u][ge];
+#pragma unroll
+          for (int m = 0; m < MT; ++m) acc[m][8 * i + e] = __builtin_fmaf(dm[m], wv, acc[m][8 * i + e]);
+        }
+      }
+    }
+  }
+
+  // add the 4 waves' sums (waves 1..3 in turn through one buffer: register
+  // order [m][e], lane-major so the accesses are unit-stride)
+  for (int src = 1; src < kGWaves; ++src) {
+    if (w == src) {
+#pragma unroll
+      for (int m = 0; m < MT; ++m)
+#pragma unroll
+        for (int e = 0; e < CPT; ++e) gsm[(m * CPT + e) * kWave + lane] = acc[m][e];
+    }
+    __syncthreads();
+    if (w == 0) {
+#pragma unroll
+      for (int m = 0; m < MT; ++m)
+#pragma unroll
+        for (int e = 0; e < CPT; ++e) acc[m][e] += gsm[(m * CPT + e) * kWave + lane];
+    }
+    __syncthreads();
+  }
+  if (w != 0 || !live) return;
+  float* part = a.partial + static_cast<int64_t>(blockIdx.y) * M * a.K;
+#pragma unroll
+  for (int m = 0; m < MT; ++m) {
+    if (m >= M) continue;
+    float* dst = part + static_cast<int64_t>(m) * a.K + k0;
+    if (cnt == CPT && (a.K & 3) == 0) {
+#pragma unroll
+      for (int q = 0; q < CPT / 4; ++q)
+        reinterpret_cast<f32x4_t*>(dst)[q] = f32x4_t{acc[m][4 * q], acc[m][4 * q + 1], acc[m][4 * q + 2], acc[m][4 * q + 3]};
+    } else {
+#pragma unroll
+      for (int e = 0; e < CPT; ++e)
+        if (e < cnt) dst[e] = acc[m][e];
+    }
+  }
+}
+
+// dx[i] = bf16(sum over slices p = 0 .. P-1 of partial[p][i]), i over M * K.
+// A workgroup takes 64 outputs; its 16 waves sum 16 fixed ranges of slices
+// (8 loads in flight per lane), then wave 0 adds the 16 range sums in order,
+// so the result does not depend on scheduling.
+constexpr int kRParts = 16;
+__global__ __launch_bounds__(kRParts * kWave) void grad_reduce_kernel(const float* __restrict__ partial,
+                                                                      int P, int64_t total, uint16_t* __restrict__ dx) {
+  __shared__ float red[kRParts][kWave];
+  const int lane = lane_id();
+  const int part = threadIdx.x >> 6;
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * kWave + lane;
+  const int64_t ic = min(i, total - 1);
+  const int per = (P + kRParts - 1) / kRParts;
+  const int p0 = part * per, p1 = min(P, p0 + per);
+  float sum = 0.0f;
+  for (int p = p0; p < p1; p += 8) {
+    float v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = partial[static_cast<int64_t>(min(p + u, p1 - 1)) * total + ic];
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      if (p + u < p1) sum += v[u];
+  }
+  red[part][lane] = sum;
+  __syncthreads();
+  if (part != 0 || i >= total) return;
+  float t = 0.0f;
+#pragma unroll
+  for (int q = 0; q < kRParts; ++q) t += red[q][lane];
+  dx[i] = static_cast<uint16_t>(f32_to_bf16(t));
+}
+
+// Transposed dequantize: wt[k][n] = bf16(value(n, k) * s[n, gid(k)]), a
+// 64 x 64 tile per workgroup.  The tile's scale / zero-point rows and group
+// indices are staged in LDS; a thread reads 8 code bytes (16 columns) of one
+// row, and the bf16 values go through an LDS tile (rows padded by 2 bytes)
+// to be written out as rows of wt.
+constexpr int kTT = 64;
+template <bool ASYM, bool GIDX, bool TAB>
+__global__ __launch_bounds__(kGThreads) void dequantize_t_kernel(DequantArgs a, uint16_t* __restrict__ wt) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t tsm[];
+  uint16_t (*tile)[kTT + 2] = reinterpret_cast<uint16_t (*)[kTT + 2]>(tsm);     // [k][n]
+  int* gsh = reinterpret_cast<int*>(tsm + kTT * (kTT + 2) * 2);                 // [64] group of column
+  const int NG = static_cast<int>(a.NG);
+  float* stab = reinterpret_cast<float*>(gsh + kTT);                            // [64 rows][NG]
+  uint8_t* ztab = reinterpret_cast<uint8_t*>(stab + kTT * NG);                  // [64 rows][NG]
+  const int64_t n0 = static_cast<int64_t>(blockIdx.y) * kTT;
+  const int k0 = blockIdx.x * kTT;
+  const int K = static_cast<int>(a.K);
+  const int64_t KB = (a.K + 1) / 2;
+  const int rows = static_cast<int>(min(static_cast<int64_t>(kTT), a.N - n0));
+  for (int e = threadIdx.x; e < kTT; e += kGThreads) {
+    const int k = min(k0 + e, K - 1);
+    gsh[e] = GIDX ? min(max(a.g_idx[k], 0), NG - 1) : k / static_cast<int>(a.G);
+  }
+  if constexpr (TAB) {                             // (else the rows' tables are read from memory)
+    for (int e = threadIdx.x; e < rows * NG; e += kGThreads) {
+      const int64_t gi = (n0 + e / NG) * a.NG + e % NG;
+      stab[e] = a.scales[gi];
+      if constexpr (ASYM) ztab[e] = a.zeros[gi];
+    }
+  }
+  __syncthreads();
+  {
+    const int nl = threadIdx.x >> 2, kq = (threadIdx.x & 3) * 16;
+    if (nl < rows) {
+      const int64_t n = n0 + nl;
+      const int kb = k0 + kq;                          // first of this thread's 16 columns
+      uint32_t d[2] = {0u, 0u};
+      if (kb + 16 <= K && (KB & 3) == 0) {
+        const uint32_t* src = reinterpret_cast<const uint32_t*>(a.codes + n * KB + kb / 2);
+        d[0] = src[0];
+        d[1] = src[1];
+      } else {
+        for (int b = 0; b < 8; ++b)
+          if (kb + 2 * b < K) d[b >> 2] |= static_cast<uint32_t>(a.codes[n * KB + kb / 2 + b]) << (8 * (b & 3));
+      }
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const uint32_t nib = (d[e >> 3] >> (4 * (e & 7))) & 15u;
+        const int gi = gsh[kq + e];
+        const float sc = TAB ? stab[nl * NG + gi] : a.scales[n * a.NG + gi];
+        const int zp = ASYM ? (TAB ? ztab[nl * NG + gi] : a.zeros[n * a.NG + gi]) : 8;
+        const float val = ASYM ? static_cast<float>(static_cast<int>(nib) - zp)
+                               : static_cast<float>(static_cast<int>(nib ^ 8u) - 8);
+        tile[kq + e][nl] = static_cast<uint16_t>(f32_to_bf16(val * sc));
+      }
+    }
+  }
+  __syncthreads();
+  {
+    const int kl = threadIdx.x >> 2, nq = (threadIdx.x & 3) * 16;
+    const int k = k0 + kl;
+    if (k < K) {
+      uint16_t* dst = wt + static_cast<int64_t>(k) * a.N + n0 + nq;
+      const bool full = nq + 16 <= rows && (a.N & 7) == 0;
+      if (full) {
+        u32x4 q[2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            q[h][i] = static_cast<uint32_t>(tile[kl][nq + 8 * h + 2 * i]) |
+                      (static_cast<uint32_t>(tile[kl][nq + 8 * h + 2 * i + 1]) << 16);
+        reinterpret_cast<u32x4*>(dst)[0] = q[0];
+        reinterpret_cast<u32x4*>(dst)[1] = q[1];
+      } else {
+        for (int e = 0; e < 16; ++e)
+          if (nq + e < rows) dst[e] = tile[kl][nq + e];
+      }
+    }
+  }
+}
+
+template <bool ASYM, bool GIDX, int MT, int CPT>
+hipError_t launch_split4(const GradArgs& a, int P, int rows_per, hipStream_t s) {
+  const dim3 grid(static_cast<uint32_t>((a.K + kWave * CPT - 1) / (kWave * CPT)), static_cast<uint32_t>(P));
+  const size_t lds = static_cast<size_t>(MT) * CPT * kWave * sizeof(float);
+  grad_split_kernel<ASYM, GIDX, MT, CPT><<<grid, dim3(kGThreads), lds, s>>>(a, rows_per);
+  return hipGetLastError();
+}
+
+template <bool ASYM, bool GIDX, bool WIDE>
+hipError_t launch_split3(const GradArgs& a, int P, int rows_per, hipStream_t s) {
+  if (a.M <= 1) return launch_split4<ASYM, GIDX, 1, grad_cpt<1, WIDE>()>(a, P, rows_per, s);
+  if (a.M <= 2) return launch_split4<ASYM, GIDX, 2, grad_cpt<2, WIDE>()>(a, P, rows_per, s);
+  if (a.M <= 4) return launch_split4<ASYM, GIDX, 4, grad_cpt<4, WIDE>()>(a, P, rows_per, s);
+  if (a.M <= 8) return launch_split4<ASYM, GIDX, 8, 8>(a, P, rows_per, s);
+  return launch_split4<ASYM, GIDX, 16, 8>(a, P, rows_per, s);
+}
+
+}  // namespace
+
+GradPlan grad_plan(int64_t M, int64_t N, int64_t K, int64_t G, bool has_g_idx) {
+  GradPlan p{};
+  if (M <= kGradSkinnyMax) {
+    const int cpt = !has_g_idx && G % 32 == 0 && M <= 4 ? 32 : 8;     // columns per lane
+    const int64_t cb = (K + kWave * cpt - 1) / (kWave * cpt);        // column blocks
+    int64_t P = std::max<int64_t>(1, 512 / cb);                      // about 2 workgroups per CU
+    P = std::min<int64_t>(P, (N + 31) / 32);                          // at least 32 rows per slice
+    const int64_t per_slice = M * K * 4;
+    P = std::min<int64_t>(P, std::max<int64_t>(1, kGradPartialBytes / per_slice));
+    P = std::max<int64_t>(1, std::min<int64_t>(P, N));
+    p.slices = static_cast<int>(P);
+    p.rows_per = static_cast<int>((N + P - 1) / P);
+    p.slices = static_cast<int>((N + p.rows_per - 1) / p.rows_per);
+    p.workspace = static_cast<size_t>(p.slices) * static_cast<size_t>(M * K) * 4;
+  } else {
+    p.workspace = static_cast<size_t>(K) * static_cast<size_t>(N) * 2;
+  }
+  return p;
+}
+
+hipError_t launch_grad_input(const GradArgs& a, hipStream_t s) {
+  if (a.M <= 0) return hipSuccess;
+  const GradPlan p = grad_plan(a.M, a.N, a.K, a.G, a.g_idx != nullptr);
+  if (a.M <= kGradSkinnyMax) {
+    const bool wide = !a.g_idx && a.G % 32 == 0;
+    hipError_t e;
+    if (a.asym) {
+      e = a.g_idx ? launch_split3<true, true, false>(a, p.slices, p.rows_per, s)
+          : wide  ? launch_split3<true, false, true>(a, p.slices, p.rows_per, s)
+                  : launch_split3<true, false, false>(a, p.slices, p.rows_per, s);
+    } else {
+      e = a.g_idx ? launch_split3<false, true, false>(a, p.slices, p.rows_per, s)
+          : wide  ? launch_split3<false, false, true>(a, p.slices, p.rows_per, s)
+                  : launch_split3<false, false, false>(a, p.slices, p.rows_per, s);
+    }
+    if (e != hipSuccess) return e;
+    const int64_t total = a.M * a.K;
+    grad_reduce_kernel<<<dim3(static_cast<uint32_t>((total + kWave - 1) / kWave)), dim3(kRParts * kWave), 0, s>>>(
+        a.partial, p.slices, total, a.dx);
+    return hipGetLastError();
+  }
+  // transposed weight into the workspace, then the bf16 GEMM
+  DequantArgs d{a.codes, a.scales, a.zeros, a.g_idx, a.N, a.K, a.G, a.NG, a.asym, nullptr, 1};
+  uint16_t* wt = reinterpret_cast<uint16_t*>(a.partial);
+  const dim3 grid(static_cast<uint32_t>((a.K + kTT - 1) / kTT), static_cast<uint32_t>((a.N + kTT - 1) / kTT));
+  const size_t lds0 = kTT * (kTT + 2) * 2 + kTT * 4;
+  const size_t lds = lds0 + static_cast<size_t>(kTT) * a.NG * 5;
+  if (lds <= 65536) {
+    if (a.asym) {
+      if (a.g_idx) dequantize_t_kernel<true, true, true><<<grid, dim3(kGThreads), lds, s>>>(d, wt);
+      else dequantize_t_kernel<true, false, true><<<grid, dim3(kGThreads), lds, s>>>(d, wt);
+    } else {
+      if (a.g_idx) dequantize_t_kernel<false, true, true><<<grid, dim3(kGThreads), lds, s>>>(d, wt);
+      else dequantize_t_kernel<false, false, true><<<grid, dim3(kGThreads), lds, s>>>(d, wt);
+    }
+  } else {
+    if (a.asym) {
+      if (a.g_idx) dequantize_t_kernel<true, true, false><<<grid, dim3(kGThreads), lds0, s>>>(d, wt);
+      else dequantize_t_kernel<true, false, false><<<grid, dim3(kGThreads), lds0, s>>>(d, wt);
+    } else {
+      if (a.g_idx) dequantize_t_kernel<false, true, false><<<grid, dim3(kGThreads), lds0, s>>>(d, wt);
+      else dequantize_t_kernel<false, false, false><<<grid, dim3(kGThreads), lds0, s>>>(d, wt);
+    }
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return launch_gemm_bf16(a.dy, wt, nullptr, a.dx, a.M, a.K, a.N, s);
+}
+
+}  // namespace w4

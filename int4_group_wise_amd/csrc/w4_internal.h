@@ -43,6 +43,31 @@ struct LinearArgs {
   uint16_t* y;          // bf16 [M, N]
 };
 
+struct GradArgs {
+  const uint16_t* dy;   // bf16 [M, N]
+  int64_t M;
+  const uint8_t* codes;
+  const float* scales;
+  const uint8_t* zeros;
+  const int32_t* g_idx;
+  int64_t N, K, G, NG;
+  int asym;
+  uint16_t* dx;         // bf16 [M, K]
+  float* partial;       // workspace: fp32 slice partials (M <= 16) or bf16 Wd^T (M > 16)
+};
+
+// Input-gradient plan: M <= kGradSkinnyMax splits the rows of W into `slices`
+// of `rows_per` rows with fp32 partials (at most kGradPartialBytes of them);
+// larger M stages Wd^T.  `workspace` is the byte count either needs.
+constexpr int64_t kGradSkinnyMax = 16;
+constexpr int64_t kGradPartialBytes = int64_t(16) << 20;
+struct GradPlan {
+  int slices, rows_per;
+  size_t workspace;
+};
+GradPlan grad_plan(int64_t M, int64_t N, int64_t K, int64_t G, bool has_g_idx);
+hipError_t launch_grad_input(const GradArgs& a, hipStream_t s);
+
 // Largest group count the quantizer's per-row LDS tables hold.
 constexpr int64_t kMaxGroupsPerRow = 4096;
 

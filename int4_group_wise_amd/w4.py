@@ -57,6 +57,10 @@ def load() -> ctypes.CDLL:
     lib.w4_linear_workspace_bytes.argtypes = [I64, I64, I64, I64, I32, I32]
     lib.w4_linear.restype = I32
     lib.w4_linear.argtypes = [P, I64, P, P, P, P, I64, I64, I64, I32, P, P, P, SZ, P]
+    lib.w4_linear_grad_input_workspace_bytes.restype = SZ
+    lib.w4_linear_grad_input_workspace_bytes.argtypes = [I64, I64, I64, I64, I32, I32]
+    lib.w4_linear_grad_input.restype = I32
+    lib.w4_linear_grad_input.argtypes = [P, I64, P, P, P, P, I64, I64, I64, I32, P, P, SZ, P]
     _LIB = lib
     return lib
 
@@ -186,4 +190,36 @@ def linear(x, codes, scales, zeros, g_idx, K: int, G: int, mode="sym", bias=None
     _check(lib, lib.w4_linear(_ptr(x), M, _ptr(codes), _ptr(scales), _ptr(zeros), _ptr(g_idx),
                               N, K, G, mode, _ptr(bias), _ptr(out), _ptr(workspace), ws_bytes,
                               _stream(x.device)))
+    return out
+
+
+def linear_grad_input_workspace_bytes(M: int, N: int, K: int, G: int, mode="sym", has_g_idx=False) -> int:
+    lib = load()
+    return int(lib.w4_linear_grad_input_workspace_bytes(M, N, K, G, _mode(mode), int(bool(has_g_idx))))
+
+
+def linear_grad_input(dy, codes, scales, zeros, g_idx, K: int, G: int, mode="sym",
+                      out=None, workspace=None) -> torch.Tensor:
+    """``dx = dy . dequant(W)`` with dy bf16 [M, N]; returns bf16 [M, K].
+    ``out`` (bf16 [M, K]) and ``workspace`` (uint8, at least
+    ``linear_grad_input_workspace_bytes`` bytes) may be passed in to avoid
+    allocation."""
+    lib = load()
+    mode = _mode(mode)
+    N = codes.shape[0]
+    _format_args(N, K, G, mode, codes, scales, zeros, g_idx)
+    if dy.dim() != 2 or dy.shape[1] != N:
+        raise ValueError(f"dy must be [M, {N}]")
+    _dev(dy, "dy", torch.bfloat16)
+    M = dy.shape[0]
+    if out is None:
+        out = torch.empty((M, K), dtype=torch.bfloat16, device=dy.device)
+    _dev(out, "out", torch.bfloat16, (M, K))
+    need = int(lib.w4_linear_grad_input_workspace_bytes(M, N, K, G, mode, int(g_idx is not None)))
+    if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
+        workspace = torch.empty(need, dtype=torch.uint8, device=dy.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib, lib.w4_linear_grad_input(_ptr(dy), M, _ptr(codes), _ptr(scales), _ptr(zeros), _ptr(g_idx),
+                                         N, K, G, mode, _ptr(out), _ptr(workspace), ws_bytes,
+                                         _stream(dy.device)))
     return out

@@ -29,6 +29,7 @@ def _declared_functions():
 def test_header_declares_the_entry_points():
     names = _declared_functions()
     for f in ("w4_quantize_pack", "w4_dequantize", "w4_linear", "w4_linear_workspace_bytes",
+              "w4_linear_grad_input", "w4_linear_grad_input_workspace_bytes",
               "w4_abi_version", "w4_status_string", "w4_last_error"):
         assert f in names
 
@@ -97,6 +98,25 @@ def test_linear_rejects_and_workspace(lib):
     assert lib.w4_linear(FAKE, 64, FAKE, FAKE, None, None, 32, 128, 32, 0, None, FAKE, None, 0, None) == 1
     assert "workspace" in lib.w4_last_error().decode()
     assert lib.w4_linear(FAKE, 64, FAKE, FAKE, None, None, 32, 128, 32, 0, None, FAKE, FAKE, need - 1, None) == 1
+
+
+def test_grad_input_rejects_and_workspace(lib):
+    f = lib.w4_linear_grad_input
+    assert f(FAKE, 0, FAKE, FAKE, None, None, 4, 16, 8, 0, FAKE, None, 0, None) == 0
+    assert lib.w4_last_error() == b""
+    assert f(FAKE, -1, FAKE, FAKE, None, None, 4, 16, 8, 0, FAKE, FAKE, 1 << 20, None) == 1
+    assert f(None, 2, FAKE, FAKE, None, None, 4, 16, 8, 0, FAKE, FAKE, 1 << 20, None) == 1
+    assert f(FAKE, 2, FAKE, FAKE, None, None, 4, 16, 8, 0, ODD, FAKE, 1 << 20, None) == 1
+    assert "aligned" in lib.w4_last_error().decode()
+    assert f(FAKE, 2, FAKE, FAKE, FAKE, None, 4, 16, 8, 0, FAKE, FAKE, 1 << 20, None) == 1   # zeros with signed codes
+    # M <= 16: fp32 partials of row slices; M > 16: the transposed bf16 weight
+    small = lib.w4_linear_grad_input_workspace_bytes(2, 14336, 4096, 128, 1, 0)
+    assert small > 0 and small % (2 * 4096 * 4) == 0 and small <= 16 << 20
+    assert lib.w4_linear_grad_input_workspace_bytes(64, 32, 128, 32, 0, 0) == 32 * 128 * 2
+    need = lib.w4_linear_grad_input_workspace_bytes(2, 4, 16, 8, 0, 0)
+    assert f(FAKE, 2, FAKE, FAKE, None, None, 4, 16, 8, 0, FAKE, FAKE, need - 1, None) == 1
+    assert "workspace" in lib.w4_last_error().decode()
+    assert f(FAKE, 2, FAKE, FAKE, None, None, 4, 16, 8, 0, FAKE, None, need, None) == 1
 
 
 def test_binding_validates_before_calling():

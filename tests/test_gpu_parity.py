@@ -308,3 +308,90 @@ def test_empty_batch_and_errors():
         w4.quantize_pack(t["w"].to(DEV), 12, "sym")
     with pytest.raises(ValueError):
         w4.linear(torch.zeros(2, 64, dtype=torch.bfloat16, device=DEV), codes, scales, None, None, 64, 32, "asym")
+
+
+# ---------------------------------------------------------------------------
+# input gradient dx = dy . Wd
+# ---------------------------------------------------------------------------
+def _check_grad(M, N, K, G, mode, act, seed, cols=None, label=""):
+    rng = np.random.default_rng(seed)
+    w = (rng.standard_normal((N, K)) * 0.02).astype(np.float32)
+    gnp = (rng.permutation(K) // G % O.n_groups(K, G)).astype(np.int32) if act else None
+    oc, osc, oz = O.quantize_pack(w, G, _mode(mode), gnp)
+    dy = torch.from_numpy(rng.standard_normal((M, N)).astype(np.float32)).to(torch.bfloat16)
+    gi = None if gnp is None else torch.from_numpy(gnp).to(DEV)
+    z = None if oz is None else torch.from_numpy(oz).to(DEV)
+    c, s = torch.from_numpy(oc).to(DEV), torch.from_numpy(osc).to(DEV)
+    dx = w4.linear_grad_input(dy.to(DEV), c, s, z, gi, K, G, mode)
+    dx2 = w4.linear_grad_input(dy.to(DEV), c, s, z, gi, K, G, mode)
+    torch.cuda.synchronize()
+    assert torch.equal(dx.view(torch.int16), dx2.view(torch.int16)), f"grad not deterministic {label}"
+    sel = np.arange(K) if cols is None else cols
+    wd = O.bf16_bits_to_f32(O.dequantize(oc, osc, oz, gnp, K, G, _mode(mode), "bf16"))[:, sel]
+    ref = O.bf16_bits_to_f32(_bits(dy)).astype(np.float64) @ wd.astype(np.float64)
+    got = dx[:, torch.from_numpy(sel).to(DEV)].float().cpu().numpy().astype(np.float64)
+    err = got - ref
+    rel = np.linalg.norm(err) / max(np.linalg.norm(ref), 1e-30)
+    assert rel <= NORM_TOL, f"grad normwise {rel:.3e} {label}"
+    assert np.abs(err).max() <= ELEM_TOL * max(np.abs(ref).max(), 1e-30), f"grad max err {label}"
+
+
+GRAD_CASES = [
+    # M, N, K, G, mode, act-order: M <= 16 (row slices) and M > 16 (transposed weight + GEMM)
+    (1, 64, 512, 128, "asym", False), (4, 33, 1000, 40, "sym", True), (16, 100, 96, 32, "asym", False),
+    (3, 50, 99, 8, "sym", False), (2, 7, 8200, 64, "asym", False), (9, 300, 2048, 256, "sym", True),
+    (48, 64, 256, 64, "asym", False), (300, 130, 200, 8, "sym", True), (40, 96, 512, 128, "asym", False),
+    (17, 1, 64, 16, "sym", False), (20, 24, 2048, 8, "asym", True),   # 256 groups: tables read from memory
+]
+
+
+@pytest.mark.parametrize("case", GRAD_CASES, ids=lambda c: "M%d_N%d_K%d_G%d_%s%s" % (c[0], c[1], c[2], c[3], c[4], "_act" if c[5] else ""))
+def test_grad_input_small(case):
+    M, N, K, G, mode, act = case
+    _check_grad(M, N, K, G, mode, act, seed=M + N + K, label=str(case))
+
+
+def test_grad_input_decode_size():
+    """The decode layer's shape: the reduction runs over all 14336 rows."""
+    _check_grad(1, 14336, 4096, 128, "asym", False, seed=30, label="decode-size")
+
+
+def test_grad_input_prefill_size_sampled():
+    _check_grad(2048, 4096, 4096, 128, "asym", True, seed=31, cols=_sample_rows(4096, 256, 6), label="prefill-size")
+
+
+@pytest.mark.parametrize("M,K,mode", [(3, 520, "sym"), (24, 256, "asym")])
+def test_grad_input_unit_rows_are_exact(M, K, mode):
+    """dy row m = e_{n_m}: dx row m is the bf16 dequantized row n_m, bit for bit."""
+    N, G = 40, 8
+    rng = np.random.default_rng(32)
+    w = (rng.standard_normal((N, K)) * 0.02).astype(np.float32)
+    oc, osc, oz = O.quantize_pack(w, G, _mode(mode))
+    rows = rng.integers(0, N, size=M)
+    dy = torch.zeros(M, N)
+    dy[torch.arange(M), torch.from_numpy(rows)] = 1.0
+    z = None if oz is None else torch.from_numpy(oz).to(DEV)
+    dx = w4.linear_grad_input(dy.to(torch.bfloat16).to(DEV), torch.from_numpy(oc).to(DEV),
+                              torch.from_numpy(osc).to(DEV), z, None, K, G, mode)
+    wd = O.dequantize(oc, osc, oz, None, K, G, _mode(mode), "bf16")
+    assert np.array_equal(_bits(dx.cpu()), wd[rows])
+
+
+def test_grad_input_empty_and_errors():
+    N, K, G = 16, 64, 16
+    codes = torch.zeros(N, K // 2, dtype=torch.uint8, device=DEV)
+    scales = torch.ones(N, K // G, device=DEV)
+    dy = torch.zeros(0, N, dtype=torch.bfloat16, device=DEV)
+    assert w4.linear_grad_input(dy, codes, scales, None, None, K, G, "sym").shape == (0, K)
+    lib = w4.load()
+    dy = torch.zeros(2, N, dtype=torch.bfloat16, device=DEV)
+    dx = torch.empty(2, K, dtype=torch.bfloat16, device=DEV)
+    need = w4.linear_grad_input_workspace_bytes(2, N, K, G, "sym")
+    assert need > 0
+    ws = torch.empty(need, dtype=torch.uint8, device=DEV)
+    st = lib.w4_linear_grad_input(dy.data_ptr(), 2, codes.data_ptr(), scales.data_ptr(), None, None,
+                                  N, K, G, 0, dx.data_ptr(), ws.data_ptr(), need - 1, None)
+    assert st == 1 and b"workspace" in lib.w4_last_error()
+    st = lib.w4_linear_grad_input(dy.data_ptr() + 2, 2, codes.data_ptr(), scales.data_ptr(), None, None,
+                                  N, K, G, 0, dx.data_ptr(), ws.data_ptr(), need, None)
+    assert st == 1 and b"aligned" in lib.w4_last_error()
