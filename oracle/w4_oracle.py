@@ -1,6 +1,7 @@
 """Oracle: the plain CPU definition of group-wise 4-bit weight-only quantization
-(quantize, pack, unpack, dequantize) and of the W4A16 linear
-``y = x . dequant(W)^T + b``.
+(quantize, pack, unpack, dequantize), of the W4A16 linear
+``y = x . dequant(W)^T + b`` and its input gradient, and of the LoRA merge
+(dequantize, add a low-rank update, quantize again).
 
 TEST INFRASTRUCTURE.  Only the test suite, the smoke check and the benchmark's
 CPU-baseline leg import this module.  The HIP library never imports it, and the
@@ -40,6 +41,14 @@ Readings taken where the pages leave a step open:
   R7  The linear uses the bf16-rounded dequantized weight (the [Keras] forward
       casts the dequantized kernel to the compute dtype before the matmul),
       accumulates in fp64 and adds the bias in fp64.
+  R8  Group size -1 is per-channel: one group (one scale, and one zero-point
+      in asym mode) per row, as the [Keras] block size -1 keeps one scale per
+      output unit; any G >= K gives the same single group.
+  R9  LoRA merge: the float domain is fp32 (the [Keras] merge adds the update
+      to the dequantized kernel in the compute dtype; fp32 here).  The
+      low-rank product is accumulated in fp64 in rank order and rounded once
+      to fp32 (the page leaves the matmul's order to the backend); the merged
+      weight is quantized again with the layer's group size, mode and g_idx.
 """
 from __future__ import annotations
 
@@ -50,19 +59,27 @@ SYM = "sym"     # signed two's-complement nibbles, no zero-point
 ASYM = "asym"   # unsigned nibbles with a per-group zero-point
 
 __all__ = [
-    "SYM", "ASYM", "n_groups", "group_of_columns", "bf16_bits_to_f32",
+    "SYM", "ASYM", "PER_CHANNEL", "n_groups", "group_of_columns", "bf16_bits_to_f32",
     "f32_to_bf16_bits", "quantize", "pack_nibbles", "unpack_nibbles",
     "decode", "dequantize", "quantize_pack", "linear", "linear_grad_input", "validate_packed",
-    "payload_bytes",
+    "payload_bytes", "lora_merged_weight", "lora_merge",
 ]
 
 
 # ---------------------------------------------------------------------------
 # shapes and groups
 # ---------------------------------------------------------------------------
+PER_CHANNEL = -1   # group size meaning one group per row (R8)
+
+
 def n_groups(K: int, G: int) -> int:
     """Groups per row, ``ceil(K / G)`` ([Keras] ``_int4_build`` n_groups;
-    [LoopQ] ``validate`` scale shape with G = 32)."""
+    [LoopQ] ``validate`` scale shape with G = 32); 1 for ``G = -1``, the
+    per-channel block size of [Keras] ``_int4_build`` (R8)."""
+    if G == PER_CHANNEL:
+        return 1
+    if G < 1:
+        raise ValueError("G must be >= 1 or -1 (per-channel)")
     return -(-K // G)
 
 
@@ -70,6 +87,8 @@ def group_of_columns(K: int, G: int, g_idx=None) -> np.ndarray:
     """Group id of every input column (R6).  Default: contiguous blocks of G
     columns ([Keras] ``_int4_build``: floor of arange(input_dim) / block_size)."""
     if g_idx is None:
+        if G == PER_CHANNEL:
+            return np.zeros(K, dtype=np.int64)
         return np.arange(K, dtype=np.int64) // G
     gid = np.asarray(g_idx).astype(np.int64)
     if gid.shape != (K,):
@@ -276,6 +295,45 @@ def linear_grad_input(dy_bits, codes, scales, zeros, g_idx, K: int, G: int, mode
 # ---------------------------------------------------------------------------
 # format checks ([LoopQ] ``validate``, ``payload_bytes``)
 # ---------------------------------------------------------------------------
+# ---------------------------------------------------------------------------
+# LoRA merge ([Keras] ``Dense._get_kernel_with_merged_lora``)
+# ---------------------------------------------------------------------------
+def lora_merged_weight(codes, scales, zeros, g_idx, K: int, G: int, mode: str,
+                       lora_a, lora_b, lora_scale: float) -> np.ndarray:
+    """The float-domain merge, fp32 [N, K]:
+    ``Wd[n, k] + c * AB[n, k]`` with ``AB[n, k] = sum_j A[k, j] B[j, n]``.
+
+    ``lora_a`` fp32 [K, r] and ``lora_b`` fp32 [r, N] as the [Keras] layer
+    stores them (input features x rank, rank x units), ``c = fp32(lora_scale)``
+    (alpha / rank).  Steps (R9): Wd is the fp32 dequantized weight; AB is
+    accumulated in fp64 over j = 0 .. r-1 in that order (every product of two
+    fp32 values is exact in fp64) and rounded once to fp32; then
+    ``delta = fp32(c * AB)`` and ``merged = fp32(Wd + delta)``.
+    """
+    wd = dequantize(codes, scales, zeros, g_idx, K, G, mode, out="f32")
+    A = np.asarray(lora_a, dtype=F32)
+    B = np.asarray(lora_b, dtype=F32)
+    N = wd.shape[0]
+    if A.ndim != 2 or A.shape[0] != K or B.shape != (A.shape[1], N):
+        raise ValueError("lora_a must be [K, r] and lora_b [r, N]")
+    acc = np.zeros((N, K), dtype=np.float64)
+    for j in range(A.shape[1]):
+        acc += B[j].astype(np.float64)[:, None] * A[:, j].astype(np.float64)[None, :]
+    delta = (F32(lora_scale) * acc.astype(F32)).astype(F32)
+    return (wd + delta).astype(F32)
+
+
+def lora_merge(codes, scales, zeros, g_idx, K: int, G: int, mode: str,
+               lora_a, lora_b, lora_scale: float):
+    """Merge a low-rank update into a packed weight and quantize the result
+    again with the same group size, mode and group map ([Keras]
+    ``Dense._get_kernel_with_merged_lora``: dequantize, add
+    ``(alpha / rank) * A B``, re-quantize and pack).  Returns
+    ``(codes, scales, zeros)`` of the merged weight."""
+    merged = lora_merged_weight(codes, scales, zeros, g_idx, K, G, mode, lora_a, lora_b, lora_scale)
+    return quantize_pack(merged, G, mode, g_idx)
+
+
 def validate_packed(codes, scales, zeros, K: int, G: int, mode: str,
                     g_idx=None, narrow: bool = True) -> None:
     """Raise ValueError unless the packed tensors satisfy the format rules:

@@ -197,7 +197,11 @@ def test_per_channel_matches_gemma_uniform_quantize():
     rng = np.random.default_rng(11)
     K = 1024
     w = (rng.standard_normal((512, K)) * 0.02).astype(F32)
-    q, s, _ = O.quantize(w, K, O.SYM)
+    q, s, _ = O.quantize(w, O.PER_CHANNEL, O.SYM)
+    assert s.shape == (512, 1) and O.n_groups(K, O.PER_CHANNEL) == 1
+    qk, sk, _ = O.quantize(w, K, O.SYM)          # G = K and G > K name the same single group
+    qb, sb, _ = O.quantize(w, K + 8, O.SYM)
+    assert np.array_equal(q, qk) and np.array_equal(q, qb) and np.array_equal(s, sk) and np.array_equal(s, sb)
     inv = (F32(7) * (F32(1) / np.max(np.abs(w), axis=1))).astype(F32)
     qg = np.clip(np.rint((w * inv[:, None]).astype(F32)), -8, 7)
     diff = q.astype(np.int32) - qg.astype(np.int32)
@@ -411,3 +415,76 @@ def test_validate_rejects_malformed():
         O.validate_packed(codes, s, np.full((2, 1), 16, np.uint8), 5, 32, O.ASYM)
     with pytest.raises(ValueError):
         O.validate_packed(codes, s, None, 5, 32, O.SYM, g_idx=np.array([0, 0, 1, 0, 0]))
+
+
+# --------------------------------------------------------------------------
+# LoRA merge ([Keras] Dense._get_kernel_with_merged_lora)
+# --------------------------------------------------------------------------
+def _nearest_f32_of(fr):
+    """fp32 nearest to the rational ``fr`` (checked against both neighbours)."""
+    from fractions import Fraction
+    c = np.float32(float(fr))
+    for nb in (np.nextafter(c, np.float32(np.inf)), np.nextafter(c, np.float32(-np.inf))):
+        assert abs(Fraction(float(c)) - fr) <= abs(Fraction(float(nb)) - fr)
+    return c
+
+
+def test_lora_update_is_the_correctly_rounded_product():
+    """With all-zero codes (Wd = 0) and c = 1 the merged weight is the update
+    itself: every entry must be the fp32 nearest to the exact rational
+    sum_j A[k, j] B[j, n] (A is [K, r], B is [r, N]: entry (n, k))."""
+    from fractions import Fraction
+    rng = np.random.default_rng(21)
+    N, K, r = 5, 9, 3
+    A = rng.standard_normal((K, r)).astype(F32)
+    B = rng.standard_normal((r, N)).astype(F32)
+    codes = np.zeros((N, (K + 1) // 2), dtype=np.uint8)
+    scales = np.ones((N, 1), dtype=F32)
+    got = O.lora_merged_weight(codes, scales, None, None, K, O.PER_CHANNEL, O.SYM, A, B, 1.0)
+    for n in range(N):
+        for k in range(K):
+            exact = sum(Fraction(float(A[k, j])) * Fraction(float(B[j, n])) for j in range(r))
+            assert got[n, k] == _nearest_f32_of(exact), (n, k)
+
+
+@pytest.mark.parametrize("mode", [O.SYM, O.ASYM])
+def test_lora_zero_update_requantizes_to_itself(mode):
+    """c = 0 leaves the dequantized weight; quantizing it again must give the
+    same codes and zero-points (the quantizer is idempotent on its own grid:
+    every group reaches its extreme codes), and scales within one fp32 ulp."""
+    rng = np.random.default_rng(22)
+    N, K, G, r = 48, 320, 64, 4
+    w = (rng.standard_normal((N, K)) * 0.02).astype(F32)
+    c, s, z = O.quantize_pack(w, G, mode)
+    A = rng.standard_normal((K, r)).astype(F32)
+    B = rng.standard_normal((r, N)).astype(F32)
+    c2, s2, z2 = O.lora_merge(c, s, z, None, K, G, mode, A, B, 0.0)
+    assert np.array_equal(c2, c)
+    if z is not None:
+        assert np.array_equal(z2, z)
+    ulps = np.abs(s2.view(np.int32).astype(np.int64) - s.view(np.int32).astype(np.int64))
+    assert ulps.max() <= 1
+
+
+@pytest.mark.parametrize("mode,G,act", [(O.SYM, 32, False), (O.ASYM, 64, False), (O.ASYM, 32, True),
+                                        (O.SYM, O.PER_CHANNEL, False)])
+def test_lora_merge_is_within_the_quantization_bound(mode, G, act):
+    """End to end against real arithmetic: the merged codes dequantize to
+    Wd + (alpha / r) A B (exact, fp64 matmul) within half a step of the new
+    group scale (plus the fp32 roundings of the merge)."""
+    rng = np.random.default_rng(23)
+    N, K, r, alpha = 40, 256, 8, 16.0
+    w = (rng.standard_normal((N, K)) * 0.02).astype(F32)
+    gidx = (rng.permutation(K) // 32).astype(np.int32) if act else None
+    c, s, z = O.quantize_pack(w, G, mode, gidx)
+    A = (rng.standard_normal((K, r)) * 0.05).astype(F32)    # update ~ 2 quantization steps
+    B = (rng.standard_normal((r, N)) * 0.05).astype(F32)
+    c2, s2, z2 = O.lora_merge(c, s, z, gidx, K, G, mode, A, B, alpha / r)
+    target = O.dequantize(c, s, z, gidx, K, G, mode, out="f32").astype(np.float64) \
+        + (alpha / r) * (A.astype(np.float64) @ B.astype(np.float64)).T
+    got = O.dequantize(c2, s2, z2, gidx, K, G, mode, out="f32").astype(np.float64)
+    step = s2.astype(np.float64)[:, O.group_of_columns(K, G, gidx)]
+    slack = 4 * np.finfo(np.float32).eps * (np.abs(target) + step)
+    assert np.all(np.abs(got - target) <= 0.5 * step + slack)
+    # the update is not lost: at this size it moves many codes
+    assert np.mean(c2 != c) > 0.1
