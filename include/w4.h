@@ -14,6 +14,10 @@
  *           and group (same page: _dequantize_validated multiplies).
  *   zeros   uint8 [N, ceil(K/G)] zero-points 0..15, one per byte (W4_ASYM
  *           only; the keras dense.py diff page stores a kernel_zero per group).
+ *   G       group size: a multiple of 8 (>= 8), or per-channel, one group per
+ *           row, given as W4_PER_CHANNEL (-1) or any G >= K (keras dense.py
+ *           diff page: block size -1, one scale per output unit).  Below,
+ *           ceil(K/G) reads 1 for per-channel.
  *   g_idx   int32 [K] group of each input column, values in [0, ceil(K/G));
  *           NULL means column k belongs to group k / G (keras dense.py diff
  *           page: _int4_build g_idx initializer; MAX quantization.py page:
@@ -54,7 +58,10 @@
 extern "C" {
 #endif
 
-#define W4_ABI_VERSION 1
+#define W4_ABI_VERSION 2
+
+/* Group size meaning one group per row (per-channel scales). */
+#define W4_PER_CHANNEL (-1)
 
 typedef enum {
   W4_OK = 0,
@@ -82,8 +89,8 @@ const char* w4_last_error(void);
  *   w        [N, K] finite weights, fp32 (w_dtype = W4_F32) or bf16 (W4_BF16);
  *            codes of non-finite weights are unspecified.
  *   N, K     >= 1 (an empty matrix is rejected, as pack_weight rejects it).
- *   G        group size, 8 <= G <= 4096 and G % 8 == 0; at most 4096 groups
- *            per row, ceil(K/G) <= 4096 (else W4_ERR_UNSUPPORTED).
+ *   G        group size (see Data format); at most 4096 groups per row,
+ *            ceil(K/G) <= 4096 (else W4_ERR_UNSUPPORTED).
  *   mode     W4_SYM or W4_ASYM.
  *   g_idx    int32 [K] or NULL (contiguous groups).  Group statistics run over
  *            the columns mapped to each group; a group no column maps to gets
@@ -172,6 +179,48 @@ w4_status w4_linear_grad_input(const void* dy, int64_t M,
                                int64_t N, int64_t K, int64_t G, int mode,
                                void* dx, void* workspace, size_t workspace_bytes,
                                void* stream);
+
+/*
+ * w4_lora_merge_workspace_bytes — device scratch w4_lora_merge needs: 0 when
+ * the merge runs in one pass (no g_idx, G a power of two in [8, 512]), else
+ * the merged fp32 weight, N * K * 4 bytes.
+ */
+size_t w4_lora_merge_workspace_bytes(int64_t N, int64_t K, int64_t G, int mode,
+                                     int has_g_idx, int64_t rank);
+
+/*
+ * w4_lora_merge — fold a low-rank (LoRA) update into a packed weight and
+ * quantize the sum again.
+ *   (keras dense.py diff page: Dense._get_kernel_with_merged_lora —
+ *    dequantize, add (lora_alpha / lora_rank) * lora_kernel_a @ lora_kernel_b
+ *    in the float domain, re-quantize with the layer's block size, pack.)
+ *   merged[n, k] = fp32( fp32(v[n, k] * s[n, gid(k)])
+ *                        + fp32(lora_scale * fp32(sum_j A[k, j] * B[j, n])) )
+ *   The rank sum is accumulated in fp64 in order j = 0 .. rank-1 (each product
+ *   of two fp32 values is exact there) and rounded once to fp32.  The merged
+ *   weight is then quantized exactly as w4_quantize_pack quantizes an fp32
+ *   weight with the same G, mode and g_idx.
+ *   codes, scales, zeros, g_idx, N, K, G, mode  the packed weight, as in
+ *            w4_dequantize; at most 4096 groups per row.
+ *   lora_a   fp32 [K, rank] (input features x rank).
+ *   lora_b   fp32 [rank, N] (rank x output features).
+ *   rank     1 <= rank <= 64 (larger: W4_ERR_UNSUPPORTED).
+ *   lora_scale  the update's factor, alpha / rank.
+ *   codes_out, scales_out, zeros_out  out, shaped as codes, scales, zeros
+ *            (zeros_out NULL for W4_SYM).  Each may be the same pointer as
+ *            its input (merge in place); otherwise outputs must not overlap
+ *            the inputs.
+ *   workspace, workspace_bytes  device scratch of at least
+ *            w4_lora_merge_workspace_bytes(...) bytes (may be NULL when 0).
+ * Outputs are bit-exact functions of the inputs.
+ */
+w4_status w4_lora_merge(const uint8_t* codes, const float* scales,
+                        const uint8_t* zeros, const int32_t* g_idx,
+                        int64_t N, int64_t K, int64_t G, int mode,
+                        const float* lora_a, const float* lora_b, int64_t rank,
+                        float lora_scale,
+                        uint8_t* codes_out, float* scales_out, uint8_t* zeros_out,
+                        void* workspace, size_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus
 }

@@ -7,7 +7,8 @@ its ``workloads`` module) does not load the library.
 """
 _EXPORTS = ("SYM", "ASYM", "W4Error", "library_path", "load", "quantize_pack",
             "dequantize", "linear", "linear_workspace_bytes", "linear_grad_input",
-            "linear_grad_input_workspace_bytes")
+            "linear_grad_input_workspace_bytes", "lora_merge",
+            "lora_merge_workspace_bytes", "PER_CHANNEL", "n_groups")
 
 
 def __getattr__(name):

@@ -36,14 +36,23 @@ w4_status check_format(int64_t N, int64_t K, int64_t G, int mode, const void* ze
                        const void* g_idx, const char* fn) {
   if (N < 1 || K < 1) return fail(W4_ERR_INVALID_ARG, "%s: N and K must be >= 1 (got N=%lld K=%lld)", fn, (long long)N, (long long)K);
   if (N > kMaxDim || K > kMaxDim) return fail(W4_ERR_UNSUPPORTED, "%s: N and K must be <= 2^30", fn);
-  if (G < 8 || G > 4096 || G % 8 != 0)
-    return fail(W4_ERR_INVALID_ARG, "%s: group size G must be a multiple of 8 in [8, 4096] (got %lld)", fn, (long long)G);
+  if (G != W4_PER_CHANNEL && G < K && (G < 8 || G % 8 != 0))
+    return fail(W4_ERR_INVALID_ARG, "%s: group size G must be a multiple of 8 (>= 8), >= K, or W4_PER_CHANNEL (got %lld)",
+                fn, (long long)G);
   if (mode != W4_SYM && mode != W4_ASYM) return fail(W4_ERR_INVALID_ARG, "%s: mode must be W4_SYM or W4_ASYM", fn);
   if (mode == W4_ASYM && zeros == nullptr) return fail(W4_ERR_INVALID_ARG, "%s: W4_ASYM needs zero-points", fn);
   if (mode == W4_SYM && zeros != nullptr) return fail(W4_ERR_INVALID_ARG, "%s: W4_SYM takes no zero-points (pass NULL)", fn);
   if (zeros && !aligned16(zeros)) return fail(W4_ERR_INVALID_ARG, "%s: zeros must be 16-byte aligned", fn);
   if (g_idx && !aligned16(g_idx)) return fail(W4_ERR_INVALID_ARG, "%s: g_idx must be 16-byte aligned", fn);
   return W4_OK;
+}
+
+// Group size as the kernels take it.  W4_PER_CHANNEL or G >= K is one group
+// per row; every multiple of 128 that is >= K maps all columns to group 0 and
+// keeps open the fast paths that require G % 128 == 0.
+int64_t kernel_group(int64_t K, int64_t G) {
+  if (G == W4_PER_CHANNEL || G >= K) return (K + 127) / 128 * 128;
+  return G;
 }
 
 }  // namespace
@@ -70,6 +79,7 @@ w4_status w4_quantize_pack(const void* w, int w_dtype, int64_t N, int64_t K, int
   g_last_error.clear();
   const char* fn = "w4_quantize_pack";
   if (w4_status st = check_format(N, K, G, mode, zeros, g_idx, fn)) return st;
+  G = kernel_group(K, G);
   if (w_dtype != W4_F32 && w_dtype != W4_BF16) return fail(W4_ERR_INVALID_ARG, "%s: w_dtype must be W4_F32 or W4_BF16", fn);
   if (!w || !codes || !scales) return fail(W4_ERR_INVALID_ARG, "%s: w, codes and scales must be non-NULL", fn);
   if (!aligned16(w) || !aligned16(codes) || !aligned16(scales))
@@ -88,6 +98,7 @@ w4_status w4_dequantize(const uint8_t* codes, const float* scales, const uint8_t
   g_last_error.clear();
   const char* fn = "w4_dequantize";
   if (w4_status st = check_format(N, K, G, mode, zeros, g_idx, fn)) return st;
+  G = kernel_group(K, G);
   if (out_dtype != W4_F32 && out_dtype != W4_BF16) return fail(W4_ERR_INVALID_ARG, "%s: out_dtype must be W4_F32 or W4_BF16", fn);
   if (!codes || !scales || !out) return fail(W4_ERR_INVALID_ARG, "%s: codes, scales and out must be non-NULL", fn);
   if (!aligned16(codes) || !aligned16(scales) || !aligned16(out))
@@ -112,6 +123,7 @@ w4_status w4_linear(const void* x, int64_t M, const uint8_t* codes, const float*
   g_last_error.clear();
   const char* fn = "w4_linear";
   if (w4_status st = check_format(N, K, G, mode, zeros, g_idx, fn)) return st;
+  G = kernel_group(K, G);
   if (M < 0) return fail(W4_ERR_INVALID_ARG, "%s: M must be >= 0", fn);
   if (M > kMaxDim) return fail(W4_ERR_UNSUPPORTED, "%s: M must be <= 2^30", fn);
   if (M == 0) return W4_OK;
@@ -139,7 +151,8 @@ w4_status w4_linear(const void* x, int64_t M, const uint8_t* codes, const float*
 size_t w4_linear_grad_input_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t G, int mode,
                                             int has_g_idx) {
   (void)mode;
-  if (M < 1 || N < 1 || K < 1 || G < 1) return 0;
+  if (M < 1 || N < 1 || K < 1 || (G < 1 && G != W4_PER_CHANNEL)) return 0;
+  G = kernel_group(K, G);
   return w4::grad_plan(M, N, K, G, has_g_idx != 0).workspace;
 }
 
@@ -150,6 +163,7 @@ w4_status w4_linear_grad_input(const void* dy, int64_t M, const uint8_t* codes, 
   g_last_error.clear();
   const char* fn = "w4_linear_grad_input";
   if (w4_status st = check_format(N, K, G, mode, zeros, g_idx, fn)) return st;
+  G = kernel_group(K, G);
   if (M < 0) return fail(W4_ERR_INVALID_ARG, "%s: M must be >= 0", fn);
   if (M > kMaxDim) return fail(W4_ERR_UNSUPPORTED, "%s: M must be <= 2^30", fn);
   if (M == 0) return W4_OK;
@@ -174,6 +188,58 @@ w4_status w4_linear_grad_input(const void* dy, int64_t M, const uint8_t* codes, 
   w4::GradArgs a{static_cast<const uint16_t*>(dy), M, codes, scales, zeros, g_idx, N, K, G, NG,
                  mode == W4_ASYM, static_cast<uint16_t*>(dx), static_cast<float*>(workspace)};
   return hip_status(w4::launch_grad_input(a, static_cast<hipStream_t>(stream)), fn);
+}
+
+size_t w4_lora_merge_workspace_bytes(int64_t N, int64_t K, int64_t G, int mode, int has_g_idx, int64_t rank) {
+  (void)mode;
+  if (N < 1 || K < 1 || (G < 1 && G != W4_PER_CHANNEL) || rank < 1) return 0;
+  return w4::lora_workspace_bytes(N, K, kernel_group(K, G), has_g_idx != 0, rank);
+}
+
+w4_status w4_lora_merge(const uint8_t* codes, const float* scales, const uint8_t* zeros,
+                        const int32_t* g_idx, int64_t N, int64_t K, int64_t G, int mode,
+                        const float* lora_a, const float* lora_b, int64_t rank, float lora_scale,
+                        uint8_t* codes_out, float* scales_out, uint8_t* zeros_out,
+                        void* workspace, size_t workspace_bytes, void* stream) {
+  g_last_error.clear();
+  const char* fn = "w4_lora_merge";
+  if (w4_status st = check_format(N, K, G, mode, zeros, g_idx, fn)) return st;
+  const int64_t Gk = kernel_group(K, G);
+  if (rank < 1) return fail(W4_ERR_INVALID_ARG, "%s: rank must be >= 1", fn);
+  if (rank > w4::kLoraMaxRank) return fail(W4_ERR_UNSUPPORTED, "%s: rank must be <= %d", fn, w4::kLoraMaxRank);
+  if (!codes || !scales || !lora_a || !lora_b || !codes_out || !scales_out)
+    return fail(W4_ERR_INVALID_ARG, "%s: codes, scales, lora_a, lora_b, codes_out and scales_out must be non-NULL", fn);
+  if ((mode == W4_ASYM) != (zeros_out != nullptr))
+    return fail(W4_ERR_INVALID_ARG, "%s: zeros_out must be given for W4_ASYM and NULL for W4_SYM", fn);
+  if (!aligned16(codes) || !aligned16(scales) || !aligned16(lora_a) || !aligned16(lora_b) || !aligned16(codes_out) ||
+      !aligned16(scales_out) || (zeros_out && !aligned16(zeros_out)))
+    return fail(W4_ERR_INVALID_ARG, "%s: every tensor must be 16-byte aligned", fn);
+  const int64_t NG = (K + Gk - 1) / Gk;
+  if (NG > w4::kMaxGroupsPerRow)
+    return fail(W4_ERR_UNSUPPORTED, "%s: at most %lld groups per row (got %lld)", fn, (long long)w4::kMaxGroupsPerRow, (long long)NG);
+  // an output is either its input (in place) or disjoint from every input
+  const size_t cbytes = static_cast<size_t>(N) * static_cast<size_t>((K + 1) / 2);
+  const size_t sbytes = static_cast<size_t>(N) * static_cast<size_t>(NG) * 4u;
+  const size_t zbytes = static_cast<size_t>(N) * static_cast<size_t>(NG);
+  struct Span { const void* p; size_t n; };
+  const Span ins[] = {{codes, cbytes}, {scales, sbytes}, {zeros, zeros ? zbytes : 0}};
+  const Span outs[] = {{codes_out, cbytes}, {scales_out, sbytes}, {zeros_out, zeros_out ? zbytes : 0}};
+  for (int o = 0; o < 3; ++o)
+    for (int i = 0; i < 3; ++i) {
+      if (!outs[o].n || !ins[i].n || (o == i && outs[o].p == ins[i].p)) continue;
+      const uintptr_t a0 = reinterpret_cast<uintptr_t>(outs[o].p), b0 = reinterpret_cast<uintptr_t>(ins[i].p);
+      if (a0 < b0 + ins[i].n && b0 < a0 + outs[o].n)
+        return fail(W4_ERR_INVALID_ARG, "%s: an output overlaps an input other than its own", fn);
+    }
+  const size_t need = w4::lora_workspace_bytes(N, K, Gk, g_idx != nullptr, rank);
+  if (workspace_bytes < need || (need && !workspace))
+    return fail(W4_ERR_INVALID_ARG, "%s: workspace of %zu bytes needed (got %zu)", fn, need, workspace_bytes);
+  if (need && !aligned16(workspace)) return fail(W4_ERR_INVALID_ARG, "%s: workspace must be 16-byte aligned", fn);
+  if (N > kMaxGrid) return fail(W4_ERR_UNSUPPORTED, "%s: too many rows", fn);
+  w4::LoraArgs a{codes, scales, zeros, g_idx, N, K, Gk, NG, mode == W4_ASYM, lora_a, lora_b,
+                 static_cast<int>(rank), lora_scale, codes_out, scales_out, zeros_out,
+                 static_cast<float*>(workspace)};
+  return hip_status(w4::launch_lora_merge(a, static_cast<hipStream_t>(stream)), fn);
 }
 
 }  // extern "C"

@@ -348,26 +348,8 @@ __global__ __launch_bounds__(kDThreads) void dequantize_kernel(DequantArgs a, in
 // segments can reach up to 48 bytes into the next row, so the last row of
 // the matrix is read element by element instead.
 //
-// Division.  Only rint(fp32(w / s)) is needed.  With r = rcp(s) (relative
-// error <= 2^-23) and t = fp32(w r): |w / s| <= 15 (1 + 2^-23), hence
-// |t - w / s| < 2^-18.4, and fp32(w / s) is within 2^-20 of w / s, so
-// |t - fp32(w / s)| < 2^-18.  When t is farther than 2^-16 from the nearest
-// half-integer, rint(t) == rint(fp32(w / s)); otherwise, and whenever r is
-// not finite, the chunk is redone with the IEEE division.  The codes are
-// therefore exactly those of the plain division (weights are finite).
+// Statistics, division and packing of a chunk: quantize_chunk8 (w4_device.h).
 // ---------------------------------------------------------------------------
-constexpr float kTieMargin = 0.5f - 0x1p-16f;
-
-// max over the lanes of an aligned block of `lpg` lanes (a power of two <= 64)
-__device__ __forceinline__ float group_max(float m, int lpg) {
-  if (lpg > 1) m = fmaxf(m, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(m), 0xB1, 0xF, 0xF, false)));
-  if (lpg > 2) m = fmaxf(m, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(m), 0x4E, 0xF, 0xF, false)));
-  if (lpg > 4) m = fmaxf(m, __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(m), 0x1F | (4 << 10))));
-  if (lpg > 8) m = fmaxf(m, __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(m), 0x1F | (8 << 10))));
-  if (lpg > 16) m = fmaxf(m, __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(m), 0x1F | (16 << 10))));
-  if (lpg > 32) m = fmaxf(m, __shfl_xor(m, 32, kWave));
-  return m;
-}
 
 // The eight weights of chunk j (columns 8j .. 8j+7) of a row whose first byte
 // sits OB bytes past the 16-byte aligned pointer `rowA`.  OB < 0: element
@@ -443,61 +425,9 @@ __device__ __forceinline__ void quantize_row(const QuantArgs& a, int64_t n, int 
 #pragma unroll
       for (int e = 0; e < 8; ++e) v[c][e] = e < cnt ? v[c][e] : 0.0f;
     }
-    // group statistics: hi = max(0, max w), nl = max(0, max -w)  (signed: max |w|)
-    float m1 = 0.0f, m2 = 0.0f;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      if constexpr (ASYM) {
-        m1 = fmaxf(m1, v[c][e]);
-        m2 = fmaxf(m2, -v[c][e]);
-      } else {
-        m1 = fmaxf(m1, fabsf(v[c][e]));
-      }
-    }
-    m1 = group_max(m1, lpg);
-    if constexpr (ASYM) m2 = group_max(m2, lpg);
-    float sc, zf = 8.0f;
-    if constexpr (ASYM) {
-      sc = (m1 + m2) / 15.0f;
-      if (sc == 0.0f) sc = 1.0f;
-      zf = fminf(fmaxf(rintf(m2 / sc), 0.0f), 15.0f);
-    } else {
-      sc = m1 / 7.0f;
-      if (sc == 0.0f) sc = 1.0f;
-    }
+    float sc, zf;
+    const uint32_t packed = quantize_chunk8<ASYM>(v[c], cnt, lpg, sc, zf);
     if (cnt <= 0) continue;
-    const float rc = __builtin_amdgcn_rcpf(sc);
-    float qf[8];
-    float dmax = 0.0f;                         // largest |t - rint(t)| over the chunk
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const float t = v[c][e] * rc;
-      qf[e] = rintf(t);
-      dmax = fmaxf(dmax, fabsf(t - qf[e]));
-    }
-    // redo with the IEEE division the quotients that lie near a half-integer
-    // (about 1 weight in 300 for bf16 weights), or all of them when rc is not
-    // finite (s subnormal)
-    if (!(dmax < kTieMargin) || !(rc < __builtin_inff())) {
-      const bool all = !(rc < __builtin_inff());
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float t = v[c][e] * rc;
-        if (all || !(fabsf(t - qf[e]) < kTieMargin)) qf[e] = rintf(v[c][e] / sc);
-      }
-    }
-    // unsigned nibbles as bytes: q + z (zero-point), or q + 8 for signed codes
-    // (|w| <= 7 s there, so q is already in [-7, 7]; flipped back below)
-    uint32_t ev = 0, od = 0;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const float x = ASYM ? fminf(fmaxf(qf[e] + zf, 0.0f), 15.0f) : qf[e] + 8.0f;
-      if (e & 1) od = __builtin_amdgcn_cvt_pk_u8_f32(x, e >> 1, od);
-      else ev = __builtin_amdgcn_cvt_pk_u8_f32(x, e >> 1, ev);
-    }
-    uint32_t packed = ev | (od << 4);
-    if constexpr (!ASYM) packed ^= 0x88888888u;
-    if (cnt < 8) packed &= (1u << (4 * cnt)) - 1u;   // the nibble past the row end stays 0
     const int g = j / lpg;
     if ((lane & (lpg - 1)) == 0) {
       a.scales[n * a.NG + g] = sc;

@@ -68,6 +68,31 @@ struct GradPlan {
 GradPlan grad_plan(int64_t M, int64_t N, int64_t K, int64_t G, bool has_g_idx);
 hipError_t launch_grad_input(const GradArgs& a, hipStream_t s);
 
+struct LoraArgs {
+  const uint8_t* codes;
+  const float* scales;
+  const uint8_t* zeros;
+  const int32_t* g_idx;
+  int64_t N, K, G, NG;
+  int asym;
+  const float* a;       // fp32 [K, r]
+  const float* b;       // fp32 [r, N]
+  int r;
+  float c;              // scale of the update (alpha / rank)
+  uint8_t* codes_out;   // may be `codes` (in place)
+  float* scales_out;    // may be `scales`
+  uint8_t* zeros_out;   // may be `zeros`
+  float* merged;        // workspace: fp32 [N, K] merged weight (generic path)
+};
+
+// LoRA merge: contiguous power-of-two groups of 8 .. 512 columns with rank <=
+// kLoraMaxRank merge and quantize in one kernel (no workspace); any other
+// layout writes the merged fp32 weight to the workspace and quantizes it.
+constexpr int kLoraMaxRank = 64;
+bool lora_fused(int64_t K, int64_t G, bool has_g_idx, int64_t r);
+size_t lora_workspace_bytes(int64_t N, int64_t K, int64_t G, bool has_g_idx, int64_t r);
+hipError_t launch_lora_merge(const LoraArgs& a, hipStream_t s);
+
 // Largest group count the quantizer's per-row LDS tables hold.
 constexpr int64_t kMaxGroupsPerRow = 4096;
 

@@ -1,0 +1,242 @@
+// LoRA merge of a packed int4 weight (keras dense.py diff page:
+// Dense._get_kernel_with_merged_lora): dequantize, add the low-rank update
+// c * (A B)^T in the float domain, quantize again with the same group size,
+// mode and group map, and pack.
+//
+//   merged[n, k] = fp32( fp32(v[n, k] * s[n, gid(k)]) + fp32(c * fp32(AB[n, k])) )
+//   AB[n, k]     = sum_j A[k, j] B[j, n], accumulated in fp64 for j = 0 .. r-1
+//
+// A is [K, r] and B is [r, N] as the layer stores them.  Every product of two
+// fp32 values is exact in fp64, so the fp64 fused multiply-adds in rank order
+// round exactly like the plain definition; one rounding to fp32 follows.  The
+// merge's fp32 multiplies and add are compiled with contraction off, so each
+// rounds separately as the definition states.
+//
+// Layout.  A workgroup of 4 waves takes 512 columns (lane l owns columns
+// 8l .. 8l+7 of the block) and a block of rows; A^T for its columns is staged
+// once in LDS (fp32, [r][516]).  A wave takes 8 rows at a time: per rank step
+// a lane reads its 8 A values from LDS, the 8 rows' B values are uniform
+// (scalar loads), and 64 fp64 FMAs update its 8 x 8 accumulator tile.
+//
+// Epilogue.  Contiguous power-of-two groups of 8 .. 512 columns lie inside
+// the block, so the merged values are quantized in registers (group
+// statistics by lane reduction) and written over the outputs; the inputs of a
+// row are read before its outputs are written, so the merge may run in place.
+// Any other grouping (act-order, other group sizes, per-channel) writes the
+// merged fp32 weight to the workspace and the codec's quantizer packs it.
+
+#include "w4_device.h"
+#include "w4_internal.h"
+
+#include <algorithm>
+
+namespace w4 {
+namespace {
+
+constexpr int kLThreads = 256;
+constexpr int kLWaves = kLThreads / kWave;
+constexpr int kLCols = 8 * kWave;         // columns per workgroup
+constexpr int kLStride = kLCols + 4;      // LDS row of A^T (floats): 16-byte aligned, rows on different banks
+constexpr int kLRows = 8;                 // rows per wave step
+
+__device__ __forceinline__ uint32_t load_code_word(const uint8_t* __restrict__ codes, int64_t off, int cnt,
+                                                   bool aligned) {
+  if (aligned && cnt >= 8) return *reinterpret_cast<const uint32_t*>(codes + off);
+  uint32_t w = 0;
+  const int nbytes = min(4, (cnt + 1) / 2);
+  for (int b = 0; b < nbytes; ++b) w |= static_cast<uint32_t>(codes[off + b]) << (8 * b);
+  return w;
+}
+
+// fp32(fp32(v * s) + fp32(c * fp32(ab))): three separately rounded operations
+__device__ __forceinline__ float merge_value(int v, float s, float c, double ab) {
+#pragma clang fp contract(off)
+  const float wd = static_cast<float>(v) * s;
+  const float delta = c * static_cast<float>(ab);
+  return wd + delta;
+}
+
+template <bool ASYM, bool GIDX, bool QUANT>
+__global__ __launch_bounds__(kLThreads) void lora_merge_kernel(LoraArgs a, int rows_per_block) {
+  extern __shared__ __attribute__((aligned(16))) float at[];   // [r][kLStride]
+  const int lane = lane_id();
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int K = static_cast<int>(a.K);
+  const int r = a.r;
+  const int kb0 = blockIdx.x * kLCols;
+
+  // A^T of the block's columns (columns past K read as 0)
+  for (int kk = threadIdx.x; kk < kLCols; kk += kLThreads) {
+    const int k = kb0 + kk;
+    if (k < K) {
+      const float* src = a.a + static_cast<int64_t>(k) * r;
+      if ((r & 3) == 0) {
+        for (int j = 0; j < r; j += 4) {
+          const f32x4_t v = *reinterpret_cast<const f32x4_t*>(src + j);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) at[(j + i) * kLStride + kk] = v[i];
+        }
+      } else {
+        for (int j = 0; j < r; ++j) at[j * kLStride + kk] = src[j];
+      }
+    } else {
+      for (int j = 0; j < r; ++j) at[j * kLStride + kk] = 0.0f;
+    }
+  }
+  __syncthreads();
+
+  const int k0 = kb0 + 8 * lane;
+  const int cnt = K - k0;                              // valid columns of the lane (>= 8: all)
+  const int kc = min(k0, K - 1);
+  const int64_t KB = (a.K + 1) / 2;
+  const bool aligned = (KB & 3) == 0;
+  const int NG = static_cast<int>(a.NG);
+  const int gl = GIDX ? 0 : kc / static_cast<int>(a.G);   // the lane's group (contiguous groups)
+  int ge[8];                                           // group of each column (act-order)
+  if constexpr (GIDX) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) ge[e] = min(max(a.g_idx[min(kc + e, K - 1)], 0), NG - 1);
+  }
+  const int lpg = QUANT ? static_cast<int>(a.G) / 8 : 1;
+  const float c = a.c;
+
+  const int64_t n_begin = static_cast<int64_t>(blockIdx.y) * rows_per_block;
+  const int64_t n_end = min(a.N, n_begin + rows_per_block);
+  for (int64_t nb = n_begin + kLRows * w; nb < n_end; nb += kLRows * kLWaves) {
+    // the rows' codes and (contiguous groups) scales / zero-points, issued
+    // before the rank loop so that their latency hides behind it
+    uint32_t cw[kLRows];
+    float sc[kLRows];
+    int zp[kLRows];
+#pragma unroll
+    for (int q = 0; q < kLRows; ++q) {
+      const int64_t n = min(nb + q, n_end - 1);
+      cw[q] = cnt > 0 ? load_code_word(a.codes, n * KB + k0 / 2, cnt, aligned) : 0u;
+      if constexpr (!GIDX) {
+        sc[q] = a.scales[n * a.NG + gl];
+        zp[q] = ASYM ? static_cast<int>(a.zeros[n * a.NG + gl]) : 8;
+      }
+    }
+
+    double acc[kLRows][8];
+#pragma unroll
+    for (int q = 0; q < kLRows; ++q)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[q][e] = 0.0;
+    for (int j = 0; j < r; ++j) {
+      const f32x4_t a0 = *reinterpret_cast<const f32x4_t*>(&at[j * kLStride + 8 * lane]);
+      const f32x4_t a1 = *reinterpret_cast<const f32x4_t*>(&at[j * kLStride + 8 * lane + 4]);
+      double av[8];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        av[i] = static_cast<double>(a0[i]);
+        av[4 + i] = static_cast<double>(a1[i]);
+      }
+      const float* brow = a.b + static_cast<int64_t>(j) * a.N;
+#pragma unroll
+      for (int q = 0; q < kLRows; ++q) {
+        const double bv = static_cast<double>(brow[min(nb + q, n_end - 1)]);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[q][e] = __builtin_fma(av[e], bv, acc[q][e]);
+      }
+    }
+
+#pragma unroll
+    for (int q = 0; q < kLRows; ++q) {
+      const int64_t n = nb + q;
+      if (n >= n_end) break;                           // uniform: rows are per wave
+      float m[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int nib = static_cast<int>((cw[q] >> (4 * e)) & 15u);
+        float s;
+        int z;
+        if constexpr (GIDX) {
+          s = a.scales[n * a.NG + ge[e]];
+          z = ASYM ? static_cast<int>(a.zeros[n * a.NG + ge[e]]) : 8;
+        } else {
+          s = sc[q];
+          z = zp[q];
+        }
+        const int v = ASYM ? nib - z : ((nib ^ 8) - 8);
+        m[e] = e < cnt ? merge_value(v, s, c, acc[q][e]) : 0.0f;
+      }
+      if constexpr (QUANT) {
+        float gs, gz;
+        const uint32_t packed = quantize_chunk8<ASYM>(m, cnt, lpg, gs, gz);
+        if (cnt > 0) {
+          const int64_t off = n * KB + k0 / 2;
+          if (aligned && cnt >= 8) {
+            *reinterpret_cast<uint32_t*>(a.codes_out + off) = packed;
+          } else {
+            const int nbytes = min(4, (cnt + 1) / 2);
+            for (int b = 0; b < nbytes; ++b) a.codes_out[off + b] = static_cast<uint8_t>(packed >> (8 * b));
+          }
+          if ((lane & (lpg - 1)) == 0) {
+            a.scales_out[n * a.NG + gl] = gs;
+            if constexpr (ASYM) a.zeros_out[n * a.NG + gl] = static_cast<uint8_t>(gz);
+          }
+        }
+      } else {
+        if (cnt > 0) {
+          float* dst = a.merged + n * a.K + k0;
+          if (cnt >= 8 && (a.K & 3) == 0) {
+            reinterpret_cast<f32x4_t*>(dst)[0] = f32x4_t{m[0], m[1], m[2], m[3]};
+            reinterpret_cast<f32x4_t*>(dst)[1] = f32x4_t{m[4], m[5], m[6], m[7]};
+          } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+              if (e < cnt) dst[e] = m[e];
+          }
+        }
+      }
+    }
+  }
+}
+
+template <bool ASYM, bool GIDX, bool QUANT>
+hipError_t launch_lora3(const LoraArgs& a, hipStream_t s) {
+  const size_t lds = static_cast<size_t>(a.r) * kLStride * sizeof(float);
+  static bool attr_set = false;   // once per process: the A^T tile may pass 64 KB
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(lora_merge_kernel<ASYM, GIDX, QUANT>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       static_cast<int>(kLoraMaxRank * kLStride * sizeof(float)));
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  // about four workgroups per compute unit, row blocks a multiple of the
+  // workgroup's 32-row step
+  const int64_t cb = (a.K + kLCols - 1) / kLCols;
+  const int64_t step = kLRows * kLWaves;
+  int64_t rows = (a.N * cb + 1023) / 1024;
+  rows = std::max<int64_t>(step, (rows + step - 1) / step * step);
+  const dim3 grid(static_cast<uint32_t>(cb), static_cast<uint32_t>((a.N + rows - 1) / rows));
+  lora_merge_kernel<ASYM, GIDX, QUANT><<<grid, dim3(kLThreads), lds, s>>>(a, static_cast<int>(rows));
+  return hipGetLastError();
+}
+
+}  // namespace
+
+bool lora_fused(int64_t K, int64_t G, bool has_g_idx, int64_t r) {
+  (void)K;
+  return !has_g_idx && G >= 8 && G <= 512 && (G & (G - 1)) == 0 && r <= kLoraMaxRank;
+}
+
+size_t lora_workspace_bytes(int64_t N, int64_t K, int64_t G, bool has_g_idx, int64_t r) {
+  if (lora_fused(K, G, has_g_idx, r)) return 0;
+  return static_cast<size_t>(N) * static_cast<size_t>(K) * sizeof(float);
+}
+
+hipError_t launch_lora_merge(const LoraArgs& a, hipStream_t s) {
+  if (lora_fused(a.K, a.G, a.g_idx != nullptr, a.r))
+    return a.asym ? launch_lora3<true, false, true>(a, s) : launch_lora3<false, false, true>(a, s);
+  hipError_t e;
+  if (a.asym) e = a.g_idx ? launch_lora3<true, true, false>(a, s) : launch_lora3<true, false, false>(a, s);
+  else e = a.g_idx ? launch_lora3<false, true, false>(a, s) : launch_lora3<false, false, false>(a, s);
+  if (e != hipSuccess) return e;
+  const QuantArgs q{a.merged, 0, a.N, a.K, a.G, a.NG, a.asym, a.g_idx, a.codes_out, a.scales_out, a.zeros_out};
+  return launch_quantize_pack(q, s);
+}
+
+}  // namespace w4

@@ -29,6 +29,9 @@ class W4Error(RuntimeError):
         self.status = status
 
 
+ABI_VERSION = 2   # W4_ABI_VERSION of include/w4.h
+
+
 def library_path() -> str:
     return os.path.join(os.path.dirname(os.path.abspath(__file__)), "libw4.so")
 
@@ -45,6 +48,8 @@ def load() -> ctypes.CDLL:
     P, I64, I32, SZ = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_size_t
     lib.w4_abi_version.restype = I32
     lib.w4_abi_version.argtypes = []
+    if lib.w4_abi_version() != ABI_VERSION:
+        raise W4Error(-1, f"{path} has ABI version {lib.w4_abi_version()}, this binding needs {ABI_VERSION} (rebuild it)")
     lib.w4_status_string.restype = ctypes.c_char_p
     lib.w4_status_string.argtypes = [I32]
     lib.w4_last_error.restype = ctypes.c_char_p
@@ -61,6 +66,10 @@ def load() -> ctypes.CDLL:
     lib.w4_linear_grad_input_workspace_bytes.argtypes = [I64, I64, I64, I64, I32, I32]
     lib.w4_linear_grad_input.restype = I32
     lib.w4_linear_grad_input.argtypes = [P, I64, P, P, P, P, I64, I64, I64, I32, P, P, SZ, P]
+    lib.w4_lora_merge_workspace_bytes.restype = SZ
+    lib.w4_lora_merge_workspace_bytes.argtypes = [I64, I64, I64, I32, I32, I64]
+    lib.w4_lora_merge.restype = I32
+    lib.w4_lora_merge.argtypes = [P, P, P, P, I64, I64, I64, I32, P, P, I64, ctypes.c_float, P, P, P, P, SZ, P]
     _LIB = lib
     return lib
 
@@ -97,8 +106,18 @@ def _mode(mode) -> int:
     raise ValueError("mode must be 'sym' or 'asym'")
 
 
+PER_CHANNEL = -1   # group size: one group per row (W4_PER_CHANNEL)
+
+
+def n_groups(K: int, G: int) -> int:
+    """Groups per row: ceil(K / G), or 1 for per-channel (G = -1 or G >= K)."""
+    if G == PER_CHANNEL or G >= K:
+        return 1
+    return -(-K // G) if G > 0 else 0
+
+
 def _format_args(N, K, G, mode, codes, scales, zeros, g_idx):
-    NG = -(-K // G)
+    NG = n_groups(K, G)
     _dev(codes, "codes", torch.uint8, (N, (K + 1) // 2))
     _dev(scales, "scales", torch.float32, (N, NG))
     if mode == ASYM:
@@ -115,7 +134,8 @@ def quantize_pack(w: torch.Tensor, G: int, mode="sym", g_idx: torch.Tensor | Non
     """Quantize ``w`` [N, K] (fp32 or bf16, on the GPU) group-wise and pack it.
     Returns ``(codes uint8 [N, ceil(K/2)], scales fp32 [N, ceil(K/G)],
     zeros uint8 [N, ceil(K/G)] or None)``; ``out`` may hold that tuple
-    preallocated."""
+    preallocated.  ``G = -1`` (or any G >= K) is per-channel: one group per
+    row."""
     lib = load()
     mode = _mode(mode)
     if w.dim() != 2:
@@ -124,14 +144,14 @@ def quantize_pack(w: torch.Tensor, G: int, mode="sym", g_idx: torch.Tensor | Non
         raise ValueError("w must be float32 or bfloat16")
     _dev(w, "w", w.dtype)
     N, K = w.shape
-    NG = -(-K // G) if G > 0 else 0
+    NG = n_groups(K, G)
     if out is None:
         codes = torch.empty((N, (K + 1) // 2), dtype=torch.uint8, device=w.device)
         scales = torch.empty((N, NG), dtype=torch.float32, device=w.device)
         zeros = torch.empty((N, NG), dtype=torch.uint8, device=w.device) if mode == ASYM else None
     else:
         codes, scales, zeros = out
-    if G > 0:
+    if NG > 0:
         _format_args(N, K, G, mode, codes, scales, zeros, None)
     if g_idx is not None:
         _dev(g_idx, "g_idx", torch.int32, (K,))
@@ -223,3 +243,37 @@ def linear_grad_input(dy, codes, scales, zeros, g_idx, K: int, G: int, mode="sym
                                          N, K, G, mode, _ptr(out), _ptr(workspace), ws_bytes,
                                          _stream(dy.device)))
     return out
+
+
+def lora_merge_workspace_bytes(N: int, K: int, G: int, mode="sym", has_g_idx=False, rank=1) -> int:
+    lib = load()
+    return int(lib.w4_lora_merge_workspace_bytes(N, K, G, _mode(mode), int(bool(has_g_idx)), rank))
+
+
+def lora_merge(codes, scales, zeros, g_idx, K: int, G: int, mode, lora_a, lora_b, lora_scale: float,
+               out=None, workspace=None):
+    """Fold ``lora_scale * (lora_a @ lora_b)`` (lora_a fp32 [K, r], lora_b
+    fp32 [r, N]) into the packed weight and quantize again with the same
+    grouping.  Returns ``(codes, scales, zeros)``; ``out`` may be that tuple
+    preallocated, or the inputs themselves to merge in place."""
+    lib = load()
+    mode = _mode(mode)
+    N = codes.shape[0]
+    _format_args(N, K, G, mode, codes, scales, zeros, g_idx)
+    if lora_a.dim() != 2 or lora_a.shape[0] != K:
+        raise ValueError(f"lora_a must be [{K}, rank]")
+    r = lora_a.shape[1]
+    _dev(lora_a, "lora_a", torch.float32, (K, r))
+    _dev(lora_b, "lora_b", torch.float32, (r, N))
+    if out is None:
+        out = (torch.empty_like(codes), torch.empty_like(scales), None if zeros is None else torch.empty_like(zeros))
+    co, so, zo = out
+    _format_args(N, K, G, mode, co, so, zo, None)
+    need = int(lib.w4_lora_merge_workspace_bytes(N, K, G, mode, int(g_idx is not None), r))
+    if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
+        workspace = torch.empty(need, dtype=torch.uint8, device=codes.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib, lib.w4_lora_merge(_ptr(codes), _ptr(scales), _ptr(zeros), _ptr(g_idx), N, K, G, mode,
+                                  _ptr(lora_a), _ptr(lora_b), r, float(lora_scale), _ptr(co), _ptr(so), _ptr(zo),
+                                  _ptr(workspace), ws_bytes, _stream(codes.device)))
+    return co, so, zo

@@ -30,6 +30,7 @@ def test_header_declares_the_entry_points():
     names = _declared_functions()
     for f in ("w4_quantize_pack", "w4_dequantize", "w4_linear", "w4_linear_workspace_bytes",
               "w4_linear_grad_input", "w4_linear_grad_input_workspace_bytes",
+              "w4_lora_merge", "w4_lora_merge_workspace_bytes",
               "w4_abi_version", "w4_status_string", "w4_last_error"):
         assert f in names
 
@@ -45,7 +46,7 @@ def test_library_has_gfx950_code_object():
 
 
 def test_version_and_status_strings(lib):
-    assert lib.w4_abi_version() == 1
+    assert lib.w4_abi_version() == 2
     assert lib.w4_status_string(0) == b"ok"
     assert lib.w4_status_string(1) == b"invalid argument"
     assert lib.w4_status_string(2) == b"unsupported"
@@ -62,6 +63,11 @@ ODD = ctypes.c_void_p((1 << 20) + 2)
     ((FAKE, 0, 4, 0, 8, 0, None, FAKE, FAKE, None, None), 1, "N and K"),
     ((FAKE, 0, 4, 16, 12, 0, None, FAKE, FAKE, None, None), 1, "group size"),
     ((FAKE, 0, 4, 16, 0, 0, None, FAKE, FAKE, None, None), 1, "group size"),
+    ((FAKE, 0, 4, 16, -2, 0, None, FAKE, FAKE, None, None), 1, "group size"),
+    ((FAKE, 0, 4, 100, 4, 0, None, FAKE, FAKE, None, None), 1, "group size"),
+    ((FAKE, 7, 4, 100, -1, 0, None, FAKE, FAKE, None, None), 1, "w_dtype"),   # per-channel G passes
+    ((FAKE, 7, 4, 100, 100, 0, None, FAKE, FAKE, None, None), 1, "w_dtype"),  # G = K passes
+    ((FAKE, 7, 4, 100, 101, 0, None, FAKE, FAKE, None, None), 1, "w_dtype"),  # G > K passes
     ((FAKE, 0, 4, 16, 8, 7, None, FAKE, FAKE, None, None), 1, "mode"),
     ((FAKE, 0, 4, 16, 8, 1, None, FAKE, FAKE, None, None), 1, "zero-points"),
     ((FAKE, 0, 4, 16, 8, 0, None, FAKE, FAKE, FAKE, None), 1, "no zero-points"),
@@ -117,6 +123,38 @@ def test_grad_input_rejects_and_workspace(lib):
     assert f(FAKE, 2, FAKE, FAKE, None, None, 4, 16, 8, 0, FAKE, FAKE, need - 1, None) == 1
     assert "workspace" in lib.w4_last_error().decode()
     assert f(FAKE, 2, FAKE, FAKE, None, None, 4, 16, 8, 0, FAKE, None, need, None) == 1
+
+
+def test_lora_merge_rejects_and_workspace(lib):
+    f = lib.w4_lora_merge
+    B2 = ctypes.c_void_p((1 << 21))                 # a second buffer, disjoint from FAKE's spans
+    B3 = ctypes.c_void_p((1 << 22))
+    SC = ctypes.c_void_p((1 << 20) + 1024)          # scales, merged in place with the codes
+    ok = (FAKE, SC, None, None, 4, 16, 8, 0, B2, B3, 2, 1.0, FAKE, SC, None, None, 0, None)
+
+    def call(**kw):
+        args = list(ok)
+        names = ["codes", "scales", "zeros", "g_idx", "N", "K", "G", "mode", "a", "b", "rank", "c",
+                 "co", "so", "zo", "ws", "wsb", "stream"]
+        for k, v in kw.items():
+            args[names.index(k)] = v
+        return f(*args)
+
+    assert call(rank=0) == 1 and "rank" in lib.w4_last_error().decode()
+    assert call(rank=65) == 2 and "rank" in lib.w4_last_error().decode()
+    assert call(a=None) == 1 and "non-NULL" in lib.w4_last_error().decode()
+    assert call(zo=FAKE) == 1 and "zeros_out" in lib.w4_last_error().decode()
+    assert call(co=ODD) == 1 and "aligned" in lib.w4_last_error().decode()
+    # an output that overlaps another input (codes_out on top of scales)
+    assert call(co=ctypes.c_void_p((1 << 20) + 16), so=B3) == 1
+    assert "overlaps" in lib.w4_last_error().decode()
+    # one pass for contiguous power-of-two groups up to 512, else the fp32 merged weight
+    assert lib.w4_lora_merge_workspace_bytes(4, 16, 8, 0, 0, 2) == 0
+    assert lib.w4_lora_merge_workspace_bytes(4, 16, 8, 0, 1, 2) == 4 * 16 * 4
+    assert lib.w4_lora_merge_workspace_bytes(4, 4096, -1, 0, 0, 2) == 4 * 4096 * 4
+    assert lib.w4_lora_merge_workspace_bytes(4, 640, 40, 0, 0, 2) == 4 * 640 * 4
+    assert lib.w4_lora_merge_workspace_bytes(4, 640, 64, 0, 0, 64) == 0
+    assert call(g_idx=FAKE, wsb=4 * 16 * 4 - 1, ws=B2) == 1 and "workspace" in lib.w4_last_error().decode()
 
 
 def test_binding_validates_before_calling():

@@ -167,6 +167,13 @@ CASES = [
     (40, 70, 99, 16, "sym", False, "f32", "none"),      # prefill, K % 8 != 0
     (300, 260, 1024, 128, "asym", True, "f32", "randn"),
     (129, 128, 4096, 4096, "sym", False, "bf16", "none"),  # one group per row
+    # per-channel (G = -1, or any G >= K): one scale per row
+    (1, 40, 100, -1, "sym", False, "f32", "randn"),
+    (4, 33, 4096, -1, "sym", False, "bf16", "none"),     # matrix-core decode
+    (1, 24, 14336, -1, "asym", False, "f32", "randn"),   # decode kernel, one group over 14336 columns
+    (16, 64, 8192, -1, "asym", False, "f32", "none"),    # matrix-core batched decode
+    (20, 64, 8191, -1, "sym", False, "bf16", "none"),    # prefill, odd K
+    (3, 10, 5000, 6000, "sym", False, "f32", "randn"),   # G > K, not a multiple of 8
 ]
 
 
@@ -342,6 +349,7 @@ GRAD_CASES = [
     (3, 50, 99, 8, "sym", False), (2, 7, 8200, 64, "asym", False), (9, 300, 2048, 256, "sym", True),
     (48, 64, 256, 64, "asym", False), (300, 130, 200, 8, "sym", True), (40, 96, 512, 128, "asym", False),
     (17, 1, 64, 16, "sym", False), (20, 24, 2048, 8, "asym", True),   # 256 groups: tables read from memory
+    (1, 64, 4100, -1, "asym", False), (2, 50, 4096, -1, "sym", False), (20, 40, 300, -1, "sym", False),
 ]
 
 
@@ -395,3 +403,75 @@ def test_grad_input_empty_and_errors():
     st = lib.w4_linear_grad_input(dy.data_ptr() + 2, 2, codes.data_ptr(), scales.data_ptr(), None, None,
                                   N, K, G, 0, dx.data_ptr(), ws.data_ptr(), need, None)
     assert st == 1 and b"aligned" in lib.w4_last_error()
+
+
+# ---------------------------------------------------------------------------
+# LoRA merge: codes, scales and zero-points bit-exact against the oracle
+# ---------------------------------------------------------------------------
+def _lora_inputs(N, K, G, mode, act, r, seed):
+    rng = np.random.default_rng(seed)
+    w = (rng.standard_normal((N, K)) * 0.02).astype(np.float32)
+    gnp = (rng.permutation(K) // G % O.n_groups(K, G)).astype(np.int32) if act else None
+    oc, osc, oz = O.quantize_pack(w, G, _mode(mode), gnp)
+    A = (rng.standard_normal((K, r)) * 0.05).astype(np.float32)
+    B = (rng.standard_normal((r, N)) * 0.05).astype(np.float32)
+    return oc, osc, oz, gnp, A, B
+
+
+def _check_lora(N, K, G, mode, act, r, scale, seed, rows=None, in_place=False, label=""):
+    oc, osc, oz, gnp, A, B = _lora_inputs(N, K, G, mode, act, r, seed)
+    c, s = torch.from_numpy(oc).to(DEV), torch.from_numpy(osc).to(DEV)
+    z = None if oz is None else torch.from_numpy(oz).to(DEV)
+    gi = None if gnp is None else torch.from_numpy(gnp).to(DEV)
+    a, b = torch.from_numpy(A).to(DEV), torch.from_numpy(B).to(DEV)
+    out = (c, s, z) if in_place else None
+    c2, s2, z2 = w4.lora_merge(c, s, z, gi, K, G, mode, a, b, scale, out=out)
+    torch.cuda.synchronize()
+    sel = np.arange(N) if rows is None else rows
+    zsel = None if oz is None else oz[sel]
+    ec, es, ez = O.lora_merge(oc[sel], osc[sel], zsel, gnp, K, G, _mode(mode), A, B[:, sel], scale)
+    tsel = torch.from_numpy(sel).to(DEV)
+    assert np.array_equal(c2[tsel].cpu().numpy(), ec), f"merged codes differ {label}"
+    assert np.array_equal(s2[tsel].cpu().numpy().view(np.uint32), es.view(np.uint32)), f"merged scales differ {label}"
+    if ez is not None:
+        assert np.array_equal(z2[tsel].cpu().numpy(), ez), f"merged zeros differ {label}"
+    # the update moved codes (the inputs are sized for it unless scale = 0)
+    if scale != 0:
+        assert np.mean(ec != oc[sel]) > 0.05, f"update too small to test {label}"
+
+
+LORA_CASES = [
+    # N, K, G, mode, act-order, rank, alpha / rank: one pass (contiguous power-of-two groups <= 512)
+    (64, 512, 64, "sym", False, 8, 2.0),
+    (37, 1000, 8, "asym", False, 5, 0.5),        # partial column block, rank % 4 != 0
+    (33, 777, 32, "sym", False, 3, 1.0),         # odd K: code rows not word aligned
+    (20, 1536, 512, "asym", False, 64, 0.25),    # largest group, largest rank
+    (10, 64, 16, "asym", False, 1, 4.0),
+    (300, 2048, 128, "asym", False, 16, 2.0),    # several row blocks
+    # merged fp32 weight + quantizer
+    (50, 640, 64, "asym", True, 8, 2.0),         # act-order
+    (40, 640, 40, "sym", False, 4, 1.0),         # group size not a power of two
+    (24, 4100, -1, "asym", False, 16, 2.0),      # per-channel
+    (30, 2048, 1024, "sym", False, 12, 1.0),     # group wider than the column block
+]
+
+
+@pytest.mark.parametrize("case", LORA_CASES, ids=lambda c: "N%d_K%d_G%d_%s%s_r%d" % (c[0], c[1], c[2], c[3], "_act" if c[4] else "", c[5]))
+def test_lora_merge_small(case):
+    N, K, G, mode, act, r, scale = case
+    _check_lora(N, K, G, mode, act, r, scale, seed=N + K + r, label=str(case))
+
+
+@pytest.mark.parametrize("G,act", [(64, False), (64, True)])
+def test_lora_merge_in_place(G, act):
+    _check_lora(70, 1024, G, "asym", act, 8, 2.0, seed=5, in_place=True, label="in place")
+
+
+def test_lora_merge_zero_update():
+    _check_lora(40, 512, 32, "sym", False, 4, 0.0, seed=6, label="zero update")
+
+
+def test_lora_merge_decode_layer_sampled():
+    """The decode layer's weight (14336 x 4096, G = 128, zero-points), rank 16."""
+    _check_lora(14336, 4096, 128, "asym", False, 16, 2.0, seed=7, rows=_sample_rows(14336, 128, 8),
+                label="decode-size")
