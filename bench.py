@@ -10,8 +10,8 @@ model with many layers.  The JSON line reports whole-job HBM GB/s of the
 algorithmic bytes, the decode kernel's roofline (its average launch duration
 measured with HIP events on the launch stream), and the CPU oracle on a
 bounded sample.  Secondary entries cover the prefill GEMM (TFLOP/s), the
-batched decode, the input gradient (decode and prefill shapes) and the codec
-round trip.
+batched decode, the input gradient (decode and prefill shapes), the LoRA
+merge and the codec round trip.
 """
 from __future__ import annotations
 
@@ -28,6 +28,7 @@ import torch
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 BF16_MFMA_PEAK_TFS = 2516.6    # MI355X dense bf16 matrix cores
 MALL_BYTES = 256 << 20         # Infinity Cache
+FP64_VEC_PEAK_TFS = 78.6       # MI355X fp64 vector
 
 
 def algorithmic_bytes_linear(M, N, K, G, asym, bias):
@@ -268,6 +269,32 @@ def bench_secondary(w4):
                                  "config": {"workload": "prefill", "M": wl.M, "N": wl.N, "K": wl.K, "G": wl.G,
                                             "mode": wl.mode, "act_order": True}}
     del c, s, z, gi, dy, dx, gws
+
+    # LoRA merge at the decode layer's shape, rank 16: dequantize, add the
+    # fp64-accumulated update, quantize again (fp64 FMA bound)
+    wl = workload("decode")
+    t = generate(wl)
+    c, s, z = w4.quantize_pack(t["w"].to(dev), wl.G, wl.mode)
+    del t
+    rank = 16
+    gen = torch.Generator().manual_seed(3)
+    la = (torch.randn(wl.K, rank, generator=gen) * 0.05).to(dev)
+    lb = (torch.randn(rank, wl.N, generator=gen) * 0.05).to(dev)
+    outs = (torch.empty_like(c), torch.empty_like(s), torch.empty_like(z))
+    steps = 200
+    ev_ms, _ = time_graph(lambda i: w4.lora_merge(c, s, z, None, wl.K, wl.G, wl.mode, la, lb, 2.0, out=outs),
+                          20, steps, 20, 1)
+    sec = ev_ms * 1e-3 / steps
+    fl = 2.0 * wl.N * wl.K * rank                        # fp64 multiply-adds of the update
+    nbytes = 2 * (c.numel() + s.numel() * 4 + z.numel()) + (la.numel() + lb.numel()) * 4
+    out["lora_merge"] = {"metric": "LoRA merge fp64 GFLOP/s (rank 16)", "value": round(fl / sec / 1e9, 1),
+                         "unit": "GFLOP/s", "us_per_call": round(sec * 1e6, 2),
+                         "gbs_algorithmic": round(nbytes / sec / 1e9, 1),
+                         "roofline": {"bound": "alu", "achieved": round(fl / sec / 1e12, 3), "peak": FP64_VEC_PEAK_TFS,
+                                      "unit": "TFLOP/s", "frac": round(fl / sec / 1e12 / FP64_VEC_PEAK_TFS, 4)},
+                         "config": {"workload": "decode", "N": wl.N, "K": wl.K, "G": wl.G, "mode": wl.mode,
+                                    "rank": rank}}
+    del c, s, z, la, lb, outs
 
     # codec: bf16 W [28672, 8191] -> quantize_pack -> dequantize (bf16)
     wl = workload("codec")

@@ -15,6 +15,7 @@ typedef __attribute__((ext_vector_type(4))) float f32x4_t;
 typedef __attribute__((ext_vector_type(16))) float f32x16_t;
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
 typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
+typedef __attribute__((ext_vector_type(2))) double f64x2_t;
 
 // bf16 <-> fp32.  bf16 is the upper half of an fp32; rounding to bf16 is to
 // the nearest value, ties to the even significand, done on the bit pattern so
@@ -67,9 +68,23 @@ __device__ __forceinline__ float group_max(float m, int lpg) {
   return m;
 }
 
-template <bool ASYM>
-__device__ __forceinline__ uint32_t quantize_chunk8(const float v[8], int cnt, int lpg, float& sc_out, float& zf_out) {
-  // group statistics: hi = max(0, max w), nl = max(0, max -w)  (signed: max |w|)
+// group scale and zero-point (8 for signed codes) from the chunks of the
+// group's lpg lanes: hi = max(0, max w), nl = max(0, max -w) (signed: max |w|)
+// group_max with the group width fixed at compile time (no branches)
+template <int LPG>
+__device__ __forceinline__ float group_max_t(float m) {
+  if constexpr (LPG > 1) m = fmaxf(m, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(m), 0xB1, 0xF, 0xF, false)));
+  if constexpr (LPG > 2) m = fmaxf(m, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(m), 0x4E, 0xF, 0xF, false)));
+  if constexpr (LPG > 4) m = fmaxf(m, __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(m), 0x1F | (4 << 10))));
+  if constexpr (LPG > 8) m = fmaxf(m, __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(m), 0x1F | (8 << 10))));
+  if constexpr (LPG > 16) m = fmaxf(m, __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(m), 0x1F | (16 << 10))));
+  if constexpr (LPG > 32) m = fmaxf(m, __shfl_xor(m, 32, kWave));
+  return m;
+}
+
+// LPG > 0: the group is LPG lanes wide (compile time); LPG == 0: lpg lanes
+template <bool ASYM, int LPG = 0>
+__device__ __forceinline__ void group_scale(const float v[8], int lpg, float& sc, float& zf) {
   float m1 = 0.0f, m2 = 0.0f;
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
@@ -80,9 +95,14 @@ __device__ __forceinline__ uint32_t quantize_chunk8(const float v[8], int cnt, i
       m1 = fmaxf(m1, fabsf(v[e]));
     }
   }
-  m1 = group_max(m1, lpg);
-  if constexpr (ASYM) m2 = group_max(m2, lpg);
-  float sc, zf = 8.0f;
+  if constexpr (LPG > 0) {
+    m1 = group_max_t<LPG>(m1);
+    if constexpr (ASYM) m2 = group_max_t<LPG>(m2);
+  } else {
+    m1 = group_max(m1, lpg);
+    if constexpr (ASYM) m2 = group_max(m2, lpg);
+  }
+  zf = 8.0f;
   if constexpr (ASYM) {
     sc = (m1 + m2) / 15.0f;
     if (sc == 0.0f) sc = 1.0f;
@@ -91,8 +111,12 @@ __device__ __forceinline__ uint32_t quantize_chunk8(const float v[8], int cnt, i
     sc = m1 / 7.0f;
     if (sc == 0.0f) sc = 1.0f;
   }
+}
+
+// qf = rint(v * rcp(sc)); true when some quotient lies near a half-integer or
+// the reciprocal is not finite (then quant8_redo must run)
+__device__ __forceinline__ bool quant8_fast(const float v[8], float sc, float qf[8]) {
   const float rc = __builtin_amdgcn_rcpf(sc);
-  float qf[8];
   float dmax = 0.0f;                         // largest |t - rint(t)| over the chunk
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
@@ -100,19 +124,26 @@ __device__ __forceinline__ uint32_t quantize_chunk8(const float v[8], int cnt, i
     qf[e] = rintf(t);
     dmax = fmaxf(dmax, fabsf(t - qf[e]));
   }
-  // redo with the IEEE division the quotients that lie near a half-integer
-  // (about 1 weight in 300 for bf16 weights), or all of them when rc is not
-  // finite (s subnormal)
-  if (!(dmax < kTieMargin) || !(rc < __builtin_inff())) {
-    const bool all = !(rc < __builtin_inff());
+  return !(dmax < kTieMargin) || !(rc < __builtin_inff());
+}
+
+// redo with the IEEE division the quotients that lie near a half-integer
+// (about 1 weight in 300 for bf16 weights), or all of them when the
+// reciprocal is not finite (s subnormal); other values are left as they are
+__device__ __forceinline__ void quant8_redo(const float v[8], float sc, float qf[8]) {
+  const float rc = __builtin_amdgcn_rcpf(sc);
+  const bool all = !(rc < __builtin_inff());
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const float t = v[e] * rc;
-      if (all || !(fabsf(t - qf[e]) < kTieMargin)) qf[e] = rintf(v[e] / sc);
-    }
+  for (int e = 0; e < 8; ++e) {
+    const float t = v[e] * rc;
+    if (all || !(fabsf(t - qf[e]) < kTieMargin)) qf[e] = rintf(v[e] / sc);
   }
-  // unsigned nibbles as bytes: q + z (zero-point), or q + 8 for signed codes
-  // (|w| <= 7 s there, so q is already in [-7, 7]; flipped back below)
+}
+
+// unsigned nibbles as bytes: q + z (zero-point), or q + 8 for signed codes
+// (|w| <= 7 s there, so q is already in [-7, 7]; flipped back below)
+template <bool ASYM>
+__device__ __forceinline__ uint32_t pack8(const float qf[8], float zf, int cnt) {
   uint32_t ev = 0, od = 0;
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
@@ -123,9 +154,17 @@ __device__ __forceinline__ uint32_t quantize_chunk8(const float v[8], int cnt, i
   uint32_t packed = ev | (od << 4);
   if constexpr (!ASYM) packed ^= 0x88888888u;
   if (cnt < 8) packed &= cnt > 0 ? (1u << (4 * cnt)) - 1u : 0u;   // nibbles past the row end stay 0
+  return packed;
+}
+
+template <bool ASYM>
+__device__ __forceinline__ uint32_t quantize_chunk8(const float v[8], int cnt, int lpg, float& sc_out, float& zf_out) {
+  float sc, zf, qf[8];
+  group_scale<ASYM>(v, lpg, sc, zf);
+  if (quant8_fast(v, sc, qf)) quant8_redo(v, sc, qf);
   sc_out = sc;
   zf_out = zf;
-  return packed;
+  return pack8<ASYM>(qf, zf, cnt);
 }
 
 }  // namespace w4
