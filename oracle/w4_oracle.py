@@ -16,7 +16,8 @@ Sources, cited by page and section:
   [Gemma]  Gemma peft ``_quantization_utils.py`` page: ``uniform_quantize``.
   [Paddle] PaddleNLP ``quantization_linear.py`` page: ``quant_weight_forward``,
            ``QuantizationLinearFunc``.
-  [MAX]    Modular MAX ``graph/quantization.py`` page: ``QuantizationConfig``.
+  [MAX]    Modular MAX ``graph/quantization.py`` page: ``QuantizationConfig``,
+           ``QuantizationEncoding`` block parameters.
 
 Arithmetic.  The codec runs in fp32: ``np.float32`` arrays and constants only,
 IEEE round-to-nearest-even division, ``np.rint`` (round half to even).  The
@@ -49,6 +50,14 @@ Readings taken where the pages leave a step open:
       low-rank product is accumulated in fp64 in rank order and rounded once
       to fp32 (the page leaves the matmul's order to the backend); the merged
       weight is quantized again with the layer's group size, mode and g_idx.
+  R10 Packed zero-points: the zero-points are 4-bit values, stored two per
+      byte with the codes' nibble order (group 2j low, 2j+1 high).
+  R11 GGUF Q4_0 ([MAX] gives only the block: 32 weights in 18 bytes, the
+      scale d then 4-bit codes): d is fp16; codes are stored as q + 8 and
+      read as (q - 8) * d; weight i of a block sits in the low nibble of byte
+      i for i < 16 and in the high nibble of byte i - 16 otherwise (the GGUF
+      layout); the quantizer is the signed group-32 rule R3 taken against the
+      stored fp16 scale.
 """
 from __future__ import annotations
 
@@ -62,7 +71,8 @@ __all__ = [
     "SYM", "ASYM", "PER_CHANNEL", "n_groups", "group_of_columns", "bf16_bits_to_f32",
     "f32_to_bf16_bits", "quantize", "pack_nibbles", "unpack_nibbles",
     "decode", "dequantize", "quantize_pack", "linear", "linear_grad_input", "validate_packed",
-    "payload_bytes", "lora_merged_weight", "lora_merge",
+    "payload_bytes", "lora_merged_weight", "lora_merge", "pack_zeros", "unpack_zeros", "Q4_0_BLOCK", "Q4_0_BYTES",
+    "q4_0_quantize", "q4_0_dequantize",
 ]
 
 
@@ -295,6 +305,71 @@ def linear_grad_input(dy_bits, codes, scales, zeros, g_idx, K: int, G: int, mode
 # ---------------------------------------------------------------------------
 # format checks ([LoopQ] ``validate``, ``payload_bytes``)
 # ---------------------------------------------------------------------------
+# ---------------------------------------------------------------------------
+# packed zero-points (R10)
+# ---------------------------------------------------------------------------
+def pack_zeros(zeros) -> np.ndarray:
+    """Zero-points two per byte along the row, group 2j in the low nibble of
+    byte j and group 2j+1 in the high nibble (the [LoopQ] nibble order of the
+    codes); an odd group count leaves the last high nibble 0.  uint8 [N, NG]
+    -> uint8 [N, ceil(NG/2)]."""
+    z = np.asarray(zeros)
+    if z.ndim != 2 or z.size and (z.min() < 0 or z.max() > 15):
+        raise ValueError("zeros must be a matrix of values 0..15")
+    return pack_nibbles(z.astype(np.int16))
+
+
+def unpack_zeros(packed, NG: int) -> np.ndarray:
+    """Inverse of ``pack_zeros``: uint8 [N, ceil(NG/2)] -> uint8 [N, NG]."""
+    return unpack_nibbles(packed, NG).astype(np.uint8)
+
+
+# ---------------------------------------------------------------------------
+# GGUF Q4_0 block codec (R11)
+# ---------------------------------------------------------------------------
+Q4_0_BLOCK = 32    # weights per block ([MAX] block parameters of Q4_0)
+Q4_0_BYTES = 18    # the block's 2-byte scale d, then 16 bytes of 4-bit codes
+
+
+def q4_0_quantize(w) -> np.ndarray:
+    """Quantize ``w`` fp32 [N, K] (K a multiple of 32) into Q4_0 blocks,
+    uint8 [N, K/32, 18] (R11): per block of 32 consecutive weights of a row
+    ``d = fp16(fp32(amax / 7))``; ``q = clamp(rint(fp32(w / d)), -7, 7)``
+    with d widened back to fp32 (every code 0 when d is 0); bytes 0..1 hold d
+    (little-endian fp16), byte 2 + i holds q[i] + 8 in its low nibble and
+    q[i + 16] + 8 in its high nibble."""
+    w = np.asarray(w, dtype=F32)
+    N, K = w.shape
+    if K % Q4_0_BLOCK:
+        raise ValueError("Q4_0 needs K to be a multiple of 32")
+    nb = K // Q4_0_BLOCK
+    blk = w.reshape(N, nb, Q4_0_BLOCK)
+    amax = np.max(np.abs(blk), axis=2)
+    d16 = (amax / F32(7)).astype(F32).astype(np.float16)
+    d = d16.astype(F32)
+    safe = np.where(d == F32(0), F32(1), d)
+    q = np.clip(np.rint((blk / safe[..., None]).astype(F32)), -7, 7)
+    q = np.where(d[..., None] == F32(0), 0, q)
+    u = (q + 8).astype(np.uint8)
+    out = np.empty((N, nb, Q4_0_BYTES), dtype=np.uint8)
+    out[..., 0:2] = d16.astype("<f2").view(np.uint8).reshape(N, nb, 2)
+    out[..., 2:] = u[..., :16] | (u[..., 16:] << 4)
+    return out
+
+
+def q4_0_dequantize(blocks, out: str = "f32") -> np.ndarray:
+    """Dense weight [N, 32 * nb] from Q4_0 blocks uint8 [N, nb, 18]:
+    ``fp32(q - 8) * d`` (one fp32 multiply), ``out='bf16'`` gives the RNE
+    bf16 bit patterns."""
+    b = np.asarray(blocks, dtype=np.uint8)
+    N, nb, _ = b.shape
+    d = np.ascontiguousarray(b[..., 0:2]).view("<f2")[..., 0].astype(F32)
+    qs = b[..., 2:]
+    u = np.concatenate([qs & 15, qs >> 4], axis=-1).astype(np.int16)
+    v = ((u - 8).astype(F32) * d[..., None]).astype(F32).reshape(N, nb * Q4_0_BLOCK)
+    return f32_to_bf16_bits(v) if out == "bf16" else v
+
+
 # ---------------------------------------------------------------------------
 # LoRA merge ([Keras] ``Dense._get_kernel_with_merged_lora``)
 # ---------------------------------------------------------------------------

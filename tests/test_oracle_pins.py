@@ -488,3 +488,121 @@ def test_lora_merge_is_within_the_quantization_bound(mode, G, act):
     assert np.all(np.abs(got - target) <= 0.5 * step + slack)
     # the update is not lost: at this size it moves many codes
     assert np.mean(c2 != c) > 0.1
+
+
+# --------------------------------------------------------------------------
+# packed zero-points (R10)
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("NG", [1, 2, 7, 32, 33])
+def test_packed_zeros_layout_and_round_trip(NG):
+    rng = np.random.default_rng(31 + NG)
+    z = rng.integers(0, 16, size=(5, NG)).astype(np.uint8)
+    p = O.pack_zeros(z)
+    assert p.shape == (5, (NG + 1) // 2) and p.dtype == np.uint8
+    # byte j holds group 2j (low nibble) and group 2j + 1 (high nibble), written out
+    for n in range(5):
+        for j in range(p.shape[1]):
+            hi = int(z[n, 2 * j + 1]) if 2 * j + 1 < NG else 0
+            assert int(p[n, j]) == int(z[n, 2 * j]) + 16 * hi
+    assert np.array_equal(O.unpack_zeros(p, NG), z)
+    with pytest.raises(ValueError):
+        O.pack_zeros(np.full((1, 2), 16, dtype=np.uint8))
+
+
+# --------------------------------------------------------------------------
+# GGUF Q4_0 block codec (R11)
+# --------------------------------------------------------------------------
+def test_q4_0_hand_worked_block():
+    """w[i] = (i - 16) * 7/128: amax = 7/8, so d = 1/8 exactly (fp16 0x3000) and
+    w/d = (i - 16) * 7/16; i = 8 and 24 are exact ties (-3.5, 3.5 -> -4, 4).
+    Expected bytes from exact rationals and Python's half-even round()."""
+    from fractions import Fraction
+    w = np.array([[(i - 16) * 7 / 128 for i in range(32)]], dtype=F32)
+    got = O.q4_0_quantize(w)
+    assert got.shape == (1, 1, 18)
+    q = [max(-7, min(7, round(Fraction(i - 16) * Fraction(7, 16)))) for i in range(32)]
+    assert q[8] == -4 and q[24] == 4
+    expect = [0x00, 0x30] + [(q[i] + 8) | ((q[i + 16] + 8) << 4) for i in range(16)]
+    assert got[0, 0].tolist() == expect
+    # and back: (q - 8) * d with d = 1/8, exact
+    assert np.array_equal(O.q4_0_dequantize(got)[0], np.array([qq / 8 for qq in q], dtype=F32))
+
+
+def test_q4_0_decodes_hand_built_bytes():
+    """d = 0.5 (fp16 0x3800); byte 2 + i = low nibble a_i, high nibble b_i gives
+    weight i = (a_i - 8) / 2 and weight 16 + i = (b_i - 8) / 2."""
+    blk = np.zeros((1, 1, 18), dtype=np.uint8)
+    blk[0, 0, 0:2] = [0x00, 0x38]
+    lo = [(3 * i) % 16 for i in range(16)]
+    hi = [(5 * i + 1) % 16 for i in range(16)]
+    blk[0, 0, 2:] = [a | (b << 4) for a, b in zip(lo, hi)]
+    want = [(a - 8) / 2 for a in lo] + [(b - 8) / 2 for b in hi]
+    assert O.q4_0_dequantize(blk)[0].tolist() == want
+
+
+def test_q4_0_equals_signed_group32_when_the_scale_is_exact():
+    """When amax / 7 is representable in fp16 the Q4_0 block holds exactly the
+    signed G = 32 quantization (R3): same codes, same dequantized values."""
+    rng = np.random.default_rng(41)
+    N, K = 16, 256
+    w = (rng.uniform(-1, 1, size=(N, K)) * 0.8).astype(F32)
+    blk = w.reshape(N, K // 32, 32)
+    pos = rng.integers(0, 32, size=(N, K // 32))
+    scale = np.float32(2.0) ** rng.integers(-6, 2, size=(N, K // 32)).astype(F32)
+    for n in range(N):
+        for b in range(K // 32):
+            blk[n, b] *= scale[n, b]
+            blk[n, b, pos[n, b]] = 0.875 * scale[n, b] * (1 if (n + b) % 2 else -1)   # amax = 7 * 2^k / 8
+    w = blk.reshape(N, K)
+    q4 = O.q4_0_quantize(w)
+    qs = q4[..., 2:]
+    u = np.concatenate([qs & 15, qs >> 4], axis=-1).reshape(N, K).astype(np.int16) - 8
+    q, s, _ = O.quantize(w, 32, O.SYM)
+    assert np.array_equal(u, q)
+    assert np.array_equal(O.q4_0_dequantize(q4), O.dequantize(O.pack_nibbles(q), s, None, None, K, 32, O.SYM, "f32"))
+
+
+def test_q4_0_scale_is_nearest_fp16_and_error_bound():
+    rng = np.random.default_rng(42)
+    w = (rng.standard_normal((64, 512)) * 0.02).astype(F32)
+    q4 = O.q4_0_quantize(w)
+    d = np.ascontiguousarray(q4[..., 0:2]).view("<f2")[..., 0].astype(np.float64)
+    amax = np.max(np.abs(w.reshape(64, 16, 32)), axis=2).astype(np.float64)
+    ideal = amax / 7
+    # nearest fp16: no fp16 neighbour is closer (fp32(amax/7) is within 2^-24 relative)
+    for nb in (np.nextafter(d.astype(np.float16), np.float16(np.inf)), np.nextafter(d.astype(np.float16), np.float16(0))):
+        assert np.all(np.abs(d - ideal) <= np.abs(nb.astype(np.float64) - ideal) + ideal * 2 ** -23)
+    deq = O.q4_0_dequantize(q4).astype(np.float64).reshape(64, 16, 32)
+    err = np.abs(deq - w.astype(np.float64).reshape(64, 16, 32))
+    bound = d[..., None] / 2 + 7 * np.abs(ideal - d)[..., None] + 1e-12
+    assert np.all(err <= bound * (1 + 2 ** -20))
+    u = np.concatenate([q4[..., 2:] & 15, q4[..., 2:] >> 4], axis=-1)
+    assert u.min() >= 1 and u.max() <= 15          # codes q + 8 with |q| <= 7
+
+
+def test_q4_0_zero_block_and_shape_check():
+    w = np.zeros((2, 64), dtype=F32)
+    w[1, 32:] = np.linspace(-1, 1, 32, dtype=F32)
+    q4 = O.q4_0_quantize(w)
+    assert q4[0].tolist() == [[0, 0] + [0x88] * 16] * 2 and q4[1, 0].tolist() == [0, 0] + [0x88] * 16
+    assert np.all(O.q4_0_dequantize(q4)[0] == 0)
+    with pytest.raises(ValueError):
+        O.q4_0_quantize(np.zeros((1, 48), dtype=F32))
+
+
+def test_q4_0_quantizes_against_the_stored_scale():
+    """The codes are taken against the stored fp16 d, and clamped to [-7, 7].
+    amax = 1: d = fp16(1/7) = 1170/1024 * 2^-3, 0.024% below 1/7; the weight
+    3.5 d is an exact tie for d (-> 4) but lies below the tie for 1/7 (-> 3).
+    A block with amax = 10 * 2^-24 has d = 2^-24 (the smallest fp16
+    subnormal), so w / d = 10 clamps to 7."""
+    d16 = 1170 / 1024 / 8
+    w = np.zeros((2, 32), dtype=F32)
+    w[0, 0] = 1.0
+    w[0, 1] = 3.5 * d16
+    w[1, 0] = 10 * 2.0 ** -24
+    q4 = O.q4_0_quantize(w)
+    assert np.ascontiguousarray(q4[0, 0, 0:2]).view("<f2")[0] == np.float16(d16)
+    assert (q4[0, 0, 2] & 15) == 15 and (q4[0, 0, 3] & 15) == 8 + 4
+    assert np.ascontiguousarray(q4[1, 0, 0:2]).view("<f2")[0] == np.float16(2.0 ** -24)
+    assert (q4[1, 0, 2] & 15) == 15
