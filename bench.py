@@ -11,7 +11,7 @@ algorithmic bytes, the decode kernel's roofline (its average launch duration
 measured with HIP events on the launch stream), and the CPU oracle on a
 bounded sample.  Secondary entries cover the prefill GEMM (TFLOP/s), the
 batched decode, the input gradient (decode and prefill shapes), the LoRA
-merge and the codec round trip.
+merge, the codec round trip, the GGUF Q4_0 codec and the zero-point packing.
 """
 from __future__ import annotations
 
@@ -315,6 +315,39 @@ def bench_secondary(w4):
                     "quantize_pack": {"GB/s": round(gq, 1), "us": round(ev_q * 1e3 / steps, 1), "frac": round(gq / HBM_PEAK_GBS, 4)},
                     "dequantize": {"GB/s": round(gd, 1), "us": round(ev_d * 1e3 / steps, 1), "frac": round(gd / HBM_PEAK_GBS, 4)},
                     "config": {"workload": "codec", "N": wl.N, "K": wl.K, "G": wl.G, "mode": wl.mode, "w_dtype": "bf16"}}
+    del c, s, d, c2, s2, w
+
+    # GGUF Q4_0 blocks of the codec weight at K = 8192 (bf16 [28672, 8192]):
+    # quantize (2 B read + 18/32 B written per weight) and dequantize to bf16
+    wl = workload("codec", K=8192)
+    t = generate(wl)
+    w = t["w"].to(dev)
+    del t
+    blocks = w4.q4_0_quantize(w)
+    d = torch.empty(wl.N, wl.K, dtype=torch.bfloat16, device=dev)
+    ev_q, _ = time_graph(lambda i: w4.q4_0_quantize(w, out=blocks), 5, steps, 5, 1)
+    ev_d, _ = time_graph(lambda i: w4.q4_0_dequantize(blocks, torch.bfloat16, out=d), 5, steps, 5, 1)
+    nb = wl.N * wl.K * 2 + blocks.numel()
+    gq = nb * steps / (ev_q * 1e-3) / 1e9
+    gd = nb * steps / (ev_d * 1e-3) / 1e9
+    out["q4_0_codec"] = {"metric": "GGUF Q4_0 codec HBM GB/s (quantize + dequantize)",
+                         "value": round(2 * nb * steps / ((ev_q + ev_d) * 1e-3) / 1e9, 1), "unit": "GB/s",
+                         "quantize": {"GB/s": round(gq, 1), "us": round(ev_q * 1e3 / steps, 1), "frac": round(gq / HBM_PEAK_GBS, 4)},
+                         "dequantize": {"GB/s": round(gd, 1), "us": round(ev_d * 1e3 / steps, 1), "frac": round(gd / HBM_PEAK_GBS, 4)},
+                         "config": {"workload": "codec", "N": wl.N, "K": wl.K, "w_dtype": "bf16", "format": "Q4_0"}}
+    del blocks, d, w
+
+    # packed zero-points of a [28672, 256]-group table (pack + unpack)
+    zt = torch.randint(0, 16, (28672, 256), dtype=torch.uint8, device=dev)
+    zp = w4.pack_zeros(zt)
+    zu = torch.empty_like(zt)
+    ev_p, _ = time_graph(lambda i: w4.pack_zeros(zt, out=zp), 20, 200, 20, 1)
+    ev_u, _ = time_graph(lambda i: w4.unpack_zeros(zp, 256, out=zu), 20, 200, 20, 1)
+    zb = zt.numel() + zp.numel()
+    out["packed_zeros"] = {"metric": "zero-point pack / unpack HBM GB/s", "unit": "GB/s",
+                           "pack": {"GB/s": round(zb * 200 / (ev_p * 1e-3) / 1e9, 1), "us": round(ev_p * 1e3 / 200, 2)},
+                           "unpack": {"GB/s": round(zb * 200 / (ev_u * 1e-3) / 1e9, 1), "us": round(ev_u * 1e3 / 200, 2)},
+                           "config": {"N": 28672, "NG": 256}}
     return out
 
 

@@ -222,6 +222,41 @@ w4_status w4_lora_merge(const uint8_t* codes, const float* scales,
                         uint8_t* codes_out, float* scales_out, uint8_t* zeros_out,
                         void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * w4_pack_zeros / w4_unpack_zeros — zero-points in the compact 4-bit storage:
+ * packed uint8 [N, ceil(NG/2)], group 2j in the low nibble of byte j and
+ * group 2j+1 in the high nibble (the codes' nibble order, LoopQ
+ * packed_weight.py page; the keras dense.py diff page keeps one zero-point
+ * per group); an odd NG leaves the last high nibble 0.  The compute entry
+ * points take the unpacked form, uint8 [N, NG].
+ *   zeros    uint8 [N, NG], values 0..15 (only the low nibble is packed).
+ *   N, NG    >= 1.
+ *   packed   uint8 [N, ceil(NG/2)].
+ * No alignment requirement.
+ */
+w4_status w4_pack_zeros(const uint8_t* zeros, int64_t N, int64_t NG, uint8_t* packed, void* stream);
+w4_status w4_unpack_zeros(const uint8_t* packed, int64_t N, int64_t NG, uint8_t* zeros, void* stream);
+
+/*
+ * w4_q4_0_quantize / w4_q4_0_dequantize — the GGUF Q4_0 block format
+ * (Modular MAX quantization.py page: QuantizationEncoding Q4_0, 32 weights
+ * per block in 2 + 16 bytes, the scale d then the 4-bit codes).
+ *   Block layout: bytes 0..1 the fp16 scale d (little-endian); byte 2 + i
+ *   holds q[i] + 8 in its low nibble and q[i + 16] + 8 in its high nibble;
+ *   weight i of the block reads as fp32(q[i] - 8) * d.
+ *   Quantizer: d = fp16(fp32(max |w| / 7)) over the block (nearest, ties to
+ *   even), q = clamp(rint(fp32(w / d)), -7, 7) with d widened to fp32, all
+ *   codes 0 when d is 0 — the signed group rule of w4_quantize_pack taken
+ *   against the stored fp16 scale.  Weights must be finite with
+ *   max |w| / 7 within fp16 range (else the block is unspecified).
+ *   w        [N, K] fp32 (W4_F32) or bf16 (W4_BF16), 16-byte aligned.
+ *   N, K     N >= 1, K a positive multiple of 32.
+ *   blocks   uint8 [N, K/32, 18] (18 * N * K / 32 bytes), 16-byte aligned.
+ *   out      [N, K] fp32 or bf16 (RNE), 16-byte aligned.
+ */
+w4_status w4_q4_0_quantize(const void* w, int w_dtype, int64_t N, int64_t K, uint8_t* blocks, void* stream);
+w4_status w4_q4_0_dequantize(const uint8_t* blocks, int64_t N, int64_t K, void* out, int out_dtype, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -8,7 +8,8 @@ its ``workloads`` module) does not load the library.
 _EXPORTS = ("SYM", "ASYM", "W4Error", "library_path", "load", "quantize_pack",
             "dequantize", "linear", "linear_workspace_bytes", "linear_grad_input",
             "linear_grad_input_workspace_bytes", "lora_merge",
-            "lora_merge_workspace_bytes", "PER_CHANNEL", "n_groups")
+            "lora_merge_workspace_bytes", "PER_CHANNEL", "n_groups", "pack_zeros",
+            "unpack_zeros", "q4_0_quantize", "q4_0_dequantize")
 
 
 def __getattr__(name):

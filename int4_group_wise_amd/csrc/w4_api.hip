@@ -242,4 +242,51 @@ w4_status w4_lora_merge(const uint8_t* codes, const float* scales, const uint8_t
   return hip_status(w4::launch_lora_merge(a, static_cast<hipStream_t>(stream)), fn);
 }
 
+w4_status w4_pack_zeros(const uint8_t* zeros, int64_t N, int64_t NG, uint8_t* packed, void* stream) {
+  g_last_error.clear();
+  const char* fn = "w4_pack_zeros";
+  if (N < 1 || NG < 1) return fail(W4_ERR_INVALID_ARG, "%s: N and NG must be >= 1", fn);
+  if (N > kMaxDim || NG > kMaxDim) return fail(W4_ERR_UNSUPPORTED, "%s: N and NG must be <= 2^30", fn);
+  if (!zeros || !packed) return fail(W4_ERR_INVALID_ARG, "%s: zeros and packed must be non-NULL", fn);
+  return hip_status(w4::launch_pack_zeros(zeros, N, NG, packed, static_cast<hipStream_t>(stream)), fn);
+}
+
+w4_status w4_unpack_zeros(const uint8_t* packed, int64_t N, int64_t NG, uint8_t* zeros, void* stream) {
+  g_last_error.clear();
+  const char* fn = "w4_unpack_zeros";
+  if (N < 1 || NG < 1) return fail(W4_ERR_INVALID_ARG, "%s: N and NG must be >= 1", fn);
+  if (N > kMaxDim || NG > kMaxDim) return fail(W4_ERR_UNSUPPORTED, "%s: N and NG must be <= 2^30", fn);
+  if (!zeros || !packed) return fail(W4_ERR_INVALID_ARG, "%s: zeros and packed must be non-NULL", fn);
+  return hip_status(w4::launch_unpack_zeros(packed, N, NG, zeros, static_cast<hipStream_t>(stream)), fn);
+}
+
+namespace {
+w4_status check_q4_0(int64_t N, int64_t K, const void* a, const void* b, const char* fn) {
+  if (N < 1 || K < 32 || K % 32 != 0)
+    return fail(W4_ERR_INVALID_ARG, "%s: N must be >= 1 and K a positive multiple of 32 (got N=%lld K=%lld)", fn,
+                (long long)N, (long long)K);
+  if (N > kMaxDim || K > kMaxDim) return fail(W4_ERR_UNSUPPORTED, "%s: N and K must be <= 2^30", fn);
+  if (!a || !b) return fail(W4_ERR_INVALID_ARG, "%s: pointers must be non-NULL", fn);
+  if (!aligned16(a) || !aligned16(b)) return fail(W4_ERR_INVALID_ARG, "%s: tensors must be 16-byte aligned", fn);
+  if ((N * (K / 32) + 255) / 256 > kMaxGrid) return fail(W4_ERR_UNSUPPORTED, "%s: matrix too large for one launch", fn);
+  return W4_OK;
+}
+}  // namespace
+
+w4_status w4_q4_0_quantize(const void* w, int w_dtype, int64_t N, int64_t K, uint8_t* blocks, void* stream) {
+  g_last_error.clear();
+  const char* fn = "w4_q4_0_quantize";
+  if (w4_status st = check_q4_0(N, K, w, blocks, fn)) return st;
+  if (w_dtype != W4_F32 && w_dtype != W4_BF16) return fail(W4_ERR_INVALID_ARG, "%s: w_dtype must be W4_F32 or W4_BF16", fn);
+  return hip_status(w4::launch_q4_0_quantize(w, w_dtype == W4_BF16, N, K, blocks, static_cast<hipStream_t>(stream)), fn);
+}
+
+w4_status w4_q4_0_dequantize(const uint8_t* blocks, int64_t N, int64_t K, void* out, int out_dtype, void* stream) {
+  g_last_error.clear();
+  const char* fn = "w4_q4_0_dequantize";
+  if (w4_status st = check_q4_0(N, K, blocks, out, fn)) return st;
+  if (out_dtype != W4_F32 && out_dtype != W4_BF16) return fail(W4_ERR_INVALID_ARG, "%s: out_dtype must be W4_F32 or W4_BF16", fn);
+  return hip_status(w4::launch_q4_0_dequantize(blocks, N, K, out, out_dtype == W4_BF16, static_cast<hipStream_t>(stream)), fn);
+}
+
 }  // extern "C"

@@ -1,0 +1,240 @@
+// Storage formats next to the packed layout:
+//
+// GGUF Q4_0 blocks (Modular MAX quantization.py page: QuantizationEncoding,
+// Q4_0 = 32 weights per block in 2 + 16 bytes, the scale d then 4-bit codes).
+// A block is the fp16 scale d (little-endian) followed by 16 bytes; byte i
+// holds code q[i] + 8 in its low nibble and q[i + 16] + 8 in its high nibble
+// (the GGUF placement); a weight reads as (q - 8) * d.  Quantization is the
+// signed absmax rule of the packed format taken against the stored scale:
+// d = fp16(fp32(amax / 7)), q = clamp(rint(fp32(w / d)), -7, 7), all codes 0
+// when d is 0.
+//
+// The blocks of an [N, K] weight (K a multiple of 32) form one flat array:
+// block g covers weights 32 g .. 32 g + 31 and bytes 18 g .. 18 g + 17.  A
+// lane owns one block; a wave's 64 blocks are 1152 contiguous, 16-byte
+// aligned bytes, so the wave moves them through LDS and reads or writes them
+// as 72 coalesced 16-byte chunks.
+//
+// Packed zero-points: two per byte along the row, group 2j in the low nibble
+// (the codes' order), an odd group count leaving the last high nibble 0.
+
+#include "w4_device.h"
+#include "w4_internal.h"
+
+#include <algorithm>
+
+namespace w4 {
+namespace {
+
+constexpr int kFThreads = 256;
+constexpr int kQ4Block = 32;
+constexpr int kQ4Bytes = 18;
+constexpr int kQ4WaveBytes = kWave * kQ4Bytes;          // 1152 = 72 chunks of 16 bytes
+constexpr int kQ4WaveChunks = kQ4WaveBytes / 16;
+
+template <bool BF16>
+__global__ __launch_bounds__(kFThreads) void q4_0_quantize_kernel(const void* __restrict__ w, int64_t nblocks,
+                                                                   uint8_t* __restrict__ out) {
+  __shared__ __attribute__((aligned(16))) uint8_t stage[kFThreads / kWave][kQ4WaveBytes];
+  const int lane = lane_id();
+  const int wv = threadIdx.x >> 6;
+  const int64_t g0 = (static_cast<int64_t>(blockIdx.x) * kFThreads) + kWave * wv;   // the wave's first block
+  const int64_t g = g0 + lane;
+  const int64_t gc = min(g, nblocks - 1);
+
+  // the block's 32 weights (read once: non-temporal)
+  float v[kQ4Block];
+  if constexpr (BF16) {
+    const u32x4* src = reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(w) + gc * kQ4Block);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const u32x4 q = __builtin_nontemporal_load(src + c);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        v[8 * c + 2 * i] = __uint_as_float(q[i] << 16);
+        v[8 * c + 2 * i + 1] = __uint_as_float(q[i] & 0xFFFF0000u);
+      }
+    }
+  } else {
+    const u32x4* src = reinterpret_cast<const u32x4*>(static_cast<const float*>(w) + gc * kQ4Block);
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      const u32x4 q = __builtin_nontemporal_load(src + c);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) v[4 * c + i] = __uint_as_float(q[i]);
+    }
+  }
+
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < kQ4Block; ++i) amax = fmaxf(amax, fabsf(v[i]));
+  const _Float16 d16 = static_cast<_Float16>(amax / 7.0f);      // round to nearest even
+  const float d = static_cast<float>(d16);
+
+  // codes: rint(w / d) through the reciprocal with the exact redo near
+  // half-integers (|w / d| <= 10.5 even for subnormal d), clamped to [-7, 7]
+  float qf[kQ4Block];
+  if (d != 0.0f) {
+    bool redo = false;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) redo |= quant8_fast(&v[8 * c], d, &qf[8 * c]);
+    if (redo) {
+#pragma unroll
+      for (int c = 0; c < 4; ++c) quant8_redo(&v[8 * c], d, &qf[8 * c]);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < kQ4Block; ++i) qf[i] = 0.0f;
+  }
+  uint32_t word[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    uint32_t lo = 0, hi = 0;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      lo = __builtin_amdgcn_cvt_pk_u8_f32(fminf(fmaxf(qf[4 * k + t], -7.0f), 7.0f) + 8.0f, t, lo);
+      hi = __builtin_amdgcn_cvt_pk_u8_f32(fminf(fmaxf(qf[16 + 4 * k + t], -7.0f), 7.0f) + 8.0f, t, hi);
+    }
+    word[k] = lo | (hi << 4);
+  }
+
+  // the wave's blocks through LDS (2-byte granules: a block starts at an even
+  // offset), then 72 chunks of 16 bytes
+  const int64_t nvalid = min(static_cast<int64_t>(kWave), nblocks - g0);   // > 0
+  uint16_t* st = reinterpret_cast<uint16_t*>(stage[wv] + kQ4Bytes * lane);
+  if (g < nblocks) {
+    st[0] = __builtin_bit_cast(uint16_t, d16);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      st[1 + 2 * k] = static_cast<uint16_t>(word[k]);
+      st[2 + 2 * k] = static_cast<uint16_t>(word[k] >> 16);
+    }
+  }
+  __syncthreads();                      // every wave reaches this point
+  uint8_t* dst = out + g0 * kQ4Bytes;
+  if (nvalid == kWave) {
+    const u32x4* sv = reinterpret_cast<const u32x4*>(stage[wv]);
+    __builtin_nontemporal_store(sv[lane], reinterpret_cast<u32x4*>(dst) + lane);
+    if (lane < kQ4WaveChunks - kWave)
+      __builtin_nontemporal_store(sv[kWave + lane], reinterpret_cast<u32x4*>(dst) + kWave + lane);
+  } else {
+    const uint16_t* sv = reinterpret_cast<const uint16_t*>(stage[wv]);
+    uint16_t* d2 = reinterpret_cast<uint16_t*>(dst);
+    for (int i = lane; i < nvalid * (kQ4Bytes / 2); i += kWave) d2[i] = sv[i];
+  }
+}
+
+template <bool OUT_BF16>
+__global__ __launch_bounds__(kFThreads) void q4_0_dequantize_kernel(const uint8_t* __restrict__ blocks,
+                                                                     int64_t nblocks, void* __restrict__ out) {
+  __shared__ __attribute__((aligned(16))) uint8_t stage[kFThreads / kWave][kQ4WaveBytes];
+  const int lane = lane_id();
+  const int wv = threadIdx.x >> 6;
+  const int64_t g0 = (static_cast<int64_t>(blockIdx.x) * kFThreads) + kWave * wv;
+  const int64_t g = g0 + lane;
+  const int64_t nvalid = min(static_cast<int64_t>(kWave), nblocks - g0);
+  const uint8_t* src = blocks + g0 * kQ4Bytes;
+  if (nvalid == kWave) {
+    u32x4* sv = reinterpret_cast<u32x4*>(stage[wv]);
+    sv[lane] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src) + lane);
+    if (lane < kQ4WaveChunks - kWave)
+      sv[kWave + lane] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src) + kWave + lane);
+  } else {
+    uint16_t* sv = reinterpret_cast<uint16_t*>(stage[wv]);
+    const uint16_t* s2 = reinterpret_cast<const uint16_t*>(src);
+    for (int i = lane; i < nvalid * (kQ4Bytes / 2); i += kWave) sv[i] = s2[i];
+  }
+  __syncthreads();                      // every wave reaches this point
+  if (g >= nblocks) return;
+  const uint16_t* st = reinterpret_cast<const uint16_t*>(stage[wv] + kQ4Bytes * lane);
+  const float d = static_cast<float>(__builtin_bit_cast(_Float16, st[0]));
+  uint32_t word[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) word[k] = static_cast<uint32_t>(st[1 + 2 * k]) | (static_cast<uint32_t>(st[2 + 2 * k]) << 16);
+  float v[kQ4Block];
+#pragma unroll
+  for (int k = 0; k < 4; ++k)
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const uint32_t b = (word[k] >> (8 * t)) & 0xFFu;
+      v[4 * k + t] = static_cast<float>(static_cast<int>(b & 15u) - 8) * d;
+      v[16 + 4 * k + t] = static_cast<float>(static_cast<int>(b >> 4) - 8) * d;
+    }
+  if constexpr (OUT_BF16) {
+    u32x4* dst = reinterpret_cast<u32x4*>(static_cast<uint16_t*>(out) + g * kQ4Block);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      u32x4 q;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const bf16x2_t p = {static_cast<__bf16>(v[8 * c + 2 * i]), static_cast<__bf16>(v[8 * c + 2 * i + 1])};
+        q[i] = __builtin_bit_cast(uint32_t, p);
+      }
+      __builtin_nontemporal_store(q, dst + c);
+    }
+  } else {
+    f32x4_t* dst = reinterpret_cast<f32x4_t*>(static_cast<float*>(out) + g * kQ4Block);
+#pragma unroll
+    for (int c = 0; c < 8; ++c)
+      __builtin_nontemporal_store(f32x4_t{v[4 * c], v[4 * c + 1], v[4 * c + 2], v[4 * c + 3]}, dst + c);
+  }
+}
+
+// packed[n, j] = z[n, 2j] | z[n, 2j + 1] << 4  (0 past the last group)
+__global__ __launch_bounds__(kFThreads) void pack_zeros_kernel(const uint8_t* __restrict__ z, int64_t N, int64_t NG,
+                                                               uint8_t* __restrict__ packed) {
+  const int64_t NB = (NG + 1) / 2;
+  const int64_t total = N * NB;
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * kFThreads + threadIdx.x; i < total;
+       i += static_cast<int64_t>(gridDim.x) * kFThreads) {
+    const int64_t n = i / NB, j = i - n * NB;
+    const uint32_t lo = z[n * NG + 2 * j] & 15u;
+    const uint32_t hi = 2 * j + 1 < NG ? (z[n * NG + 2 * j + 1] & 15u) : 0u;
+    packed[i] = static_cast<uint8_t>(lo | (hi << 4));
+  }
+}
+
+__global__ __launch_bounds__(kFThreads) void unpack_zeros_kernel(const uint8_t* __restrict__ packed, int64_t N,
+                                                                 int64_t NG, uint8_t* __restrict__ z) {
+  const int64_t NB = (NG + 1) / 2;
+  const int64_t total = N * NG;
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * kFThreads + threadIdx.x; i < total;
+       i += static_cast<int64_t>(gridDim.x) * kFThreads) {
+    const int64_t n = i / NG, g = i - n * NG;
+    z[i] = static_cast<uint8_t>((packed[n * NB + g / 2] >> (4 * (g & 1))) & 15u);
+  }
+}
+
+uint32_t grid_for(int64_t total) {
+  return static_cast<uint32_t>(std::min<int64_t>((total + kFThreads - 1) / kFThreads, int64_t(1) << 20));
+}
+
+}  // namespace
+
+hipError_t launch_q4_0_quantize(const void* w, bool bf16, int64_t N, int64_t K, uint8_t* blocks, hipStream_t s) {
+  const int64_t nb = N * (K / kQ4Block);
+  const dim3 grid(static_cast<uint32_t>((nb + kFThreads - 1) / kFThreads));
+  if (bf16) q4_0_quantize_kernel<true><<<grid, dim3(kFThreads), 0, s>>>(w, nb, blocks);
+  else q4_0_quantize_kernel<false><<<grid, dim3(kFThreads), 0, s>>>(w, nb, blocks);
+  return hipGetLastError();
+}
+
+hipError_t launch_q4_0_dequantize(const uint8_t* blocks, int64_t N, int64_t K, void* out, bool bf16, hipStream_t s) {
+  const int64_t nb = N * (K / kQ4Block);
+  const dim3 grid(static_cast<uint32_t>((nb + kFThreads - 1) / kFThreads));
+  if (bf16) q4_0_dequantize_kernel<true><<<grid, dim3(kFThreads), 0, s>>>(blocks, nb, out);
+  else q4_0_dequantize_kernel<false><<<grid, dim3(kFThreads), 0, s>>>(blocks, nb, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_pack_zeros(const uint8_t* z, int64_t N, int64_t NG, uint8_t* packed, hipStream_t s) {
+  pack_zeros_kernel<<<dim3(grid_for(N * ((NG + 1) / 2))), dim3(kFThreads), 0, s>>>(z, N, NG, packed);
+  return hipGetLastError();
+}
+
+hipError_t launch_unpack_zeros(const uint8_t* packed, int64_t N, int64_t NG, uint8_t* z, hipStream_t s) {
+  unpack_zeros_kernel<<<dim3(grid_for(N * NG)), dim3(kFThreads), 0, s>>>(packed, N, NG, z);
+  return hipGetLastError();
+}
+
+}  // namespace w4

@@ -93,6 +93,13 @@ bool lora_fused(int64_t K, int64_t G, bool has_g_idx, int64_t r);
 size_t lora_workspace_bytes(int64_t N, int64_t K, int64_t G, bool has_g_idx, int64_t r);
 hipError_t launch_lora_merge(const LoraArgs& a, hipStream_t s);
 
+// Storage formats: GGUF Q4_0 blocks of an [N, K] weight (K % 32 == 0) and
+// packed zero-points [N, ceil(NG/2)].
+hipError_t launch_q4_0_quantize(const void* w, bool bf16, int64_t N, int64_t K, uint8_t* blocks, hipStream_t s);
+hipError_t launch_q4_0_dequantize(const uint8_t* blocks, int64_t N, int64_t K, void* out, bool bf16, hipStream_t s);
+hipError_t launch_pack_zeros(const uint8_t* z, int64_t N, int64_t NG, uint8_t* packed, hipStream_t s);
+hipError_t launch_unpack_zeros(const uint8_t* packed, int64_t N, int64_t NG, uint8_t* z, hipStream_t s);
+
 // Largest group count the quantizer's per-row LDS tables hold.
 constexpr int64_t kMaxGroupsPerRow = 4096;
 

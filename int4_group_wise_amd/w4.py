@@ -70,6 +70,14 @@ def load() -> ctypes.CDLL:
     lib.w4_lora_merge_workspace_bytes.argtypes = [I64, I64, I64, I32, I32, I64]
     lib.w4_lora_merge.restype = I32
     lib.w4_lora_merge.argtypes = [P, P, P, P, I64, I64, I64, I32, P, P, I64, ctypes.c_float, P, P, P, P, SZ, P]
+    lib.w4_pack_zeros.restype = I32
+    lib.w4_pack_zeros.argtypes = [P, I64, I64, P, P]
+    lib.w4_unpack_zeros.restype = I32
+    lib.w4_unpack_zeros.argtypes = [P, I64, I64, P, P]
+    lib.w4_q4_0_quantize.restype = I32
+    lib.w4_q4_0_quantize.argtypes = [P, I32, I64, I64, P, P]
+    lib.w4_q4_0_dequantize.restype = I32
+    lib.w4_q4_0_dequantize.argtypes = [P, I64, I64, P, I32, P]
     _LIB = lib
     return lib
 
@@ -277,3 +285,63 @@ def lora_merge(codes, scales, zeros, g_idx, K: int, G: int, mode, lora_a, lora_b
                                   _ptr(lora_a), _ptr(lora_b), r, float(lora_scale), _ptr(co), _ptr(so), _ptr(zo),
                                   _ptr(workspace), ws_bytes, _stream(codes.device)))
     return co, so, zo
+
+
+def pack_zeros(zeros: torch.Tensor, out=None) -> torch.Tensor:
+    """uint8 [N, NG] zero-points -> uint8 [N, ceil(NG/2)], two per byte."""
+    lib = load()
+    if zeros.dim() != 2:
+        raise ValueError("zeros must be a matrix")
+    _dev(zeros, "zeros", torch.uint8)
+    N, NG = zeros.shape
+    if out is None:
+        out = torch.empty((N, (NG + 1) // 2), dtype=torch.uint8, device=zeros.device)
+    _dev(out, "out", torch.uint8, (N, (NG + 1) // 2))
+    _check(lib, lib.w4_pack_zeros(_ptr(zeros), N, NG, _ptr(out), _stream(zeros.device)))
+    return out
+
+
+def unpack_zeros(packed: torch.Tensor, NG: int, out=None) -> torch.Tensor:
+    """uint8 [N, ceil(NG/2)] -> uint8 [N, NG]."""
+    lib = load()
+    _dev(packed, "packed", torch.uint8, (packed.shape[0], (NG + 1) // 2))
+    N = packed.shape[0]
+    if out is None:
+        out = torch.empty((N, NG), dtype=torch.uint8, device=packed.device)
+    _dev(out, "out", torch.uint8, (N, NG))
+    _check(lib, lib.w4_unpack_zeros(_ptr(packed), N, NG, _ptr(out), _stream(packed.device)))
+    return out
+
+
+def q4_0_quantize(w: torch.Tensor, out=None) -> torch.Tensor:
+    """GGUF Q4_0 blocks of ``w`` [N, K] (fp32 or bf16, K % 32 == 0):
+    uint8 [N, K/32, 18]."""
+    lib = load()
+    if w.dim() != 2 or w.dtype not in (torch.float32, torch.bfloat16):
+        raise ValueError("w must be a float32 or bfloat16 matrix")
+    _dev(w, "w", w.dtype)
+    N, K = w.shape
+    if K % 32:
+        raise ValueError("Q4_0 needs K to be a multiple of 32")
+    if out is None:
+        out = torch.empty((N, K // 32, 18), dtype=torch.uint8, device=w.device)
+    _dev(out, "out", torch.uint8, (N, K // 32, 18))
+    _check(lib, lib.w4_q4_0_quantize(_ptr(w), _BF16 if w.dtype == torch.bfloat16 else _F32, N, K, _ptr(out),
+                                     _stream(w.device)))
+    return out
+
+
+def q4_0_dequantize(blocks: torch.Tensor, out_dtype=torch.bfloat16, out=None) -> torch.Tensor:
+    """Dense [N, 32 * nb] weight from Q4_0 blocks uint8 [N, nb, 18]."""
+    lib = load()
+    if blocks.dim() != 3 or blocks.shape[2] != 18:
+        raise ValueError("blocks must be [N, K/32, 18]")
+    _dev(blocks, "blocks", torch.uint8)
+    N, nb = blocks.shape[0], blocks.shape[1]
+    K = 32 * nb
+    if out is None:
+        out = torch.empty((N, K), dtype=out_dtype, device=blocks.device)
+    _dev(out, "out", out_dtype, (N, K))
+    _check(lib, lib.w4_q4_0_dequantize(_ptr(blocks), N, K, _ptr(out),
+                                       _BF16 if out_dtype == torch.bfloat16 else _F32, _stream(blocks.device)))
+    return out

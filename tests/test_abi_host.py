@@ -31,6 +31,7 @@ def test_header_declares_the_entry_points():
     for f in ("w4_quantize_pack", "w4_dequantize", "w4_linear", "w4_linear_workspace_bytes",
               "w4_linear_grad_input", "w4_linear_grad_input_workspace_bytes",
               "w4_lora_merge", "w4_lora_merge_workspace_bytes",
+              "w4_pack_zeros", "w4_unpack_zeros", "w4_q4_0_quantize", "w4_q4_0_dequantize",
               "w4_abi_version", "w4_status_string", "w4_last_error"):
         assert f in names
 
@@ -155,6 +156,19 @@ def test_lora_merge_rejects_and_workspace(lib):
     assert lib.w4_lora_merge_workspace_bytes(4, 640, 40, 0, 0, 2) == 4 * 640 * 4
     assert lib.w4_lora_merge_workspace_bytes(4, 640, 64, 0, 0, 64) == 0
     assert call(g_idx=FAKE, wsb=4 * 16 * 4 - 1, ws=B2) == 1 and "workspace" in lib.w4_last_error().decode()
+
+
+def test_formats_reject(lib):
+    assert lib.w4_q4_0_quantize(FAKE, 0, 4, 48, FAKE, None) == 1 and "multiple of 32" in lib.w4_last_error().decode()
+    assert lib.w4_q4_0_quantize(FAKE, 0, 0, 64, FAKE, None) == 1
+    assert lib.w4_q4_0_quantize(FAKE, 5, 4, 64, FAKE, None) == 1 and "w_dtype" in lib.w4_last_error().decode()
+    assert lib.w4_q4_0_quantize(ODD, 0, 4, 64, FAKE, None) == 1 and "aligned" in lib.w4_last_error().decode()
+    assert lib.w4_q4_0_dequantize(FAKE, 4, 64, FAKE, 9, None) == 1 and "out_dtype" in lib.w4_last_error().decode()
+    assert lib.w4_q4_0_dequantize(None, 4, 64, FAKE, 1, None) == 1
+    assert lib.w4_q4_0_quantize(FAKE, 0, 4, (1 << 30) + 32, FAKE, None) == 2
+    assert lib.w4_pack_zeros(FAKE, 0, 4, FAKE, None) == 1
+    assert lib.w4_pack_zeros(None, 2, 4, FAKE, None) == 1
+    assert lib.w4_unpack_zeros(FAKE, 2, 0, FAKE, None) == 1
 
 
 def test_binding_validates_before_calling():

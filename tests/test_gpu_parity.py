@@ -475,3 +475,72 @@ def test_lora_merge_decode_layer_sampled():
     """The decode layer's weight (14336 x 4096, G = 128, zero-points), rank 16."""
     _check_lora(14336, 4096, 128, "asym", False, 16, 2.0, seed=7, rows=_sample_rows(14336, 128, 8),
                 label="decode-size")
+
+
+# ---------------------------------------------------------------------------
+# storage formats: GGUF Q4_0 blocks and packed zero-points, bit-exact
+# ---------------------------------------------------------------------------
+def _q4_weights(N, K, seed):
+    rng = np.random.default_rng(seed)
+    w = (rng.standard_normal((N, K)) * 0.02).astype(np.float32)
+    nb = K // 32
+    if N * nb >= 4:                      # a zero block, a subnormal-scale block, a tie of the stored scale
+        w[0, 0:32] = 0
+        w.reshape(-1, 32)[1] = 0
+        w.reshape(-1, 32)[1][0] = 10 * 2.0 ** -24
+        w.reshape(-1, 32)[2][0] = 1.0
+        w.reshape(-1, 32)[2][1] = 3.5 * (1170 / 1024 / 8)
+    return w
+
+
+@pytest.mark.parametrize("N,K,wdt", [(1, 32, "f32"), (3, 64, "bf16"), (37, 96, "bf16"), (100, 4096, "f32"),
+                                     (65, 32, "f32"), (7, 8192, "bf16")])
+def test_q4_0_codec(N, K, wdt):
+    w = torch.from_numpy(_q4_weights(N, K, seed=N + K))
+    if wdt == "bf16":
+        w = w.to(torch.bfloat16)
+    blocks = w4.q4_0_quantize(w.to(DEV))
+    torch.cuda.synchronize()
+    ref = O.q4_0_quantize(_np_w(w))
+    assert np.array_equal(blocks.cpu().numpy(), ref), f"Q4_0 blocks differ N{N} K{K} {wdt}"
+    for dt, kind in ((torch.bfloat16, "bf16"), (torch.float32, "f32")):
+        got = w4.q4_0_dequantize(blocks, dt).cpu()
+        exp = O.q4_0_dequantize(ref, kind)
+        if kind == "bf16":
+            assert np.array_equal(_bits(got), exp), f"Q4_0 bf16 decode differs N{N} K{K}"
+        else:
+            assert np.array_equal(got.numpy().view(np.uint32), exp.view(np.uint32)), f"Q4_0 f32 decode differs N{N} K{K}"
+
+
+def test_q4_0_decodes_arbitrary_blocks():
+    """Every nibble pattern and finite fp16 scales, including subnormal ones."""
+    rng = np.random.default_rng(50)
+    N, nb = 40, 70
+    blk = rng.integers(0, 256, size=(N, nb, 18), dtype=np.uint8)
+    d = rng.standard_normal((N, nb)).astype(np.float16) * np.float16(0.01)
+    d[0, :8] = np.float16(2.0 ** -24) * np.arange(1, 9, dtype=np.float16)
+    blk[..., 0:2] = d.astype("<f2").view(np.uint8).reshape(N, nb, 2)
+    got = w4.q4_0_dequantize(torch.from_numpy(blk).to(DEV), torch.float32).cpu().numpy()
+    assert np.array_equal(got.view(np.uint32), O.q4_0_dequantize(blk, "f32").view(np.uint32))
+
+
+def test_q4_0_full_size_sampled():
+    """The codec weight's shape at K = 8192 (bf16 [28672, 8192]), sampled rows."""
+    wl = workload("codec", K=8192)
+    t = generate(wl)
+    w = t["w"]
+    blocks = w4.q4_0_quantize(w.to(DEV))
+    torch.cuda.synchronize()
+    rows = _sample_rows(wl.N, 256, 9)
+    ref = O.q4_0_quantize(_np_w(w[torch.from_numpy(rows)]))
+    assert np.array_equal(blocks[torch.from_numpy(rows).to(DEV)].cpu().numpy(), ref)
+
+
+@pytest.mark.parametrize("N,NG", [(1, 1), (5, 7), (300, 32), (1000, 257)])
+def test_packed_zeros_round_trip(N, NG):
+    rng = np.random.default_rng(N + NG)
+    z = rng.integers(0, 16, size=(N, NG), dtype=np.uint8)
+    p = w4.pack_zeros(torch.from_numpy(z).to(DEV))
+    assert np.array_equal(p.cpu().numpy(), O.pack_zeros(z))
+    u = w4.unpack_zeros(p, NG)
+    assert np.array_equal(u.cpu().numpy(), z)
