@@ -268,7 +268,7 @@ w4_status check_q4_0(int64_t N, int64_t K, const void* a, const void* b, const c
   if (N > kMaxDim || K > kMaxDim) return fail(W4_ERR_UNSUPPORTED, "%s: N and K must be <= 2^30", fn);
   if (!a || !b) return fail(W4_ERR_INVALID_ARG, "%s: pointers must be non-NULL", fn);
   if (!aligned16(a) || !aligned16(b)) return fail(W4_ERR_INVALID_ARG, "%s: tensors must be 16-byte aligned", fn);
-  if ((N * (K / 32) + 255) / 256 > kMaxGrid) return fail(W4_ERR_UNSUPPORTED, "%s: matrix too large for one launch", fn);
+  if ((N * (K / 32) + 31) / 32 > kMaxGrid) return fail(W4_ERR_UNSUPPORTED, "%s: matrix too large for one launch", fn);
   return W4_OK;
 }
 }  // namespace

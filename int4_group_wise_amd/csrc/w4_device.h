@@ -11,6 +11,7 @@ constexpr int kWave = 64;
 // Plain vector types (HIP's uint4 is a union-based struct whose copies can
 // defeat register promotion; these stay in registers).
 typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
+typedef __attribute__((ext_vector_type(2))) uint32_t u32x2;
 typedef __attribute__((ext_vector_type(4))) float f32x4_t;
 typedef __attribute__((ext_vector_type(16))) float f32x16_t;
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;

@@ -124,59 +124,60 @@ __global__ __launch_bounds__(kFThreads) void q4_0_quantize_kernel(const void* __
   }
 }
 
+// Dequantize: a lane decodes WPL consecutive weights of one block (8 for bf16,
+// 4 for fp32 output: 16 bytes), so the wave's stores are one contiguous run.
+// A wave covers 64 / (32 / WPL) blocks; their bytes (288 or 144, 16-byte
+// aligned) come in through LDS.
 template <bool OUT_BF16>
 __global__ __launch_bounds__(kFThreads) void q4_0_dequantize_kernel(const uint8_t* __restrict__ blocks,
                                                                      int64_t nblocks, void* __restrict__ out) {
-  __shared__ __attribute__((aligned(16))) uint8_t stage[kFThreads / kWave][kQ4WaveBytes];
+  constexpr int kWPL = OUT_BF16 ? 8 : 4;                 // weights per lane
+  constexpr int kLPB = kQ4Block / kWPL;                  // lanes per block
+  constexpr int kBPW = kWave / kLPB;                     // blocks per wave
+  constexpr int kChunks = kBPW * kQ4Bytes / 16;          // 18 or 9
+  __shared__ __attribute__((aligned(16))) uint8_t stage[kFThreads / kWave][kBPW * kQ4Bytes];
   const int lane = lane_id();
   const int wv = threadIdx.x >> 6;
-  const int64_t g0 = (static_cast<int64_t>(blockIdx.x) * kFThreads) + kWave * wv;
-  const int64_t g = g0 + lane;
-  const int64_t nvalid = min(static_cast<int64_t>(kWave), nblocks - g0);
+  const int64_t g0 = (static_cast<int64_t>(blockIdx.x) * (kFThreads / kWave) + wv) * kBPW;   // the wave's first block
+  const int64_t nvalid = min(static_cast<int64_t>(kBPW), nblocks - g0);
   const uint8_t* src = blocks + g0 * kQ4Bytes;
-  if (nvalid == kWave) {
-    u32x4* sv = reinterpret_cast<u32x4*>(stage[wv]);
-    sv[lane] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src) + lane);
-    if (lane < kQ4WaveChunks - kWave)
-      sv[kWave + lane] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src) + kWave + lane);
+  if (nvalid == kBPW) {
+    if (lane < kChunks)
+      reinterpret_cast<u32x4*>(stage[wv])[lane] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src) + lane);
   } else {
     uint16_t* sv = reinterpret_cast<uint16_t*>(stage[wv]);
     const uint16_t* s2 = reinterpret_cast<const uint16_t*>(src);
     for (int i = lane; i < nvalid * (kQ4Bytes / 2); i += kWave) sv[i] = s2[i];
   }
   __syncthreads();                      // every wave reaches this point
-  if (g >= nblocks) return;
-  const uint16_t* st = reinterpret_cast<const uint16_t*>(stage[wv] + kQ4Bytes * lane);
+  const int bl = lane / kLPB;           // block of the wave
+  const int i0 = kWPL * (lane % kLPB);  // first weight of the lane in its block
+  if (bl >= nvalid) return;
+  const uint16_t* st = reinterpret_cast<const uint16_t*>(stage[wv] + kQ4Bytes * bl);
   const float d = static_cast<float>(__builtin_bit_cast(_Float16, st[0]));
-  uint32_t word[4];
+  // code bytes (i0 mod 16) .. + WPL - 1 of the block: low nibbles for the
+  // first 16 weights, high nibbles for the last 16
+  const int b0 = i0 & 15;
+  const int sh = i0 < 16 ? 0 : 4;
+  float v[kWPL];
 #pragma unroll
-  for (int k = 0; k < 4; ++k) word[k] = static_cast<uint32_t>(st[1 + 2 * k]) | (static_cast<uint32_t>(st[2 + 2 * k]) << 16);
-  float v[kQ4Block];
-#pragma unroll
-  for (int k = 0; k < 4; ++k)
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      const uint32_t b = (word[k] >> (8 * t)) & 0xFFu;
-      v[4 * k + t] = static_cast<float>(static_cast<int>(b & 15u) - 8) * d;
-      v[16 + 4 * k + t] = static_cast<float>(static_cast<int>(b >> 4) - 8) * d;
-    }
+  for (int h = 0; h < kWPL / 2; ++h) {
+    const uint32_t two = st[1 + (b0 >> 1) + h];        // bytes b0 + 2h, b0 + 2h + 1 (b0 is even)
+    v[2 * h] = static_cast<float>(static_cast<int>((two >> sh) & 15u) - 8) * d;
+    v[2 * h + 1] = static_cast<float>(static_cast<int>((two >> (8 + sh)) & 15u) - 8) * d;
+  }
+  const int64_t g = g0 + bl;
   if constexpr (OUT_BF16) {
-    u32x4* dst = reinterpret_cast<u32x4*>(static_cast<uint16_t*>(out) + g * kQ4Block);
+    u32x4 q;
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      u32x4 q;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const bf16x2_t p = {static_cast<__bf16>(v[8 * c + 2 * i]), static_cast<__bf16>(v[8 * c + 2 * i + 1])};
-        q[i] = __builtin_bit_cast(uint32_t, p);
-      }
-      __builtin_nontemporal_store(q, dst + c);
+    for (int i = 0; i < 4; ++i) {
+      const bf16x2_t p = {static_cast<__bf16>(v[2 * i]), static_cast<__bf16>(v[2 * i + 1])};
+      q[i] = __builtin_bit_cast(uint32_t, p);
     }
+    __builtin_nontemporal_store(q, reinterpret_cast<u32x4*>(static_cast<uint16_t*>(out) + g * kQ4Block + i0));
   } else {
-    f32x4_t* dst = reinterpret_cast<f32x4_t*>(static_cast<float*>(out) + g * kQ4Block);
-#pragma unroll
-    for (int c = 0; c < 8; ++c)
-      __builtin_nontemporal_store(f32x4_t{v[4 * c], v[4 * c + 1], v[4 * c + 2], v[4 * c + 3]}, dst + c);
+    __builtin_nontemporal_store(f32x4_t{v[0], v[1], v[2], v[3]},
+                                reinterpret_cast<f32x4_t*>(static_cast<float*>(out) + g * kQ4Block + i0));
   }
 }
 
@@ -205,6 +206,59 @@ __global__ __launch_bounds__(kFThreads) void unpack_zeros_kernel(const uint8_t* 
   }
 }
 
+// Even NG: rows pack to whole bytes, so the tables are flat arrays with
+// packed[i] = z[2i] | z[2i+1] << 4; a thread takes 16 zero-points (one
+// 16-byte load, one 8-byte store) and the last partial piece goes bytewise.
+__global__ __launch_bounds__(kFThreads) void pack_zeros_flat_kernel(const uint8_t* __restrict__ z, int64_t nout,
+                                                                    uint8_t* __restrict__ packed) {
+  const int64_t full = nout / 8;
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * kFThreads + threadIdx.x; i <= full;
+       i += static_cast<int64_t>(gridDim.x) * kFThreads) {
+    if (i < full) {
+      const u32x4 q = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(z) + i);
+      uint32_t o[2];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const uint32_t a = q[2 * h] & 0x0F0F0F0Fu, b = q[2 * h + 1] & 0x0F0F0F0Fu;
+        // bytes (a0 a1 a2 a3) -> nibble pairs a0|a1<<4, a2|a3<<4 in the low half, b likewise in the high half
+        const uint32_t pa = (a | (a >> 4)) & 0x00FF00FFu;      // a0|a1<<4 at byte 0, a2|a3<<4 at byte 2
+        const uint32_t pb = (b | (b >> 4)) & 0x00FF00FFu;
+        o[h] = (pa & 0xFFu) | ((pa >> 8) & 0xFF00u) | ((pb & 0xFFu) << 16) | ((pb >> 8) & 0xFF00u) << 16;
+      }
+      *reinterpret_cast<u32x2*>(packed + 8 * i) = u32x2{o[0], o[1]};
+    } else {
+      for (int64_t j = 8 * full; j < nout; ++j) packed[j] = static_cast<uint8_t>((z[2 * j] & 15u) | ((z[2 * j + 1] & 15u) << 4));
+    }
+  }
+}
+
+__global__ __launch_bounds__(kFThreads) void unpack_zeros_flat_kernel(const uint8_t* __restrict__ packed, int64_t nin,
+                                                                      uint8_t* __restrict__ z) {
+  const int64_t full = nin / 8;
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * kFThreads + threadIdx.x; i <= full;
+       i += static_cast<int64_t>(gridDim.x) * kFThreads) {
+    if (i < full) {
+      const u32x2 p = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(packed) + i);
+      u32x4 q;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const uint32_t w = p[h];
+        // byte k of w -> bytes 2k (low nibble) and 2k+1 (high nibble)
+        const uint32_t lo = (w & 0xFFu) | ((w & 0xFF00u) << 8);            // bytes 0, 1 of w at 0 and 2
+        const uint32_t hi = ((w >> 16) & 0xFFu) | ((w >> 8) & 0xFF0000u);  // bytes 2, 3 of w at 0 and 2
+        q[2 * h] = (lo & 0x000F000Fu) | ((lo & 0x00F000F0u) << 4);
+        q[2 * h + 1] = (hi & 0x000F000Fu) | ((hi & 0x00F000F0u) << 4);
+      }
+      __builtin_nontemporal_store(q, reinterpret_cast<u32x4*>(z) + i);
+    } else {
+      for (int64_t j = 8 * full; j < nin; ++j) {
+        z[2 * j] = packed[j] & 15u;
+        z[2 * j + 1] = packed[j] >> 4;
+      }
+    }
+  }
+}
+
 uint32_t grid_for(int64_t total) {
   return static_cast<uint32_t>(std::min<int64_t>((total + kFThreads - 1) / kFThreads, int64_t(1) << 20));
 }
@@ -221,18 +275,31 @@ hipError_t launch_q4_0_quantize(const void* w, bool bf16, int64_t N, int64_t K, 
 
 hipError_t launch_q4_0_dequantize(const uint8_t* blocks, int64_t N, int64_t K, void* out, bool bf16, hipStream_t s) {
   const int64_t nb = N * (K / kQ4Block);
-  const dim3 grid(static_cast<uint32_t>((nb + kFThreads - 1) / kFThreads));
+  const int64_t per_wg = (kFThreads / kWave) * (bf16 ? 16 : 8);     // blocks per workgroup
+  const dim3 grid(static_cast<uint32_t>((nb + per_wg - 1) / per_wg));
   if (bf16) q4_0_dequantize_kernel<true><<<grid, dim3(kFThreads), 0, s>>>(blocks, nb, out);
   else q4_0_dequantize_kernel<false><<<grid, dim3(kFThreads), 0, s>>>(blocks, nb, out);
   return hipGetLastError();
 }
 
+bool aligned_to(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
 hipError_t launch_pack_zeros(const uint8_t* z, int64_t N, int64_t NG, uint8_t* packed, hipStream_t s) {
+  if (NG % 2 == 0 && aligned_to(z, 16) && aligned_to(packed, 8)) {
+    const int64_t nout = N * NG / 2;
+    pack_zeros_flat_kernel<<<dim3(grid_for(nout / 8 + 1)), dim3(kFThreads), 0, s>>>(z, nout, packed);
+    return hipGetLastError();
+  }
   pack_zeros_kernel<<<dim3(grid_for(N * ((NG + 1) / 2))), dim3(kFThreads), 0, s>>>(z, N, NG, packed);
   return hipGetLastError();
 }
 
 hipError_t launch_unpack_zeros(const uint8_t* packed, int64_t N, int64_t NG, uint8_t* z, hipStream_t s) {
+  if (NG % 2 == 0 && aligned_to(z, 16) && aligned_to(packed, 8)) {
+    const int64_t nin = N * NG / 2;
+    unpack_zeros_flat_kernel<<<dim3(grid_for(nin / 8 + 1)), dim3(kFThreads), 0, s>>>(packed, nin, z);
+    return hipGetLastError();
+  }
   unpack_zeros_kernel<<<dim3(grid_for(N * NG)), dim3(kFThreads), 0, s>>>(packed, N, NG, z);
   return hipGetLastError();
 }

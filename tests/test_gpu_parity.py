@@ -536,7 +536,7 @@ def test_q4_0_full_size_sampled():
     assert np.array_equal(blocks[torch.from_numpy(rows).to(DEV)].cpu().numpy(), ref)
 
 
-@pytest.mark.parametrize("N,NG", [(1, 1), (5, 7), (300, 32), (1000, 257)])
+@pytest.mark.parametrize("N,NG", [(1, 1), (5, 7), (300, 32), (1000, 257), (3, 6), (7, 22), (28672, 256)])
 def test_packed_zeros_round_trip(N, NG):
     rng = np.random.default_rng(N + NG)
     z = rng.integers(0, 16, size=(N, NG), dtype=np.uint8)
