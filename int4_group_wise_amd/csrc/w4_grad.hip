@@ -27,7 +27,10 @@ namespace {
 
 constexpr int kGThreads = 256;
 constexpr int kGWaves = kGThreads / kWave;
-constexpr int kGUnroll = 8;               // rows of a wave whose loads are issued together
+// rows of a wave whose loads are issued together: 16 for contiguous groups
+// when a lane's accumulators are few (MT * CPT <= 32), else 8
+template <int MT, int CPT, bool GIDX>
+constexpr int grad_unroll() { return !GIDX && MT * CPT <= 32 ? 16 : 8; }
 
 // Columns per lane: 32 (one 16-byte code load per row) for contiguous groups
 // of a multiple of 32 columns and at most 4 dy rows, else 8 (one dword).
@@ -64,11 +67,15 @@ __global__ __launch_bounds__(kGThreads) void grad_split_kernel(GradArgs a, int r
   const bool aligned = cnt == CPT && (KB & 3) == 0;
 
   float acc[MT][CPT];
+  float corr[MT];                                     // sum over rows of c z (contiguous groups)
 #pragma unroll
-  for (int m = 0; m < MT; ++m)
+  for (int m = 0; m < MT; ++m) {
+    corr[m] = 0.0f;
 #pragma unroll
     for (int e = 0; e < CPT; ++e) acc[m][e] = 0.0f;
+  }
 
+  constexpr int kGUnroll = grad_unroll<MT, CPT, GIDX>();
   for (int64_t n0 = nb + w; n0 < ne; n0 += kGUnroll * kGWaves) {
     uint32_t d[kGUnroll][kW];
     float s[kGUnroll][kNGrp];
@@ -87,9 +94,12 @@ __global__ __launch_bounds__(kGThreads) void grad_split_kernel(GradArgs a, int r
           d[u][0] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(crow));
         }
       } else {
+        const int nbytes = (cnt + 1) / 2;
 #pragma unroll
         for (int i = 0; i < kW; ++i) d[u][i] = 0;
-        for (int b = 0; b < (cnt + 1) / 2; ++b) d[u][b >> 2] |= static_cast<uint32_t>(crow[b]) << (8 * (b & 3));
+#pragma unroll
+        for (int b = 0; b < 4 * kW; ++b)       // static indices: the words stay in registers
+          if (b < nbytes) d[u][b >> 2] |= static_cast<uint32_t>(crow[b]) << (8 * (b & 3));
       }
 #pragma unroll
       for (int e = 0; e < kNGrp; ++e) {
@@ -99,26 +109,59 @@ __global__ __launch_bounds__(kGThreads) void grad_split_kernel(GradArgs a, int r
     }
 #pragma unroll
     for (int u = 0; u < kGUnroll; ++u) {
+      // rows past the slice (their loads repeated the last row) and rows
+      // m >= M (reading row M - 1) add nothing: their dy factor is 0
       const int64_t n = n0 + u * kGWaves;
-      if (n >= ne) break;
+      const bool valid = n < ne;
       float dm[MT];
 #pragma unroll
-      for (int m = 0; m < MT; ++m) {   // rows m >= M read row M - 1 and add nothing
-        const float dv = bf16_to_f32(a.dy[static_cast<int64_t>(min(m, M - 1)) * a.N + n]);
-        dm[m] = m < M ? dv : 0.0f;
+      for (int m = 0; m < MT; ++m) {
+        const float dv = bf16_to_f32(a.dy[static_cast<int64_t>(min(m, M - 1)) * a.N + min(n, ne - 1)]);
+        dm[m] = valid && m < M ? dv : 0.0f;
       }
+      if constexpr (GIDX) {
 #pragma unroll
-      for (int i = 0; i < kW; ++i) {
-        const uint32_t dd = ASYM ? d[u][i] : (d[u][i] ^ 0x88888888u);   // signed q -> q + 8
+        for (int i = 0; i < kW; ++i) {
+          const uint32_t dd = ASYM ? d[u][i] : (d[u][i] ^ 0x88888888u);   // signed q -> q + 8
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int ge = GIDX ? e : 0;
-          const float wv = (static_cast<float>((dd >> (4 * e)) & 15u) - z[u][ge]) * s[u][ge];
+          for (int e = 0; e < 8; ++e) {
+            const float wv = (static_cast<float>((dd >> (4 * e)) & 15u) - z[u][e]) * s[u][e];
 #pragma unroll
-          for (int m = 0; m < MT; ++m) acc[m][8 * i + e] = __builtin_fmaf(dm[m], wv, acc[m][8 * i + e]);
+            for (int m = 0; m < MT; ++m) acc[m][8 * i + e] = __builtin_fmaf(dm[m], wv, acc[m][8 * i + e]);
+          }
+        }
+      } else {
+        // one group for the lane's columns: sum c u with c = dy s per row and
+        // take sum c z off at the end; the nibbles go to float as unpacked bytes
+        float cm[MT];
+#pragma unroll
+        for (int m = 0; m < MT; ++m) {
+          cm[m] = dm[m] * s[u][0];
+          corr[m] = __builtin_fmaf(cm[m], z[u][0], corr[m]);
+        }
+#pragma unroll
+        for (int i = 0; i < kW; ++i) {
+          const uint32_t dd = ASYM ? d[u][i] : (d[u][i] ^ 0x88888888u);   // signed q -> q + 8
+          const uint32_t lo = dd & 0x0F0F0F0Fu, hi = (dd >> 4) & 0x0F0F0F0Fu;
+#pragma unroll
+          for (int b = 0; b < 4; ++b) {
+            const float qe = static_cast<float>((lo >> (8 * b)) & 0xFFu);     // column 8i + 2b
+            const float qo = static_cast<float>((hi >> (8 * b)) & 0xFFu);     // column 8i + 2b + 1
+#pragma unroll
+            for (int m = 0; m < MT; ++m) {
+              acc[m][8 * i + 2 * b] = __builtin_fmaf(cm[m], qe, acc[m][8 * i + 2 * b]);
+              acc[m][8 * i + 2 * b + 1] = __builtin_fmaf(cm[m], qo, acc[m][8 * i + 2 * b + 1]);
+            }
+          }
         }
       }
     }
+  }
+  if constexpr (!GIDX) {
+#pragma unroll
+    for (int m = 0; m < MT; ++m)
+#pragma unroll
+      for (int e = 0; e < CPT; ++e) acc[m][e] -= corr[m];
   }
 
   // add the 4 waves' sums (waves 1..3 in turn through one buffer: register
