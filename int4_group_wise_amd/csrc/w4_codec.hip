@@ -145,12 +145,10 @@ __device__ __forceinline__ void store_code_word(uint8_t* __restrict__ codes, int
 // 8 weights in registers between the statistics pass and the packing pass
 // (rows up to 2048 * CH columns).  CH == 0: longer rows, reloaded for packing.
 template <bool BF16, bool ASYM, bool GIDX, int CH>
-__global__ __launch_bounds__(kQThreads) void quantize_pack_kernel(QuantArgs a) {
-  extern __shared__ uint32_t lds[];
+__device__ __forceinline__ void quantize_row_generic(const QuantArgs& a, int64_t n, uint32_t* lds) {
   const int NG = static_cast<int>(a.NG);
   const int K = static_cast<int>(a.K);
   const int G = static_cast<int>(a.G);
-  const int64_t n = blockIdx.x;
   uint32_t* hi = lds;
   uint32_t* nlo = lds + NG;
   float* sc = reinterpret_cast<float*>(lds + 2 * NG);
@@ -223,6 +221,12 @@ __global__ __launch_bounds__(kQThreads) void quantize_pack_kernel(QuantArgs a) {
       store_code_word(a.codes, n * KB + 4 * j, min(4, static_cast<int>(KB) - 4 * j), p);
     }
   }
+}
+
+template <bool BF16, bool ASYM, bool GIDX, int CH>
+__global__ __launch_bounds__(kQThreads) void quantize_pack_kernel(QuantArgs a) {
+  extern __shared__ uint32_t lds[];
+  quantize_row_generic<BF16, ASYM, GIDX, CH>(a, blockIdx.x, lds);
 }
 
 // Largest row table (scales + zero-points) the act-order dequantizer stages
@@ -478,6 +482,157 @@ hipError_t launch_qrows(const QuantArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------
+// Act-order quantizer for a g_idx whose groups all hold exactly G columns (G a
+// power of two in [8, 512], K <= 8192): a workgroup sorts the columns by group
+// once (counting sort of g_idx in LDS), then for each of its kActQRows rows
+// stages the row in LDS as fp32 and reads it in group order, so that a group
+// is G / 8 consecutive lanes of eight columns and the lane-reduction
+// quantizer applies; the codes return to column order through an LDS byte
+// table and are packed and written coalesced.  The order of the columns
+// within a group does not matter (the statistics are maxima, the codes are
+// per column), so the results are deterministic.  If the groups turn out not
+// to be uniform, the workgroup quantizes its rows with the general per-row
+// algorithm instead (every workgroup sees the same g_idx).
+// ---------------------------------------------------------------------------
+constexpr int kActQRows = 4;   // rows per workgroup (measured best of 1, 2, 4, 8, 16)
+constexpr int kActQMaxK = 8192;
+
+__host__ __device__ inline size_t act_q_lds(int64_t K, int64_t NG) {
+  const size_t fast = ((4 * NG + 15) & ~15) + ((2 * K + 15) & ~15) + 4 * K + ((K + 15) & ~15);
+  const size_t slow = static_cast<size_t>(NG) * 4 * sizeof(uint32_t);
+  return fast > slow ? fast : slow;
+}
+
+template <bool BF16, bool ASYM>
+__global__ __launch_bounds__(kQThreads) void quantize_act_kernel(QuantArgs a) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t qsm[];
+  __shared__ int uniform;
+  const int K = static_cast<int>(a.K);
+  const int NG = static_cast<int>(a.NG);
+  const int G = static_cast<int>(a.G);
+  const int lpg = G / 8;
+  const int lane = lane_id();
+  int* cnt = reinterpret_cast<int*>(qsm);                                       // [NG]
+  uint16_t* perm = reinterpret_cast<uint16_t*>(qsm + ((4 * NG + 15) & ~15));    // [K] column of sorted position
+  float* rowv = reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(perm) + ((2 * K + 15) & ~15));  // [K]
+  uint8_t* cbt = reinterpret_cast<uint8_t*>(rowv + K);                          // [K] code of column
+
+  // group sizes; uniform iff every group holds exactly G columns
+  for (int g = threadIdx.x; g < NG; g += kQThreads) cnt[g] = 0;
+  if (threadIdx.x == 0) uniform = 1;
+  __syncthreads();
+  for (int k = threadIdx.x; k < K; k += kQThreads) atomicAdd(&cnt[gid_at(a.g_idx, k, NG)], 1);
+  __syncthreads();
+  for (int g = threadIdx.x; g < NG; g += kQThreads)
+    if (cnt[g] != G) uniform = 0;
+  __syncthreads();
+  const int64_t nb = static_cast<int64_t>(blockIdx.x) * kActQRows;
+  if (!uniform) {
+    for (int r = 0; r < kActQRows; ++r) {
+      if (nb + r >= a.N) break;                    // uniform
+      __syncthreads();                             // the previous row is done with the tables
+      quantize_row_generic<BF16, ASYM, true, kActQMaxK / 8 / kQThreads>(a, nb + r, reinterpret_cast<uint32_t*>(qsm));
+    }
+    return;
+  }
+  // sorted positions: group g holds positions g G .. g G + G - 1
+  for (int g = threadIdx.x; g < NG; g += kQThreads) cnt[g] = g * G;
+  __syncthreads();
+  for (int k = threadIdx.x; k < K; k += kQThreads) perm[atomicAdd(&cnt[gid_at(a.g_idx, k, NG)], 1)] = static_cast<uint16_t>(k);
+
+  constexpr int kEs = BF16 ? 2 : 4;
+  constexpr int kSegMax = kActQMaxK * kEs / 16 / kQThreads;   // 16-byte row segments per thread
+  constexpr int kChMax = kActQMaxK / 8 / kQThreads;           // 8-column chunks per thread
+  const int nseg = K * kEs / 16;
+  const int nch = K / 8;
+  const int64_t KB = a.K / 2;
+  // rows are software-pipelined: the next row's loads are in flight while
+  // the current row is quantized and packed (read once: non-temporal)
+  u32x4 seg[kSegMax];
+  auto load_row = [&](int64_t n) {
+    const u32x4* src = reinterpret_cast<const u32x4*>(static_cast<const uint8_t*>(a.w) + n * a.K * kEs);
+#pragma unroll
+    for (int i = 0; i < kSegMax; ++i) {
+      const int sg = threadIdx.x + kQThreads * i;
+      if (sg < nseg) seg[i] = __builtin_nontemporal_load(src + sg);
+    }
+  };
+  if (nb < a.N) load_row(nb);
+  for (int r = 0; r < kActQRows; ++r) {
+    const int64_t n = nb + r;
+    if (n >= a.N) break;                           // uniform
+    // the row into LDS as fp32 (the previous row's reads of it are done:
+    // barrier after its quantization)
+#pragma unroll
+    for (int i = 0; i < kSegMax; ++i) {
+      const int sg = threadIdx.x + kQThreads * i;
+      if (sg < nseg) {
+        if constexpr (BF16) {
+          f32x4_t lo, hi;
+#pragma unroll
+          for (int j = 0; j < 2; ++j) {
+            lo[2 * j] = __uint_as_float(seg[i][j] << 16);
+            lo[2 * j + 1] = __uint_as_float(seg[i][j] & 0xFFFF0000u);
+            hi[2 * j] = __uint_as_float(seg[i][2 + j] << 16);
+            hi[2 * j + 1] = __uint_as_float(seg[i][2 + j] & 0xFFFF0000u);
+          }
+          reinterpret_cast<f32x4_t*>(rowv)[2 * sg] = lo;
+          reinterpret_cast<f32x4_t*>(rowv)[2 * sg + 1] = hi;
+        } else {
+          reinterpret_cast<u32x4*>(rowv)[sg] = seg[i];
+        }
+      }
+    }
+    __syncthreads();                               // row staged (and, for the first row, perm built)
+    if (r + 1 < kActQRows && n + 1 < a.N) load_row(n + 1);
+    // quantize in group order: chunk c = sorted positions 8c .. 8c + 7, group 8c / G
+#pragma unroll
+    for (int i = 0; i < kChMax; ++i) {
+      const int c = threadIdx.x + kQThreads * i;
+      if (i * kQThreads >= nch) break;             // uniform; within a pass idle lanes form whole groups
+      float v[8];
+      int col[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        col[e] = c < nch ? perm[8 * c + e] : 0;
+        v[e] = c < nch ? rowv[col[e]] : 0.0f;
+      }
+      float sc, zf;
+      const uint32_t packed = quantize_chunk8<ASYM>(v, c < nch ? 8 : 0, lpg, sc, zf);
+      if (c < nch) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) cbt[col[e]] = static_cast<uint8_t>((packed >> (4 * e)) & 15u);
+        if ((lane & (lpg - 1)) == 0) {
+          const int g = (8 * c) / G;
+          a.scales[n * a.NG + g] = sc;
+          if constexpr (ASYM) a.zeros[n * a.NG + g] = static_cast<uint8_t>(zf);
+        }
+      }
+    }
+    __syncthreads();                               // codes of the row complete in column order
+    // pack 8 columns per thread into one code word
+#pragma unroll
+    for (int i = 0; i < kChMax; ++i) {
+      const int j = threadIdx.x + kQThreads * i;
+      if (j < nch) {
+        const u32x2 b = *reinterpret_cast<const u32x2*>(cbt + 8 * j);
+        const uint32_t lo = b[0] | (b[0] >> 4), hi = b[1] | (b[1] >> 4);   // nibble pairs at bytes 0 and 2
+        const uint32_t w = (lo & 0xFFu) | ((lo >> 8) & 0xFF00u) | ((hi & 0xFFu) << 16) | (((hi >> 8) & 0xFF00u) << 16);
+        __builtin_nontemporal_store(w, reinterpret_cast<uint32_t*>(a.codes + n * KB) + j);
+      }
+    }
+  }
+}
+
+template <bool BF16, bool ASYM>
+hipError_t launch_qact(const QuantArgs& a, hipStream_t s) {
+  const size_t lds = act_q_lds(a.K, a.NG);
+  const dim3 grid(static_cast<uint32_t>((a.N + kActQRows - 1) / kActQRows)), block(kQThreads);
+  quantize_act_kernel<BF16, ASYM><<<grid, block, lds, s>>>(a);
+  return hipGetLastError();
+}
+
 template <bool BF16, bool ASYM, bool GIDX>
 hipError_t launch_q3(const QuantArgs& a, hipStream_t s) {
   const size_t lds = static_cast<size_t>(a.NG) * 4 * sizeof(uint32_t);
@@ -498,10 +653,16 @@ hipError_t launch_q3(const QuantArgs& a, hipStream_t s) {
 
 template <bool BF16, bool ASYM>
 hipError_t launch_q2(const QuantArgs& a, hipStream_t s) {
-  if (a.g_idx) return launch_q3<BF16, ASYM, true>(a, s);
+  const bool pow2 = (a.G & (a.G - 1)) == 0;
+  if (a.g_idx) {
+    // act-order: group-sorted rows when the groups can be uniform and the
+    // tables fit in LDS (the kernel checks the g_idx itself)
+    if (pow2 && a.G >= 8 && a.G <= 512 && a.K <= kActQMaxK && a.K % a.G == 0 && act_q_lds(a.K, a.NG) <= 65536)
+      return launch_qact<BF16, ASYM>(a, s);
+    return launch_q3<BF16, ASYM, true>(a, s);
+  }
   // fast path: contiguous power-of-two groups of at most 512 columns, rows
   // of at most 2048 * 8 columns
-  const bool pow2 = (a.G & (a.G - 1)) == 0;
   if (pow2 && a.G >= 8 && a.G <= 512 && a.K >= 64 && a.K <= 8 * 8 * kQThreads) return launch_qrows<BF16, ASYM>(a, s);
   return launch_q3<BF16, ASYM, false>(a, s);
 }
@@ -727,13 +888,15 @@ __global__ __launch_bounds__(kDThreads) void dequantize_act_kernel(DequantArgs a
   for (int p = threadIdx.x; p < nrows * NG; p += kDThreads) {
     const int64_t gi = (row0 + p / NG) * a.NG + p % NG;
     const float s = a.scales[gi];
-    const float z = ASYM ? static_cast<float>(a.zeros[gi]) : 8.0f;
+    const int z = ASYM ? static_cast<int>(a.zeros[gi]) : 8;
     uint32_t wv[16 * kEB / 4];
 #pragma unroll
     for (int u = 0; u < 16; u += 2) {
-      // signed codes: nibble u holds q with u = q & 15, value (u ^ 8) - 8
-      const float v0 = (static_cast<float>(ASYM ? u : (u ^ 8)) - z) * s;
-      const float v1 = (static_cast<float>(ASYM ? u + 1 : ((u + 1) ^ 8)) - z) * s;
+      // signed codes: nibble u holds q with u = q & 15, value (u ^ 8) - 8.
+      // The value is formed in integers (a float 0 - z may be folded to -z,
+      // which gives -0 for z = 0)
+      const float v0 = static_cast<float>((ASYM ? u : (u ^ 8)) - z) * s;
+      const float v1 = static_cast<float>((ASYM ? u + 1 : ((u + 1) ^ 8)) - z) * s;
       if constexpr (OUT_BF16) {
         wv[u / 2] = f32_to_bf16(v0) | (f32_to_bf16(v1) << 16);
       } else {

@@ -276,6 +276,22 @@ def test_codec_degenerate_values():
             _check_codec(x.to(torch.bfloat16), G, mode, label=f"degenerate{lab} bf16 {mode}")
 
 
+@pytest.mark.parametrize("N,K,G,dt,uniform", [(13, 4096, 128, torch.float32, True), (9, 8192, 512, torch.bfloat16, True),
+                                               (20, 512, 8, torch.bfloat16, True), (17, 1024, 64, torch.float32, False),
+                                               (11, 2048, 256, torch.bfloat16, False)])
+def test_act_order_codec(N, K, G, dt, uniform):
+    """Act-order quantize: uniform groups (every group G columns: the
+    group-sorted row kernel) and uneven random groups (its per-row fallback)."""
+    g = torch.Generator().manual_seed(N + K + G)
+    w = (torch.randn(N, K, generator=g) * 0.05).to(dt)
+    if uniform:
+        g_idx = (torch.randperm(K, generator=g) // G).to(torch.int32)
+    else:
+        g_idx = torch.randint(0, K // G, (K,), generator=g).to(torch.int32)
+    for mode in ("sym", "asym"):
+        _check_codec(w, G, mode, g_idx, label=f"act {N}x{K} G{G} {dt} {mode} uniform={uniform}")
+
+
 def test_act_order_with_unused_groups():
     """A g_idx that leaves some groups empty: those keep scale 1 (zero-point 0)."""
     N, K, G = 6, 64, 16
