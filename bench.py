@@ -172,7 +172,8 @@ def run_counters(w4):
 
 
 def bench_secondary(w4):
-    """Prefill GEMM, batched decode and codec round trip, each timed the same way."""
+    """Secondary entries (prefill quantize and GEMM, batched decode, input
+    gradient, LoRA merge, codecs), each timed the same way."""
     from int4_group_wise_amd.workloads import workload, generate
     dev = "cuda:0"
     out = {}
@@ -181,7 +182,19 @@ def bench_secondary(w4):
     wl = workload("prefill")
     t = generate(wl)
     gi = t["g_idx"].to(dev)
-    c, s, z = w4.quantize_pack(t["w"].to(dev), wl.G, wl.mode, gi)
+    wf = t["w"].to(dev)
+    c, s, z = w4.quantize_pack(wf, wl.G, wl.mode, gi)
+    # its act-order quantize: fp32 W [4096, 4096] -> codes, scales, zero-points
+    ev_ms, _ = time_graph(lambda i: w4.quantize_pack(wf, wl.G, wl.mode, gi, out=(c, s, z)), 20, 200, 20, 1)
+    qb = wf.numel() * 4 + gi.numel() * 4 + c.numel() + s.numel() * 4 + z.numel()
+    gq = qb * 200 / (ev_ms * 1e-3) / 1e9
+    out["prefill_quantize"] = {"metric": "act-order quantize_pack HBM GB/s", "value": round(gq, 1), "unit": "GB/s",
+                               "us_per_call": round(ev_ms * 1e3 / 200, 2),
+                               "roofline": {"bound": "hbm", "achieved": round(gq, 1), "peak": HBM_PEAK_GBS,
+                                            "unit": "GB/s", "frac": round(gq / HBM_PEAK_GBS, 4)},
+                               "config": {"workload": "prefill", "N": wl.N, "K": wl.K, "G": wl.G, "mode": wl.mode,
+                                          "w_dtype": "f32", "act_order": True}}
+    del wf
     x = t["x"].to(dev)
     y = torch.empty(wl.M, wl.N, dtype=torch.bfloat16, device=dev)
     ws = torch.empty(w4.linear_workspace_bytes(wl.M, wl.N, wl.K, wl.G, wl.mode, True), dtype=torch.uint8, device=dev)
