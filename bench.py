@@ -220,11 +220,12 @@ def bench_secondary(w4):
     rot = Rotation([c, s], 2 * MALL_BYTES)
     del c, s
     y = torch.empty(wl.M, wl.N, dtype=torch.bfloat16, device=dev)
+    bws = torch.empty(max(1, w4.linear_workspace_bytes(wl.M, wl.N, wl.K, wl.G, wl.mode)), dtype=torch.uint8, device=dev)
     steps = 100
 
     def call_b(i):
         cc, ss = rot.sets[i]
-        w4.linear(x, cc, ss, None, None, wl.K, wl.G, wl.mode, None, out=y)
+        w4.linear(x, cc, ss, None, None, wl.K, wl.G, wl.mode, None, out=y, workspace=bws)
 
     ev_ms, _ = time_graph(call_b, rot.count * 5, steps, rot.count, rot.count)
     nb = algorithmic_bytes_linear(wl.M, wl.N, wl.K, wl.G, False, False)

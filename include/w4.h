@@ -122,7 +122,9 @@ w4_status w4_dequantize(const uint8_t* codes, const float* scales,
 /*
  * w4_linear_workspace_bytes — device scratch w4_linear needs for this shape
  * (0 when none).  The prefill path (M > 16) stages the bf16 dequantized weight
- * [N, K] there.
+ * [N, K] there; the batched decode path (4 < M <= 16) may split K over a few
+ * workgroups and keep their fp32 partial sums there (splits * M * N * 4
+ * bytes), then add them in a fixed order.
  */
 size_t w4_linear_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t G,
                                  int mode, int has_g_idx);

@@ -111,8 +111,10 @@ w4_status w4_dequantize(const uint8_t* codes, const float* scales, const uint8_t
 }
 
 size_t w4_linear_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t G, int mode, int has_g_idx) {
-  (void)G; (void)mode; (void)has_g_idx;
-  if (M <= 16 || N < 1 || K < 1) return 0;
+  (void)mode;
+  if (M < 1 || N < 1 || K < 1 || (G < 1 && G != W4_PER_CHANNEL)) return 0;
+  if (M <= 16)   // fp32 split-K partials of the batched decode kernel, if it splits
+    return w4::skinny_workspace_bytes(M, N, K, kernel_group(K, G), has_g_idx != 0);
   return static_cast<size_t>(N) * static_cast<size_t>(K) * 2u;   // bf16 dequantized weight
 }
 
@@ -134,11 +136,14 @@ w4_status w4_linear(const void* x, int64_t M, const uint8_t* codes, const float*
   hipStream_t s = static_cast<hipStream_t>(stream);
   w4::LinearArgs a{static_cast<const uint16_t*>(x), M, codes, scales, zeros, g_idx, N, K, G, NG,
                    mode == W4_ASYM, static_cast<const uint16_t*>(bias), static_cast<uint16_t*>(y)};
-  if (w4::skinny_supported(a)) return hip_status(w4::launch_linear_skinny(a, s), fn);
   const size_t need = w4_linear_workspace_bytes(M, N, K, G, mode, g_idx != nullptr);
   if (workspace_bytes < need || (need && !workspace))
     return fail(W4_ERR_INVALID_ARG, "%s: workspace of %zu bytes needed (got %zu)", fn, need, workspace_bytes);
-  if (!aligned16(workspace)) return fail(W4_ERR_INVALID_ARG, "%s: workspace must be 16-byte aligned", fn);
+  if (need && !aligned16(workspace)) return fail(W4_ERR_INVALID_ARG, "%s: workspace must be 16-byte aligned", fn);
+  if (w4::skinny_supported(a)) {
+    a.partial = need ? static_cast<float*>(workspace) : nullptr;
+    return hip_status(w4::launch_linear_skinny(a, s), fn);
+  }
   const int64_t chunk_blocks = ((K + 7) / 8 + 255) / 256;
   const int64_t gemm_blocks = K % 8 == 0 ? ((M + 127) / 128) * ((N + 127) / 128) : (M * N + 255) / 256;
   if (N * chunk_blocks > kMaxGrid || gemm_blocks > kMaxGrid)

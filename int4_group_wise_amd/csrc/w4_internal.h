@@ -41,6 +41,7 @@ struct LinearArgs {
   int asym;
   const uint16_t* bias; // bf16 [N] or NULL
   uint16_t* y;          // bf16 [M, N]
+  float* partial;       // workspace for split-K partial sums (batched decode), or NULL
 };
 
 struct GradArgs {
@@ -110,6 +111,9 @@ hipError_t launch_dequantize(const DequantArgs& a, hipStream_t s);
 // covers the request (the caller then takes the prefill path).
 bool skinny_supported(const LinearArgs& a);
 hipError_t launch_linear_skinny(const LinearArgs& a, hipStream_t s);
+// Workspace the skinny path needs (fp32 split-K partials of the batched
+// decode kernel; 0 when it runs in one pass).
+size_t skinny_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t G, bool has_g_idx);
 
 // Dense bf16 GEMM  y = x . wd^T + bias  (x [M, K], wd [N, K], y [M, N]).
 hipError_t launch_gemm_bf16(const uint16_t* x, const uint16_t* wd,

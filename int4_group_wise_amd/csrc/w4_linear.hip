@@ -46,17 +46,19 @@ __device__ __forceinline__ void pair_x(const uint32_t a[4], uint32_t xp[4]) {
   xp[3] = perm(a[3], a[1], 0x07060302u);   // (x3, x7)
 }
 
-// (a & m) | e in one instruction.  The compiler does not form v_and_or_b32
-// from C (a VOP3 op may read only one scalar or literal operand here), so it
-// is written out; the nibble mask lives in a VGPR, the exponent pattern in an
-// SGPR.
+// (a & m) | e.  Written in C so that the compiler sees the definition: its
+// result often feeds a matrix-core operand, and only instructions the
+// compiler can see get the wait states a VALU write needs before an MFMA
+// reads the same register.
 __device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t m, uint32_t e) {
-  uint32_t r;
-  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(m), "s"(e));
-  return r;
+  return (a & m) | e;
 }
 
-// The nibble-pair mask 0x000F000F held in a VGPR (see and_or).
+// The nibble-pair mask 0x000F000F in a VGPR.  Loaded in asm so that the
+// compiler cannot fold it into a constant: with the mask in a register and the
+// exponent pattern in an SGPR, (a & m) | e selects one v_and_or_b32 (a VOP3
+// op here may read one scalar and no literal).  Its only readers are VALU
+// ops, so no matrix-core hazard hides behind the asm.
 __device__ __forceinline__ uint32_t nibble_mask() {
   uint32_t r;
   asm volatile("v_mov_b32 %0, 0x000F000F" : "=v"(r));
@@ -646,12 +648,13 @@ __device__ __forceinline__ void rows_compute(const LinearArgs& a, int b, int nkb
 #pragma unroll
   for (int j = 0; j < kRowsKB; ++j) {
     if (kbf + j < nkb) {
-      // the wave's LDS operations complete in order, so the read sees the
-      // write; alternating halves let consecutive blocks overlap
-      // (chunk c of row r sits at slot 4 r + (c ^ ((r >> 1) & 3)), so that
-      // both the write and the transposed read hit distinct banks)
+      // the transposed read needs other lanes' writes: wait for the wave's
+      // own LDS writes in between (alternating halves let consecutive blocks
+      // overlap; chunk c of row r sits at slot 4 r + (c ^ ((r >> 1) & 3)), so
+      // that both the write and the transposed read hit distinct banks)
       u32x4* sc2 = scratch + 64 * (j & 1);
       sc2[rq * 4 + (cq ^ ((rq >> 1) & 3))] = R.cw[j];
+      __builtin_amdgcn_s_waitcnt(0xc07f);          // lgkmcnt(0)
       const u32x4 v = sc2[n * 4 + (q ^ ((n >> 1) & 3))];
       uint32_t d[4] = {v[0], v[1], v[2], v[3]};
       if constexpr (!ASYM) {
@@ -688,8 +691,11 @@ __device__ __forceinline__ void rows_compute(const LinearArgs& a, int b, int nkb
   }
 }
 
+// Split-K: blockIdx.y = split s of `splits` takes batches [s nbat / splits,
+// (s + 1) nbat / splits); with more than one split the fp32 partial tiles go to
+// a.partial [splits][M][N] and rows_reduce_kernel adds them in split order.
 template <bool ASYM, bool TR, int GU>
-__global__ __launch_bounds__(kRowsWaves * kWave, 2) void skinny_rows_kernel(LinearArgs a) {
+__global__ __launch_bounds__(kRowsWaves * kWave, 2) void skinny_rows_kernel(LinearArgs a, int splits) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   const RowsLayout L = rows_layout();
   const int lane = lane_id();
@@ -702,25 +708,38 @@ __global__ __launch_bounds__(kRowsWaves * kWave, 2) void skinny_rows_kernel(Line
   const uint32_t mask = nibble_mask();
   float out[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 
+  const int bb = static_cast<int>(static_cast<int64_t>(blockIdx.y) * nbat / splits);
+  const int be = static_cast<int>(static_cast<int64_t>(blockIdx.y + 1) * nbat / splits);
   RowsRegs ra, rb;
-  rows_issue<ASYM>(a, 0, nkb, n0c, lane, ra);
-  rows_stage(a, 0, lane, ra, smem, L, wave_lds);
+  rows_issue<ASYM>(a, bb, nkb, n0c, lane, ra);
+  rows_stage(a, bb, lane, ra, smem, L, wave_lds);
   __syncthreads();
-  for (int b = 0; b < nbat; b += 2) {
-    if (b + 1 < nbat) rows_issue<ASYM>(a, b + 1, nkb, n0c, lane, rb);
+  for (int b = bb; b < be; b += 2) {
+    if (b + 1 < be) rows_issue<ASYM>(a, b + 1, nkb, n0c, lane, rb);
     rows_compute<ASYM, TR, GU>(a, b, nkb, lane, mask, ra, smem, L, wave_lds, out);
-    if (b + 1 >= nbat) break;
+    if (b + 1 >= be) break;
     rows_stage(a, b + 1, lane, rb, smem, L, wave_lds);
     __syncthreads();
-    if (b + 2 < nbat) rows_issue<ASYM>(a, b + 2, nkb, n0c, lane, ra);
+    if (b + 2 < be) rows_issue<ASYM>(a, b + 2, nkb, n0c, lane, ra);
     rows_compute<ASYM, TR, GU>(a, b + 1, nkb, lane, mask, rb, smem, L, wave_lds, out);
-    if (b + 2 >= nbat) break;
+    if (b + 2 >= be) break;
     rows_stage(a, b + 2, lane, ra, smem, L, wave_lds);
     __syncthreads();
   }
 
   // lane holds output rows m = 4 q + t of weight row n0 + n
   const int n = lane & 15, q = lane >> 4;
+  if (splits > 1) {
+    if (n0 + n < a.N) {
+      float* part = a.partial + static_cast<int64_t>(blockIdx.y) * a.M * a.N;
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const int m = 4 * q + t;
+        if (m < a.M) part[static_cast<int64_t>(m) * a.N + n0 + n] = out[t];
+      }
+    }
+    return;
+  }
   if (n0 + n < a.N) {
     const float bias = a.bias ? bf16_to_f32(a.bias[n0 + n]) : 0.0f;
 #pragma unroll
@@ -729,6 +748,19 @@ __global__ __launch_bounds__(kRowsWaves * kWave, 2) void skinny_rows_kernel(Line
       if (m < a.M) a.y[static_cast<int64_t>(m) * a.N + n0 + n] = static_cast<uint16_t>(f32_to_bf16(out[t] + bias));
     }
   }
+}
+
+// y[m, n] = bf16(sum over splits s = 0 .. S-1 of partial[s][m][n] + b[n]),
+// one thread per output, the splits added in order.
+__global__ __launch_bounds__(256) void rows_reduce_kernel(const float* __restrict__ partial, int splits, int64_t M,
+                                                          int64_t N, const uint16_t* __restrict__ bias,
+                                                          uint16_t* __restrict__ y) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (i >= M * N) return;
+  float t = 0.0f;
+  for (int sp = 0; sp < splits; ++sp) t += partial[static_cast<int64_t>(sp) * M * N + i];
+  const float b = bias ? bf16_to_f32(bias[i % N]) : 0.0f;
+  y[i] = static_cast<uint16_t>(f32_to_bf16(t + b));
 }
 
 // Any G, K and g_idx, M <= 16: one wave per weight row.  Each lane handles one
@@ -819,11 +851,29 @@ bool mfma_ok(const LinearArgs& a) {
   return x_layout(MT, a.K).bytes <= 65536;
 }
 
+// Split-K count for the batched decode kernel: doubled (within the number of
+// batches) until the grid holds at least kRowsMinWaves waves, four per SIMD.
+constexpr int64_t kRowsMinWaves = 4096;
+int rows_splits(int64_t N, int64_t K) {
+  const int64_t waves = (N + 15) / 16;
+  const int64_t nbat = (K / 128 + kRowsKB - 1) / kRowsKB;
+  int sp = 1;
+  while (waves * sp < kRowsMinWaves && 2 * sp <= nbat) sp *= 2;
+  return sp;
+}
+
 template <bool ASYM, bool TR, int GU>
 hipError_t launch_rows3(const LinearArgs& a, hipStream_t s) {
   const RowsLayout L = rows_layout();
-  const dim3 grid(static_cast<uint32_t>((a.N + 16 * kRowsWaves - 1) / (16 * kRowsWaves)));
-  skinny_rows_kernel<ASYM, TR, GU><<<grid, dim3(kRowsWaves * kWave), L.bytes, s>>>(a);
+  const int splits = a.partial ? rows_splits(a.N, a.K) : 1;
+  const dim3 grid(static_cast<uint32_t>((a.N + 16 * kRowsWaves - 1) / (16 * kRowsWaves)), static_cast<uint32_t>(splits));
+  skinny_rows_kernel<ASYM, TR, GU><<<grid, dim3(kRowsWaves * kWave), L.bytes, s>>>(a, splits);
+  if (splits > 1) {
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    rows_reduce_kernel<<<dim3(static_cast<uint32_t>((a.M * a.N + 255) / 256)), dim3(256), 0, s>>>(
+        a.partial, splits, a.M, a.N, a.bias, a.y);
+  }
   return hipGetLastError();
 }
 
@@ -848,6 +898,15 @@ bool dot2_ok(const LinearArgs& a) {
 }  // namespace
 
 bool skinny_supported(const LinearArgs& a) { return a.M >= 1 && a.M <= 16; }
+
+size_t skinny_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t G, bool has_g_idx) {
+  LinearArgs a{};
+  a.M = M; a.N = N; a.K = K; a.G = G;
+  a.g_idx = has_g_idx ? reinterpret_cast<const int32_t*>(16) : nullptr;
+  if (!rows_ok(a)) return 0;
+  const int sp = rows_splits(N, K);
+  return sp > 1 ? static_cast<size_t>(sp) * static_cast<size_t>(M) * static_cast<size_t>(N) * sizeof(float) : 0;
+}
 
 hipError_t launch_linear_skinny(const LinearArgs& a, hipStream_t s) {
   if (!skinny_supported(a)) return hipErrorInvalidValue;

@@ -167,6 +167,12 @@ CASES = [
     (40, 70, 99, 16, "sym", False, "f32", "none"),      # prefill, K % 8 != 0
     (300, 260, 1024, 128, "asym", True, "f32", "randn"),
     (129, 128, 4096, 4096, "sym", False, "bf16", "none"),  # one group per row
+    # prefill through the fragment-tiled weight (K % 64 == 0): one and two
+    # K-steps, a step count that is not a multiple of 3, M and N tails
+    (33, 40, 64, 16, "sym", False, "f32", "randn"),
+    (18, 256, 128, 128, "asym", False, "f32", "none"),
+    (257, 300, 640, 32, "asym", True, "f32", "none"),
+    (65, 33, 128, 64, "sym", False, "bf16", "randn"),
     # per-channel (G = -1, or any G >= K): one scale per row
     (1, 40, 100, -1, "sym", False, "f32", "randn"),
     (4, 33, 4096, -1, "sym", False, "bf16", "none"),     # matrix-core decode
