@@ -114,13 +114,17 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_nt_kernel(
 //
 // LDS layout of a stage: A rows (256) then B rows (128), 128 bytes each (64
 // bf16), split in 8 chunks of 16 bytes; chunk c of row r is stored at slot
-// c ^ (r & 7), so the 16 rows a fragment read touches hit distinct banks.  A
-// load instruction fills 1 KB of consecutive slots (8 rows): lane i writes
-// slot i, so lane i fetches the global chunk that belongs there.
+// c ^ swz(r).  A 16-byte LDS read serves 16 lanes per cycle from 64 banks (8
+// lanes from 32 banks on parts with 32); swz keeps the 16 rows such a group
+// touches on distinct 16-byte bank groups either way.  A load instruction
+// fills 1 KB of consecutive slots (8 rows): lane i writes slot i, so lane i
+// fetches the global chunk that belongs there.
 // ---------------------------------------------------------------------------
 constexpr int PM = 256, PN = 128, PK = 64, PSTAGES = 3;
 constexpr int kPStageBytes = (PM + PN) * PK * 2;          // 48 KB
 constexpr int kPLdsBytes = PSTAGES * kPStageBytes;       // 144 KB
+
+__device__ __forceinline__ int swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
 
 __device__ __forceinline__ void lds_dma16(const void* gsrc, void* ldst) {
   __builtin_amdgcn_global_load_lds(gsrc, reinterpret_cast<__attribute__((address_space(3))) void*>(
@@ -152,13 +156,13 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_pipe_kernel(
   for (int p = 0; p < 8; ++p) {
     const int r = 64 * wid + 8 * p + lr;
     const int gm = min(m0 + r, M - 1);
-    asrc[p] = x + static_cast<int64_t>(gm) * K + 8 * (ls ^ (r & 7));
+    asrc[p] = x + static_cast<int64_t>(gm) * K + 8 * (ls ^ swz(r));
   }
 #pragma unroll
   for (int p = 0; p < 4; ++p) {
     const int r = 32 * wid + 8 * p + lr;
     const int gn = min(n0 + r, N - 1);
-    bsrc[p] = wd + static_cast<int64_t>(gn) * K + 8 * (ls ^ (r & 7));
+    bsrc[p] = wd + static_cast<int64_t>(gn) * K + 8 * (ls ^ swz(r));
   }
   auto issue = [&](int kt) {
     uint8_t* st = psm + (kt % PSTAGES) * kPStageBytes;
@@ -209,12 +213,12 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_pipe_kernel(
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
         const int r = 32 * j + fr;
-        bfr[ks][j] = *reinterpret_cast<const bf16x8_t*>(sb + r * 128 + 16 * (chunk ^ (r & 7)));
+        bfr[ks][j] = *reinterpret_cast<const bf16x8_t*>(sb + r * 128 + 16 * (chunk ^ swz(r)));
       }
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int r = 32 * i + fr;
-        af[ks][i] = *reinterpret_cast<const bf16x8_t*>(sa + r * 128 + 16 * (chunk ^ (r & 7)));
+        af[ks][i] = *reinterpret_cast<const bf16x8_t*>(sa + r * 128 + 16 * (chunk ^ swz(r)));
       }
     }
 #pragma unroll

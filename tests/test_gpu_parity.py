@@ -173,6 +173,18 @@ CASES = [
     (18, 256, 128, 128, "asym", False, "f32", "none"),
     (257, 300, 640, 32, "asym", True, "f32", "none"),
     (65, 33, 128, 64, "sym", False, "bf16", "randn"),
+    # prefill with the dequantization fused into the GEMM (contiguous groups,
+    # K % 64 == 0): 1, 2, 3, 4 and 17 K-steps of the 4-stage ring, M and N
+    # tile tails (128 x 256 tiles), G from 32 to 256, a partial last group,
+    # one group per row
+    (17, 300, 64, 64, "sym", False, "bf16", "none"),
+    (40, 512, 128, 32, "asym", False, "f32", "none"),
+    (200, 96, 192, 64, "sym", False, "f32", "randn"),
+    (130, 257, 256, 32, "asym", False, "f32", "randn"),
+    (33, 64, 1088, 256, "sym", False, "f32", "none"),
+    (64, 256, 2048, 128, "asym", False, "bf16", "randn"),
+    (300, 520, 512, 128, "sym", False, "f32", "randn"),
+    (96, 80, 1024, -1, "sym", False, "f32", "none"),
     # per-channel (G = -1, or any G >= K): one scale per row
     (1, 40, 100, -1, "sym", False, "f32", "randn"),
     (4, 33, 4096, -1, "sym", False, "bf16", "none"),     # matrix-core decode
@@ -308,7 +320,8 @@ def test_act_order_with_unused_groups():
 
 
 @pytest.mark.parametrize("M,K,G,mode", [(16, 256, 32, "asym"), (4, 512, 128, "sym"), (1, 96, 32, "asym"),
-                                        (7, 100, 8, "sym"), (256, 256, 64, "asym"), (96, 96, 32, "sym")])
+                                        (7, 100, 8, "sym"), (256, 256, 64, "asym"), (96, 96, 32, "sym"),
+                                        (130, 1024, 256, "asym"), (200, 512, 32, "sym"), (48, 640, -1, "sym")])
 def test_identity_activation_is_exact(M, K, G, mode):
     """x = rows of the identity: every output is a single product, so
     y[i, n] must equal the bf16 dequantized weight Wd[n, k_i] bit for bit."""
