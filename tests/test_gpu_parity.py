@@ -173,10 +173,9 @@ CASES = [
     (18, 256, 128, 128, "asym", False, "f32", "none"),
     (257, 300, 640, 32, "asym", True, "f32", "none"),
     (65, 33, 128, 64, "sym", False, "bf16", "randn"),
-    # prefill with the dequantization fused into the GEMM (contiguous groups,
-    # K % 64 == 0): 1, 2, 3, 4 and 17 K-steps of the 4-stage ring, M and N
-    # tile tails (128 x 256 tiles), G from 32 to 256, a partial last group,
-    # one group per row
+    # prefill with contiguous groups and K % 64 == 0 (dequantize + pipelined
+    # GEMM): 1, 2, 3, 4 and 17 K-steps, M and N tile tails, G from 32 to 256,
+    # a partial last group, one group per row
     (17, 300, 64, 64, "sym", False, "bf16", "none"),
     (40, 512, 128, 32, "asym", False, "f32", "none"),
     (200, 96, 192, 64, "sym", False, "f32", "randn"),
