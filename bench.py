@@ -9,7 +9,8 @@ Infinity Cache, so each call streams its weights from HBM as it would in a
 model with many layers.  The JSON line reports whole-job HBM GB/s of the
 algorithmic bytes, the decode kernel's roofline (its average launch duration
 measured with HIP events on the launch stream), and the CPU oracle on a
-bounded sample.  Secondary entries cover the prefill GEMM (TFLOP/s), the
+bounded sample.  Secondary entries cover a hot-cache decode figure (labelled
+as such), the prefill GEMM (TFLOP/s), the
 batched decode, the input gradient (decode and prefill shapes), the LoRA
 merge, the codec round trip, the GGUF Q4_0 codec and the zero-point packing.
 """
@@ -115,6 +116,25 @@ def bench_decode(w4, steps, warmup):
     return wl, nbytes, ev_ms, host_ms, rot
 
 
+def bench_decode_hot(w4, steps=2000):
+    """The decode workload on one weight copy, resident in the Infinity Cache:
+    a hot-cache figure, not the headline (which streams from HBM)."""
+    from int4_group_wise_amd.workloads import workload, generate
+    wl = workload("decode")
+    t = generate(wl)
+    dev = "cuda:0"
+    c, s, z = w4.quantize_pack(t["w"].to(dev), wl.G, wl.mode)
+    x, b = t["x"].to(dev), t["bias"].to(dev)
+    y = torch.empty(wl.M, wl.N, dtype=torch.bfloat16, device=dev)
+    ev_ms, _ = time_graph(lambda i: w4.linear(x, c, s, z, None, wl.K, wl.G, wl.mode, b, out=y), 100, steps, 100, 1)
+    nbytes = algorithmic_bytes_linear(wl.M, wl.N, wl.K, wl.G, True, True)
+    gbs = nbytes * steps / (ev_ms * 1e-3) / 1e9
+    return {"metric": "W4A16 linear GB/s M=1, hot cache (one weight copy, Infinity-Cache resident; not HBM-bound)",
+            "value": round(gbs, 1), "unit": "GB/s", "us_per_call": round(ev_ms * 1e3 / steps, 3),
+            "config": {"workload": "decode", "M": wl.M, "N": wl.N, "K": wl.K, "G": wl.G, "mode": wl.mode,
+                       "weight_copies_rotated": 1}}
+
+
 PROFILES = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles")
 TRAFFIC_FILE = os.path.join(PROFILES, "gemv_dot2_decode_traffic.txt")
 DECODE_SOURCES = ("w4_linear.hip", "w4_device.h", "w4_internal.h")
@@ -151,7 +171,9 @@ def measured_traffic():
 
 def run_counters(w4):
     """Eager launches for rocprofv3 --pmc: 12 decode calls over 3 weight
-    copies, then 3 plain device copies of 256 MiB that calibrate the counters."""
+    copies, then 3 plain device copies of 256 MiB that calibrate the counters,
+    then 8 batched-decode calls over 2 weight copies, 2 codec round trips
+    (quantize_pack + dequantize) and 3 prefill calls."""
     from int4_group_wise_amd.workloads import workload, generate
     dev = "cuda:0"
     wl = workload("decode")
@@ -167,6 +189,41 @@ def run_counters(w4):
         w4.linear(x, c, s, z, None, wl.K, wl.G, wl.mode, b, out=y)
     for _ in range(3):
         dst.copy_(src)
+    torch.cuda.synchronize()
+    del sets, src, dst, t
+    # batched decode
+    wl = workload("batched_decode")
+    t = generate(wl)
+    sets = [w4.quantize_pack(t["w"].to(dev), wl.G, wl.mode) for _ in range(2)]
+    del t["w"]
+    x = t["x"].to(dev)
+    y = torch.empty(wl.M, wl.N, dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(max(1, w4.linear_workspace_bytes(wl.M, wl.N, wl.K, wl.G, wl.mode)), dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+    for i in range(8):
+        c, s, _ = sets[i % 2]
+        w4.linear(x, c, s, None, None, wl.K, wl.G, wl.mode, None, out=y, workspace=ws)
+    torch.cuda.synchronize()
+    del sets, x, y, ws, t
+    # codec round trip
+    wl = workload("codec")
+    w = generate(wl)["w"].to(dev)
+    for _ in range(2):
+        c, s, z = w4.quantize_pack(w, wl.G, wl.mode)
+        d = w4.dequantize(c, s, z, None, wl.K, wl.G, wl.mode, torch.bfloat16)
+        del c, s, z, d
+    torch.cuda.synchronize()
+    del w
+    # prefill (act-order dequantize + GEMM)
+    wl = workload("prefill")
+    t = generate(wl)
+    gi = t["g_idx"].to(dev)
+    c, s, z = w4.quantize_pack(t["w"].to(dev), wl.G, wl.mode, gi)
+    x = t["x"].to(dev)
+    y = torch.empty(wl.M, wl.N, dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(w4.linear_workspace_bytes(wl.M, wl.N, wl.K, wl.G, wl.mode, True), dtype=torch.uint8, device=dev)
+    for _ in range(3):
+        w4.linear(x, c, s, z, gi, wl.K, wl.G, wl.mode, None, out=y, workspace=ws)
     torch.cuda.synchronize()
     print("counter launches done", flush=True)
 
@@ -365,10 +422,20 @@ def bench_secondary(w4):
     return out
 
 
-def cpu_baseline(seconds=12.0):
+def _repeat(fn, seconds):
+    n, t0 = 0, time.perf_counter()
+    while True:
+        fn()
+        n += 1
+        if time.perf_counter() - t0 >= seconds:
+            return n, time.perf_counter() - t0
+
+
+def cpu_baseline(seconds=12.0, stage_seconds=4.0):
     """The oracle, untuned, on a bounded sample of the decode workload: the
     linear (dequantize to bf16 + fp64 matmul) over the first rows of W,
-    repeated until `seconds` have passed.  One BLAS thread."""
+    repeated until `seconds` have passed, then its quantize_pack and
+    dequantize stages on the same rows.  One BLAS thread."""
     from oracle import w4_oracle as O
     from int4_group_wise_amd.workloads import workload, generate, bf16_bits
     try:
@@ -399,10 +466,21 @@ def cpu_baseline(seconds=12.0):
     el = time.perf_counter() - t0
     per_row = algorithmic_bytes_linear(wl.M, wl.N, wl.K, wl.G, True, True) / wl.N
     gbs = per_row * rows * n / el / 1e9
+    # stages on the same rows: bytes as the GPU codec counts them
+    ng = (wl.K + wl.G - 1) // wl.G
+    packed = rows * ((wl.K + 1) // 2 + 5 * ng)
+    nq, tq = _repeat(lambda: O.quantize_pack(wr, wl.G, O.ASYM), stage_seconds)
+    nd, td = _repeat(lambda: O.dequantize(codes, sc, z, None, wl.K, wl.G, O.ASYM, "bf16"), stage_seconds)
+    stages = {"quantize_pack": {"GB/s": round((rows * wl.K * 4 + packed) * nq / tq / 1e9, 4), "repetitions": nq,
+                                "seconds": round(tq, 1)},
+              "dequantize_bf16": {"GB/s": round((packed + rows * wl.K * 2) * nd / td / 1e9, 4), "repetitions": nd,
+                                  "seconds": round(td, 1)}}
     return {"value": round(gbs, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
             "sample": f"oracle linear (dequantize to bf16, fp64 matmul, bias) on the first {rows} of "
                       f"{wl.N} weight rows of the decode workload, {n} repetitions in {el:.1f} s, "
-                      f"bytes scaled per row"}
+                      f"bytes scaled per row; stages: quantize_pack (fp32 rows in) and dequantize "
+                      f"(bf16 out) on the same rows",
+            "stages": stages}
 
 
 def main():
@@ -456,7 +534,8 @@ def main():
     del rot
     torch.cuda.empty_cache()
     if not args.no_secondary:
-        line["secondary"] = bench_secondary(w4)
+        line["secondary"] = {"decode_hot_cache": bench_decode_hot(w4)}
+        line["secondary"].update(bench_secondary(w4))
         torch.cuda.empty_cache()
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline()
