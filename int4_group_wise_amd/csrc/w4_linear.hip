@@ -886,10 +886,10 @@ hipError_t launch_rows2(const LinearArgs& a, hipStream_t s) {
 
 // Batched decode on the matrix cores: contiguous groups of 32, 64 or a
 // multiple of 128 columns, K a multiple of 128, 4 < M <= 16.
-bool rows_ok(const LinearArgs& a) {
-  return a.g_idx == nullptr && a.K % 128 == 0 && a.M > 4 && a.M <= 16 &&
-         (a.G == 32 || a.G == 64 || a.G % 128 == 0);
+bool rows_shape_ok(int64_t M, int64_t K, int64_t G, bool has_g_idx) {
+  return !has_g_idx && K % 128 == 0 && M > 4 && M <= 16 && (G == 32 || G == 64 || G % 128 == 0);
 }
+bool rows_ok(const LinearArgs& a) { return rows_shape_ok(a.M, a.K, a.G, a.g_idx != nullptr); }
 
 bool dot2_ok(const LinearArgs& a) {
   return a.g_idx == nullptr && a.G % 32 == 0 && a.K % 32 == 0 && a.M <= 4;
@@ -900,10 +900,7 @@ bool dot2_ok(const LinearArgs& a) {
 bool skinny_supported(const LinearArgs& a) { return a.M >= 1 && a.M <= 16; }
 
 size_t skinny_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t G, bool has_g_idx) {
-  LinearArgs a{};
-  a.M = M; a.N = N; a.K = K; a.G = G;
-  a.g_idx = has_g_idx ? reinterpret_cast<const int32_t*>(16) : nullptr;
-  if (!rows_ok(a)) return 0;
+  if (!rows_shape_ok(M, K, G, has_g_idx)) return 0;
   const int sp = rows_splits(N, K);
   return sp > 1 ? static_cast<size_t>(sp) * static_cast<size_t>(M) * static_cast<size_t>(N) * sizeof(float) : 0;
 }
