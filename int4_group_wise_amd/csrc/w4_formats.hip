@@ -35,20 +35,38 @@ constexpr int kQ4WaveChunks = kQ4WaveBytes / 16;
 template <bool BF16>
 __global__ __launch_bounds__(kFThreads) void q4_0_quantize_kernel(const void* __restrict__ w, int64_t nblocks,
                                                                    uint8_t* __restrict__ out) {
+  // The wave's 64 blocks are one contiguous run of weights: they are read
+  // with coalesced 16-byte loads (lane l of load c takes chunk 64 c + l of the
+  // run, read once: non-temporal) into LDS rows of BB + 16 bytes (the padding
+  // keeps each lane's row reads free of bank conflicts), then each lane reads
+  // its own block.
+  constexpr int BB = BF16 ? 64 : 128;   // input bytes per block
+  constexpr int PB = BB + 16;
+  constexpr int NI = BB / 16;           // 16-byte chunks per block
+  __shared__ __attribute__((aligned(16))) uint8_t inb[kFThreads / kWave][kWave * PB];
   __shared__ __attribute__((aligned(16))) uint8_t stage[kFThreads / kWave][kQ4WaveBytes];
   const int lane = lane_id();
   const int wv = threadIdx.x >> 6;
   const int64_t g0 = (static_cast<int64_t>(blockIdx.x) * kFThreads) + kWave * wv;   // the wave's first block
   const int64_t g = g0 + lane;
-  const int64_t gc = min(g, nblocks - 1);
-
-  // the block's 32 weights (read once: non-temporal)
+  // blocks of this wave that exist (<= 0 for the trailing waves of the last
+  // workgroup, which load nothing and store nothing but reach the barriers)
+  const int64_t nvalid = min(static_cast<int64_t>(kWave), nblocks - g0);
+  if (nvalid > 0) {
+    const uint8_t* src = static_cast<const uint8_t*>(w) + g0 * BB;
+#pragma unroll
+    for (int c = 0; c < NI; ++c) {
+      const int i = min(kWave * c + lane, static_cast<int>(nvalid) * NI - 1);   // clamped: in bounds
+      const u32x4 q = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src) + i);
+      *reinterpret_cast<u32x4*>(&inb[wv][(i / NI) * PB + (i % NI) * 16]) = q;
+    }
+  }
+  __syncthreads();
   float v[kQ4Block];
   if constexpr (BF16) {
-    const u32x4* src = reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(w) + gc * kQ4Block);
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
-      const u32x4 q = __builtin_nontemporal_load(src + c);
+      const u32x4 q = *reinterpret_cast<const u32x4*>(&inb[wv][lane * PB + 16 * c]);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         v[8 * c + 2 * i] = __uint_as_float(q[i] << 16);
@@ -56,10 +74,9 @@ __global__ __launch_bounds__(kFThreads) void q4_0_quantize_kernel(const void* __
       }
     }
   } else {
-    const u32x4* src = reinterpret_cast<const u32x4*>(static_cast<const float*>(w) + gc * kQ4Block);
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
-      const u32x4 q = __builtin_nontemporal_load(src + c);
+      const u32x4 q = *reinterpret_cast<const u32x4*>(&inb[wv][lane * PB + 16 * c]);
 #pragma unroll
       for (int i = 0; i < 4; ++i) v[4 * c + i] = __uint_as_float(q[i]);
     }
@@ -100,7 +117,6 @@ __global__ __launch_bounds__(kFThreads) void q4_0_quantize_kernel(const void* __
 
   // the wave's blocks through LDS (2-byte granules: a block starts at an even
   // offset), then 72 chunks of 16 bytes
-  const int64_t nvalid = min(static_cast<int64_t>(kWave), nblocks - g0);   // > 0
   uint16_t* st = reinterpret_cast<uint16_t*>(stage[wv] + kQ4Bytes * lane);
   if (g < nblocks) {
     st[0] = __builtin_bit_cast(uint16_t, d16);
