@@ -31,6 +31,7 @@ constexpr int kQ4Block = 32;
 constexpr int kQ4Bytes = 18;
 constexpr int kQ4WaveBytes = kWave * kQ4Bytes;          // 1152 = 72 chunks of 16 bytes
 constexpr int kQ4WaveChunks = kQ4WaveBytes / 16;
+constexpr int kQ4DeqBlocks = 128;                       // blocks per wave when dequantizing
 
 template <bool BF16>
 __global__ __launch_bounds__(kFThreads) void q4_0_quantize_kernel(const void* __restrict__ w, int64_t nblocks,
@@ -140,60 +141,71 @@ __global__ __launch_bounds__(kFThreads) void q4_0_quantize_kernel(const void* __
   }
 }
 
-// Dequantize: a lane decodes WPL consecutive weights of one block (8 for bf16,
-// 4 for fp32 output: 16 bytes), so the wave's stores are one contiguous run.
-// A wave covers 64 / (32 / WPL) blocks; their bytes (288 or 144, 16-byte
-// aligned) come in through LDS.
+// Dequantize: a wave takes 128 consecutive blocks (2304 bytes, 16-byte
+// aligned), reads them with coalesced loads into LDS, then decodes them in
+// rounds: in each round a lane turns WPL consecutive weights of one block (8
+// for bf16, 4 for fp32 output: 16 bytes) into one store, so a round's stores
+// are one contiguous run of 1 KB.
 template <bool OUT_BF16>
 __global__ __launch_bounds__(kFThreads) void q4_0_dequantize_kernel(const uint8_t* __restrict__ blocks,
                                                                      int64_t nblocks, void* __restrict__ out) {
-  constexpr int kWPL = OUT_BF16 ? 8 : 4;                 // weights per lane
+  constexpr int kWPL = OUT_BF16 ? 8 : 4;                 // weights per lane and round
   constexpr int kLPB = kQ4Block / kWPL;                  // lanes per block
-  constexpr int kBPW = kWave / kLPB;                     // blocks per wave
-  constexpr int kChunks = kBPW * kQ4Bytes / 16;          // 18 or 9
-  __shared__ __attribute__((aligned(16))) uint8_t stage[kFThreads / kWave][kBPW * kQ4Bytes];
+  constexpr int kBPR = kWave / kLPB;                     // blocks per round
+  constexpr int kRounds = kQ4DeqBlocks / kBPR;
+  constexpr int kChunks = kQ4DeqBlocks * kQ4Bytes / 16;  // 144
+  __shared__ __attribute__((aligned(16))) uint8_t stage[kFThreads / kWave][kQ4DeqBlocks * kQ4Bytes];
   const int lane = lane_id();
   const int wv = threadIdx.x >> 6;
-  const int64_t g0 = (static_cast<int64_t>(blockIdx.x) * (kFThreads / kWave) + wv) * kBPW;   // the wave's first block
-  const int64_t nvalid = min(static_cast<int64_t>(kBPW), nblocks - g0);
+  const int64_t g0 = (static_cast<int64_t>(blockIdx.x) * (kFThreads / kWave) + wv) * kQ4DeqBlocks;
+  // blocks of this wave that exist (<= 0 for the trailing waves of the last
+  // workgroup, which load and store nothing but reach the barrier)
+  const int64_t nvalid = min(static_cast<int64_t>(kQ4DeqBlocks), nblocks - g0);
   const uint8_t* src = blocks + g0 * kQ4Bytes;
-  if (nvalid == kBPW) {
-    if (lane < kChunks)
-      reinterpret_cast<u32x4*>(stage[wv])[lane] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src) + lane);
-  } else {
+  if (nvalid == kQ4DeqBlocks) {
+#pragma unroll
+    for (int i = 0; i < (kChunks + kWave - 1) / kWave; ++i) {
+      const int c = lane + kWave * i;
+      if (c < kChunks)
+        reinterpret_cast<u32x4*>(stage[wv])[c] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src) + c);
+    }
+  } else if (nvalid > 0) {
     uint16_t* sv = reinterpret_cast<uint16_t*>(stage[wv]);
     const uint16_t* s2 = reinterpret_cast<const uint16_t*>(src);
     for (int i = lane; i < nvalid * (kQ4Bytes / 2); i += kWave) sv[i] = s2[i];
   }
   __syncthreads();                      // every wave reaches this point
-  const int bl = lane / kLPB;           // block of the wave
   const int i0 = kWPL * (lane % kLPB);  // first weight of the lane in its block
-  if (bl >= nvalid) return;
-  const uint16_t* st = reinterpret_cast<const uint16_t*>(stage[wv] + kQ4Bytes * bl);
-  const float d = static_cast<float>(__builtin_bit_cast(_Float16, st[0]));
   // code bytes (i0 mod 16) .. + WPL - 1 of the block: low nibbles for the
   // first 16 weights, high nibbles for the last 16
   const int b0 = i0 & 15;
   const int sh = i0 < 16 ? 0 : 4;
-  float v[kWPL];
+#pragma unroll 4
+  for (int r = 0; r < kRounds; ++r) {
+    const int bl = kBPR * r + lane / kLPB;   // block of the wave
+    if (bl >= nvalid) break;
+    const uint16_t* st = reinterpret_cast<const uint16_t*>(stage[wv] + kQ4Bytes * bl);
+    const float d = static_cast<float>(__builtin_bit_cast(_Float16, st[0]));
+    float v[kWPL];
 #pragma unroll
-  for (int h = 0; h < kWPL / 2; ++h) {
-    const uint32_t two = st[1 + (b0 >> 1) + h];        // bytes b0 + 2h, b0 + 2h + 1 (b0 is even)
-    v[2 * h] = static_cast<float>(static_cast<int>((two >> sh) & 15u) - 8) * d;
-    v[2 * h + 1] = static_cast<float>(static_cast<int>((two >> (8 + sh)) & 15u) - 8) * d;
-  }
-  const int64_t g = g0 + bl;
-  if constexpr (OUT_BF16) {
-    u32x4 q;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const bf16x2_t p = {static_cast<__bf16>(v[2 * i]), static_cast<__bf16>(v[2 * i + 1])};
-      q[i] = __builtin_bit_cast(uint32_t, p);
+    for (int h = 0; h < kWPL / 2; ++h) {
+      const uint32_t two = st[1 + (b0 >> 1) + h];        // bytes b0 + 2h, b0 + 2h + 1 (b0 is even)
+      v[2 * h] = static_cast<float>(static_cast<int>((two >> sh) & 15u) - 8) * d;
+      v[2 * h + 1] = static_cast<float>(static_cast<int>((two >> (8 + sh)) & 15u) - 8) * d;
     }
-    __builtin_nontemporal_store(q, reinterpret_cast<u32x4*>(static_cast<uint16_t*>(out) + g * kQ4Block + i0));
-  } else {
-    __builtin_nontemporal_store(f32x4_t{v[0], v[1], v[2], v[3]},
-                                reinterpret_cast<f32x4_t*>(static_cast<float*>(out) + g * kQ4Block + i0));
+    const int64_t g = g0 + bl;
+    if constexpr (OUT_BF16) {
+      u32x4 q;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const bf16x2_t p = {static_cast<__bf16>(v[2 * i]), static_cast<__bf16>(v[2 * i + 1])};
+        q[i] = __builtin_bit_cast(uint32_t, p);
+      }
+      __builtin_nontemporal_store(q, reinterpret_cast<u32x4*>(static_cast<uint16_t*>(out) + g * kQ4Block + i0));
+    } else {
+      __builtin_nontemporal_store(f32x4_t{v[0], v[1], v[2], v[3]},
+                                  reinterpret_cast<f32x4_t*>(static_cast<float*>(out) + g * kQ4Block + i0));
+    }
   }
 }
 
@@ -291,7 +303,7 @@ hipError_t launch_q4_0_quantize(const void* w, bool bf16, int64_t N, int64_t K, 
 
 hipError_t launch_q4_0_dequantize(const uint8_t* blocks, int64_t N, int64_t K, void* out, bool bf16, hipStream_t s) {
   const int64_t nb = N * (K / kQ4Block);
-  const int64_t per_wg = (kFThreads / kWave) * (bf16 ? 16 : 8);     // blocks per workgroup
+  const int64_t per_wg = (kFThreads / kWave) * kQ4DeqBlocks;       // blocks per workgroup
   const dim3 grid(static_cast<uint32_t>((nb + per_wg - 1) / per_wg));
   if (bf16) q4_0_dequantize_kernel<true><<<grid, dim3(kFThreads), 0, s>>>(blocks, nb, out);
   else q4_0_dequantize_kernel<false><<<grid, dim3(kFThreads), 0, s>>>(blocks, nb, out);
