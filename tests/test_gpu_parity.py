@@ -318,6 +318,36 @@ def test_act_order_with_unused_groups():
         _check_codec(w, G, mode, g_idx, label=f"unused groups {mode}")
 
 
+@pytest.mark.parametrize("G", [-1, 128])
+def test_act_order_one_group_per_row(G):
+    """A g_idx putting every column in group 0 with one group per row
+    (per-channel, or G >= K): the codec, then the linear through the decode,
+    batched and prefill paths."""
+    N, K = 40, 100
+    g = torch.Generator().manual_seed(11)
+    w = torch.randn(N, K, generator=g) * 0.02
+    g_idx = torch.zeros(K, dtype=torch.int32)
+    for mode in ("sym", "asym"):
+        c, s, z, orc = _check_codec(w, G, mode, g_idx, label=f"one group G{G} {mode}")
+        for M in (1, 8, 40):
+            x = torch.randn(M, K, generator=g).to(torch.bfloat16)
+            _check_linear(x, c, s, z, g_idx, K, G, mode, None, orc, f"one group G{G} {mode} M{M}")
+
+
+def test_act_order_uneven_groups_linear():
+    """A g_idx leaving some groups empty and others double size, through the
+    linear at decode, batched and prefill sizes."""
+    N, K, G = 24, 64, 16
+    g = torch.Generator().manual_seed(12)
+    w = torch.randn(N, K, generator=g) * 0.02
+    g_idx = torch.tensor([0, 3] * (K // 2), dtype=torch.int32)
+    for mode in ("sym", "asym"):
+        c, s, z, orc = _check_codec(w, G, mode, g_idx, label=f"uneven {mode}")
+        for M in (1, 8, 40):
+            x = torch.randn(M, K, generator=g).to(torch.bfloat16)
+            _check_linear(x, c, s, z, g_idx, K, G, mode, None, orc, f"uneven {mode} M{M}")
+
+
 @pytest.mark.parametrize("M,K,G,mode", [(16, 256, 32, "asym"), (4, 512, 128, "sym"), (1, 96, 32, "asym"),
                                         (7, 100, 8, "sym"), (256, 256, 64, "asym"), (96, 96, 32, "sym"),
                                         (130, 1024, 256, "asym"), (200, 512, 32, "sym"), (48, 640, -1, "sym")])
