@@ -251,6 +251,22 @@ __global__ __launch_bounds__(kGThreads) void dequantize_t_kernel(DequantArgs a, 
   const int K = static_cast<int>(a.K);
   const int64_t KB = (a.K + 1) / 2;
   const int rows = static_cast<int>(min(static_cast<int64_t>(kTT), a.N - n0));
+  // this thread's 8 code bytes (16 columns of one row), issued before the
+  // tables are staged so that both latencies overlap
+  const int nl = threadIdx.x >> 2, kq = (threadIdx.x & 3) * 16;
+  const int kb = k0 + kq;                          // first of this thread's 16 columns
+  uint32_t d[2] = {0u, 0u};
+  if (nl < rows) {
+    const int64_t n = n0 + nl;
+    if (kb + 16 <= K && (KB & 3) == 0) {
+      const uint32_t* src = reinterpret_cast<const uint32_t*>(a.codes + n * KB + kb / 2);
+      d[0] = src[0];
+      d[1] = src[1];
+    } else {
+      for (int b = 0; b < 8; ++b)
+        if (kb + 2 * b < K) d[b >> 2] |= static_cast<uint32_t>(a.codes[n * KB + kb / 2 + b]) << (8 * (b & 3));
+    }
+  }
   for (int e = threadIdx.x; e < kTT; e += kGThreads) {
     const int k = min(k0 + e, K - 1);
     gsh[e] = GIDX ? min(max(a.g_idx[k], 0), NG - 1) : k / static_cast<int>(a.G);
@@ -264,19 +280,8 @@ __global__ __launch_bounds__(kGThreads) void dequantize_t_kernel(DequantArgs a, 
   }
   __syncthreads();
   {
-    const int nl = threadIdx.x >> 2, kq = (threadIdx.x & 3) * 16;
     if (nl < rows) {
       const int64_t n = n0 + nl;
-      const int kb = k0 + kq;                          // first of this thread's 16 columns
-      uint32_t d[2] = {0u, 0u};
-      if (kb + 16 <= K && (KB & 3) == 0) {
-        const uint32_t* src = reinterpret_cast<const uint32_t*>(a.codes + n * KB + kb / 2);
-        d[0] = src[0];
-        d[1] = src[1];
-      } else {
-        for (int b = 0; b < 8; ++b)
-          if (kb + 2 * b < K) d[b >> 2] |= static_cast<uint32_t>(a.codes[n * KB + kb / 2 + b]) << (8 * (b & 3));
-      }
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         const uint32_t nib = (d[e >> 3] >> (4 * (e & 7))) & 15u;
@@ -302,8 +307,7 @@ __global__ __launch_bounds__(kGThreads) void dequantize_t_kernel(DequantArgs a, 
         for (int h = 0; h < 2; ++h)
 #pragma unroll
           for (int i = 0; i < 4; ++i)
-            q[h][i] = static_cast<uint32_t>(tile[kl][nq + 8 * h + 2 * i]) |
-                      (static_cast<uint32_t>(tile[kl][nq + 8 * h + 2 * i + 1]) << 16);
+            q[h][i] = *reinterpret_cast<const uint32_t*>(&tile[kl][nq + 8 * h + 2 * i]);   // 4-byte aligned pair
         reinterpret_cast<u32x4*>(dst)[0] = q[0];
         reinterpret_cast<u32x4*>(dst)[1] = q[1];
       } else {
