@@ -10,10 +10,10 @@
 // when d is 0.
 //
 // The blocks of an [N, K] weight (K a multiple of 32) form one flat array:
-// block g covers weights 32 g .. 32 g + 31 and bytes 18 g .. 18 g + 17.  A
-// lane owns one block; a wave's 64 blocks are 1152 contiguous, 16-byte
-// aligned bytes, so the wave moves them through LDS and reads or writes them
-// as 72 coalesced 16-byte chunks.
+// block g covers weights 32 g .. 32 g + 31 and bytes 18 g .. 18 g + 17.  The
+// quantizer gives a lane one block; a wave's 64 blocks are 1152 contiguous,
+// 16-byte aligned bytes, written through LDS as 72 coalesced 16-byte chunks.
+// The dequantizer reads a wave's 128 blocks (2304 bytes) the same way.
 //
 // Packed zero-points: two per byte along the row, group 2j in the low nibble
 // (the codes' order), an odd group count leaving the last high nibble 0.
