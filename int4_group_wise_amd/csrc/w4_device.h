@@ -83,6 +83,35 @@ __device__ __forceinline__ float group_max_t(float m) {
   return m;
 }
 
+// fp32(x / D) for x >= 0 without the IEEE division sequence: q0 = fp32(x r)
+// with r = fp32(1 / D), then one residual step q = fp32(q0 + fp32(x - q0 D) r)
+// (both fused multiply-adds).  For D = 7 and D = 15 this is the correctly
+// rounded quotient for every finite x >= 0, subnormals included (checked over
+// all of them): the binary expansion of x / D is periodic, so the quotient
+// never lies close enough to a rounding boundary for the single residual step
+// to land on the wrong side.  x = +inf is passed through (the residual would
+// be NaN).
+template <int D>
+__device__ __forceinline__ float div_const(float x) {
+  static_assert(D == 7 || D == 15, "exactness is established for 7 and 15 only");
+  constexpr float r = 1.0f / static_cast<float>(D);
+  const float q0 = x * r;
+  const float e = __builtin_fmaf(-q0, static_cast<float>(D), x);
+  const float q = __builtin_fmaf(e, r, q0);
+  return x < __builtin_inff() ? q : x;
+}
+
+// rint(fp32(x / s)) for 0 <= x <= 15 s (1 + 2^-23): the reciprocal estimate
+// decides unless the quotient is near a half-integer or rcp(s) is not finite,
+// as for the weights
+__device__ __forceinline__ float rint_quotient(float x, float s) {
+  const float rc = __builtin_amdgcn_rcpf(s);
+  const float t = x * rc;
+  float q = rintf(t);
+  if (!(fabsf(t - q) < kTieMargin) || !(rc < __builtin_inff())) q = rintf(x / s);
+  return q;
+}
+
 // LPG > 0: the group is LPG lanes wide (compile time); LPG == 0: lpg lanes
 template <bool ASYM, int LPG = 0>
 __device__ __forceinline__ void group_scale(const float v[8], int lpg, float& sc, float& zf) {
@@ -105,11 +134,11 @@ __device__ __forceinline__ void group_scale(const float v[8], int lpg, float& sc
   }
   zf = 8.0f;
   if constexpr (ASYM) {
-    sc = (m1 + m2) / 15.0f;
+    sc = div_const<15>(m1 + m2);
     if (sc == 0.0f) sc = 1.0f;
-    zf = fminf(fmaxf(rintf(m2 / sc), 0.0f), 15.0f);
+    zf = fminf(fmaxf(rint_quotient(m2, sc), 0.0f), 15.0f);
   } else {
-    sc = m1 / 7.0f;
+    sc = div_const<7>(m1);
     if (sc == 0.0f) sc = 1.0f;
   }
 }

@@ -86,7 +86,7 @@ __global__ __launch_bounds__(kFThreads) void q4_0_quantize_kernel(const void* __
   float amax = 0.0f;
 #pragma unroll
   for (int i = 0; i < kQ4Block; ++i) amax = fmaxf(amax, fabsf(v[i]));
-  const _Float16 d16 = static_cast<_Float16>(amax / 7.0f);      // round to nearest even
+  const _Float16 d16 = static_cast<_Float16>(div_const<7>(amax));      // round to nearest even
   const float d = static_cast<float>(d16);
 
   // codes: rint(w / d) through the reciprocal with the exact redo near

@@ -165,6 +165,31 @@ __device__ __forceinline__ void use_slice(const Slice& s, const XSlice<MT>& x, b
   }
 }
 
+// Wave sums of four values per lane (one per weight row of the wave), all in
+// VALU cross-lane operations: a 32-lane swap pairs rows 0/2 and 1/3 across the
+// wave halves, a 16-lane swap leaves the partial sums of row r in lanes
+// 16r .. 16r + 15, and four DPP steps (rotate by 8 and 4 within the 16-lane
+// row, then the two quad swaps) finish every row.  Lane l returns the total of
+// row l / 16.  The order of the additions is fixed.
+template <int CTRL>
+__device__ __forceinline__ float dpp_add(float v) {
+  return v + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+
+__device__ __forceinline__ float wave_sum4(float t0, float t1, float t2, float t3) {
+  const auto a02 = __builtin_amdgcn_permlane32_swap(__float_as_uint(t0), __float_as_uint(t2), false, false);
+  const auto a13 = __builtin_amdgcn_permlane32_swap(__float_as_uint(t1), __float_as_uint(t3), false, false);
+  const float s02 = __uint_as_float(a02[0]) + __uint_as_float(a02[1]);   // lanes 0-31: row 0, 32-63: row 2
+  const float s13 = __uint_as_float(a13[0]) + __uint_as_float(a13[1]);   // lanes 0-31: row 1, 32-63: row 3
+  const auto q = __builtin_amdgcn_permlane16_swap(__float_as_uint(s02), __float_as_uint(s13), false, false);
+  float v = __uint_as_float(q[0]) + __uint_as_float(q[1]);               // lanes 16r..16r+15: row r
+  v = dpp_add<0x128>(v);   // row_ror:8
+  v = dpp_add<0x124>(v);   // row_ror:4
+  v = dpp_add<0x4E>(v);    // quad_perm [2, 3, 0, 1]
+  v = dpp_add<0xB1>(v);    // quad_perm [1, 0, 3, 2]
+  return v;
+}
+
 // Each round covers two 2048-column chunks.  A lane first issues the loads of
 // its activations (L2-resident), then the code words, scales and zero-points
 // of both chunks (HBM); loads retire in order, so re-pairing the activations
@@ -186,6 +211,16 @@ __global__ __launch_bounds__(kGemvWaves * kWave) void gemv_dot2_kernel(LinearArg
   for (int r = 0; r < kGemvRows; ++r)
 #pragma unroll
     for (int m = 0; m < MT; ++m) tot[r][m] = 0.0f;
+
+  // lane l ends up with the sum of row row0 + l / 16: its bias is loaded first,
+  // so that the epilogue does not wait for a global load.  The load is
+  // unconditional (without a bias it reads x[0] and the value is dropped): a
+  // branch around it would end the block and wait for the load right there.
+  static_assert(kGemvRows == 4, "wave_sum4 reduces four rows");
+  const int64_t n_out = row0 + (lane >> 4);
+  const uint16_t* bsrc = a.bias ? a.bias + min(n_out, a.N - 1) : a.x;
+  const uint32_t braw = *bsrc;   // converted in the epilogue
+  __builtin_amdgcn_sched_barrier(0);
 
   // Slices past the row end (K not a multiple of 4096) load the last slice
   // again and are discarded, so the loads need no branches: a branch would
@@ -211,16 +246,11 @@ __global__ __launch_bounds__(kGemvWaves * kWave) void gemv_dot2_kernel(LinearArg
   }
 
 #pragma unroll
-  for (int r = 0; r < kGemvRows; ++r) {
-#pragma unroll
-    for (int m = 0; m < MT; ++m) {
-      const float v = wave_sum(tot[r][m]);
-      const int64_t n = row0 + r;
-      if (lane == 0 && n < a.N && m < M) {
-        const float b = a.bias ? bf16_to_f32(a.bias[n]) : 0.0f;
-        a.y[static_cast<int64_t>(m) * a.N + n] = static_cast<uint16_t>(f32_to_bf16(v + b));
-      }
-    }
+  for (int m = 0; m < MT; ++m) {
+    const float v = wave_sum4(tot[0][m], tot[1][m], tot[2][m], tot[3][m]);
+    const float bias = a.bias ? bf16_to_f32(braw) : 0.0f;
+    if ((lane & 15) == 0 && n_out < a.N && m < M)
+      a.y[static_cast<int64_t>(m) * a.N + n_out] = static_cast<uint16_t>(f32_to_bf16(v + bias));
   }
 }
 
