@@ -704,6 +704,7 @@ __device__ __forceinline__ void dequantize_row(const DequantArgs& a, int64_t n, 
   const int lane = lane_id();
   const int wave = threadIdx.x / kWave;
   constexpr int kWaves = kDThreads / kWave;
+  const uint32_t bmask = byte_nibble_mask();
 
   for (int B = 63 * wave; B < J; B += 63 * kWaves) {
     const int i = B + lane - 1;
@@ -725,7 +726,7 @@ __device__ __forceinline__ void dequantize_row(const DequantArgs& a, int64_t n, 
     float o[8];
     if constexpr (ASYM) {
       const float z = static_cast<float>(zrow[g]);
-      const uint32_t lo = d & 0x0F0F0F0Fu, hi = (d >> 4) & 0x0F0F0F0Fu;
+      const uint32_t lo = d & bmask, hi = (d >> 4) & bmask;
 #pragma unroll
       for (int e = 0; e < 8; ++e)
         o[e] = (static_cast<float>((((e & 1) ? hi : lo) >> (8 * (e >> 1))) & 0xFFu) - z) * s;
@@ -733,7 +734,7 @@ __device__ __forceinline__ void dequantize_row(const DequantArgs& a, int64_t n, 
       // u = q + 8 in [0, 15]; fma(u, s, -8 s) rounds (u - 8) s once, as the
       // plain product does (-8 s is exact unless it overflows)
       d ^= 0x88888888u;
-      const uint32_t lo = d & 0x0F0F0F0Fu, hi = (d >> 4) & 0x0F0F0F0Fu;
+      const uint32_t lo = d & bmask, hi = (d >> 4) & bmask;
       const float m8 = -8.0f * s;
       if (fabsf(m8) < __builtin_inff()) {
 #pragma unroll

@@ -39,6 +39,16 @@ __device__ __forceinline__ float wave_sum(float v) {
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
 
+// 0x0F0F0F0F in a VGPR, hidden from the compiler.  After `d & 0x0F0F0F0F`
+// with the constant it knows every byte's high nibble is zero and extracts
+// bytes 1..3 with v_bfe_u32 before converting; with the mask in a register
+// each byte converts with one v_cvt_f32_ubyte{0..3}.  Read by VALU ops only.
+__device__ __forceinline__ uint32_t byte_nibble_mask() {
+  uint32_t r;
+  asm volatile("v_mov_b32 %0, 0x0F0F0F0F" : "=v"(r));
+  return r;
+}
+
 // ---------------------------------------------------------------------------
 // Group-wise quantization of one lane's chunk of 8 values (columns 8j ..
 // 8j+7); columns past the row end must hold 0 and cnt is the number of valid

@@ -65,6 +65,7 @@ __global__ __launch_bounds__(kGThreads) void grad_split_kernel(GradArgs a, int r
   for (int e = 0; e < kNGrp; ++e)
     g[e] = GIDX ? min(max(a.g_idx[min(kc + e, K - 1)], 0), NG - 1) : kc / static_cast<int>(a.G);
   const bool aligned = cnt == CPT && (KB & 3) == 0;
+  const uint32_t bmask = byte_nibble_mask();
 
   float acc[MT][CPT];
   float corr[MT];                                     // sum over rows of c z (contiguous groups)
@@ -142,7 +143,7 @@ __global__ __launch_bounds__(kGThreads) void grad_split_kernel(GradArgs a, int r
 #pragma unroll
         for (int i = 0; i < kW; ++i) {
           const uint32_t dd = ASYM ? d[u][i] : (d[u][i] ^ 0x88888888u);   // signed q -> q + 8
-          const uint32_t lo = dd & 0x0F0F0F0Fu, hi = (dd >> 4) & 0x0F0F0F0Fu;
+          const uint32_t lo = dd & bmask, hi = (dd >> 4) & bmask;
 #pragma unroll
           for (int b = 0; b < 4; ++b) {
             const float qe = static_cast<float>((lo >> (8 * b)) & 0xFFu);     // column 8i + 2b
