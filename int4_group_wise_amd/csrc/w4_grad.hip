@@ -37,9 +37,28 @@ constexpr int grad_unroll() { return !GIDX && MT * CPT <= 32 ? 16 : 8; }
 template <int MT, bool WIDE>
 constexpr int grad_cpt() { return WIDE && MT <= 4 ? 32 : 8; }
 
+// dy[i] for a wave-uniform index i, read through the scalar cache as the
+// aligned dword that holds it (that dword never crosses a page boundary the
+// element itself does not, so it stays inside mapped memory)
+__device__ __forceinline__ uint32_t load_bf16_uniform(const uint16_t* p, int64_t i) {
+  // offsets from the original pointer keep the access in the global address space
+  const uint8_t* pb = reinterpret_cast<const uint8_t*>(p);
+  const int64_t mis = static_cast<int64_t>(reinterpret_cast<uintptr_t>(pb) & 3);
+  const int64_t off = mis + 2 * i;                     // byte offset from the aligned base
+  const uint32_t word = *reinterpret_cast<const uint32_t*>(pb - mis + (off & ~static_cast<int64_t>(3)));
+  return (off & 2) ? (word >> 16) : (word & 0xFFFFu);
+}
+
+// The four waves' sums meet in LDS in one step (all four buffers at once, 32 KB
+// for 32 values per lane) when the buffers fit in 32 KB, else one buffer at a time.
+template <int MT, int CPT>
+constexpr bool grad_parallel_sum() { return kGWaves * MT * CPT * kWave * 4 <= 32768 && CPT % (4 * kGWaves) == 0; }
+
 // One workgroup: 64 * CPT columns of dx (lane l owns columns CPT l ..), one
 // slice of rows of W; wave w takes rows w, w + 4, ... of the slice.  The 4
-// waves' sums are added through LDS and wave 0 writes the slice's partial.
+// waves' sums are added through LDS in wave order and written as the slice's
+// partial (by all four waves, a quarter of the columns each, when the four
+// buffers fit; else by wave 0).
 template <bool ASYM, bool GIDX, int MT, int CPT>
 __global__ __launch_bounds__(kGThreads) void grad_split_kernel(GradArgs a, int rows_per) {
   extern __shared__ __attribute__((aligned(16))) float gsm[];
@@ -81,6 +100,7 @@ __global__ __launch_bounds__(kGThreads) void grad_split_kernel(GradArgs a, int r
     uint32_t d[kGUnroll][kW];
     float s[kGUnroll][kNGrp];
     float z[kGUnroll][kNGrp];
+    uint32_t dyr[kGUnroll][MT];   // raw bf16 dy of the block's rows
     // loads of this wave's next kGUnroll rows first (past the slice: reload the last)
 #pragma unroll
     for (int u = 0; u < kGUnroll; ++u) {
@@ -107,6 +127,8 @@ __global__ __launch_bounds__(kGThreads) void grad_split_kernel(GradArgs a, int r
         s[u][e] = a.scales[n * NG + g[e]];
         z[u][e] = ASYM ? static_cast<float>(a.zeros[n * NG + g[e]]) : 8.0f;
       }
+#pragma unroll
+      for (int m = 0; m < MT; ++m) dyr[u][m] = load_bf16_uniform(a.dy, static_cast<int64_t>(min(m, M - 1)) * a.N + n);
     }
 #pragma unroll
     for (int u = 0; u < kGUnroll; ++u) {
@@ -117,7 +139,7 @@ __global__ __launch_bounds__(kGThreads) void grad_split_kernel(GradArgs a, int r
       float dm[MT];
 #pragma unroll
       for (int m = 0; m < MT; ++m) {
-        const float dv = bf16_to_f32(a.dy[static_cast<int64_t>(min(m, M - 1)) * a.N + min(n, ne - 1)]);
+        const float dv = bf16_to_f32(dyr[u][m]);
         dm[m] = valid && m < M ? dv : 0.0f;
       }
       if constexpr (GIDX) {
@@ -165,8 +187,43 @@ __global__ __launch_bounds__(kGThreads) void grad_split_kernel(GradArgs a, int r
       for (int e = 0; e < CPT; ++e) acc[m][e] -= corr[m];
   }
 
-  // add the 4 waves' sums (waves 1..3 in turn through one buffer: register
-  // order [m][e], lane-major so the accesses are unit-stride)
+  // add the 4 waves' sums in wave order 0..3 (the same order either way)
+  float* part = a.partial + static_cast<int64_t>(blockIdx.y) * M * a.K;
+  if constexpr (grad_parallel_sum<MT, CPT>()) {
+    // every wave stores its sums (register order [m][e], lane-major so the
+    // accesses are unit-stride), then wave w adds columns e of its quarter
+    // over the four waves and writes them
+#pragma unroll
+    for (int m = 0; m < MT; ++m)
+#pragma unroll
+      for (int e = 0; e < CPT; ++e) gsm[((w * MT + m) * CPT + e) * kWave + lane] = acc[m][e];
+    __syncthreads();
+    if (!live) return;
+    constexpr int kQ = CPT / kGWaves;                 // columns per wave
+#pragma unroll
+    for (int m = 0; m < MT; ++m) {
+      if (m >= M) continue;
+      float t[kQ];
+#pragma unroll
+      for (int i = 0; i < kQ; ++i) {
+        const int e = w * kQ + i;
+        t[i] = gsm[((0 * MT + m) * CPT + e) * kWave + lane];
+#pragma unroll
+        for (int src = 1; src < kGWaves; ++src) t[i] += gsm[((src * MT + m) * CPT + e) * kWave + lane];
+      }
+      float* dst = part + static_cast<int64_t>(m) * a.K + k0 + w * kQ;
+      if (cnt == CPT && (a.K & 3) == 0) {
+#pragma unroll
+        for (int q = 0; q < kQ / 4; ++q) reinterpret_cast<f32x4_t*>(dst)[q] = f32x4_t{t[4 * q], t[4 * q + 1], t[4 * q + 2], t[4 * q + 3]};
+      } else {
+#pragma unroll
+        for (int i = 0; i < kQ; ++i)
+          if (w * kQ + i < cnt) dst[i] = t[i];
+      }
+    }
+    return;
+  }
+  // larger tiles: waves 1..3 in turn through one buffer
   for (int src = 1; src < kGWaves; ++src) {
     if (w == src) {
 #pragma unroll
@@ -184,7 +241,6 @@ __global__ __launch_bounds__(kGThreads) void grad_split_kernel(GradArgs a, int r
     __syncthreads();
   }
   if (w != 0 || !live) return;
-  float* part = a.partial + static_cast<int64_t>(blockIdx.y) * M * a.K;
 #pragma unroll
   for (int m = 0; m < MT; ++m) {
     if (m >= M) continue;
@@ -322,7 +378,7 @@ __global__ __launch_bounds__(kGThreads) void dequantize_t_kernel(DequantArgs a, 
 template <bool ASYM, bool GIDX, int MT, int CPT>
 hipError_t launch_split4(const GradArgs& a, int P, int rows_per, hipStream_t s) {
   const dim3 grid(static_cast<uint32_t>((a.K + kWave * CPT - 1) / (kWave * CPT)), static_cast<uint32_t>(P));
-  const size_t lds = static_cast<size_t>(MT) * CPT * kWave * sizeof(float);
+  const size_t lds = static_cast<size_t>(grad_parallel_sum<MT, CPT>() ? kGWaves : 1) * MT * CPT * kWave * sizeof(float);
   grad_split_kernel<ASYM, GIDX, MT, CPT><<<grid, dim3(kGThreads), lds, s>>>(a, rows_per);
   return hipGetLastError();
 }
