@@ -703,17 +703,24 @@ __device__ __forceinline__ void rows_compute(const LinearArgs& a, int b, int nkb
       }
 #pragma unroll
       for (int gi = 0; gi < GU; ++gi) {
-        const int col = 128 * (kbf + j) + (128 / GU) * gi;
-        const int gg = col / static_cast<int>(G) - g_first;
+        // table index of the group: G = 128 / GU for GU > 1, so the batch's
+        // groups start at g_first = GU kbf and this one is GU j + gi
+        int gg;
+        if constexpr (GU > 1) {
+          gg = GU * j + gi;
+        } else {
+          gg = (128 * (kbf + j)) / static_cast<int>(G) - g_first;
+        }
         const float sc = stab[n * kRowsTS + gg];
-        const float zo = 128.0f + static_cast<float>(ztab[n * kRowsTS + gg]);
+        // 128 + zero-point (signed codes: 128 + 8)
+        const float zo = ASYM ? 128.0f + static_cast<float>(ztab[n * kRowsTS + gg]) : 136.0f;
         const int u0 = 4 * j + gi * (4 / GU);
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
           const int m = 4 * q + t;                    // output row of acc[gi][t]
-          float sx = 0.0f;
+          float sx = xs[m * (kRowsKB * 4) + (u0 ^ xs_swz(m))];
 #pragma unroll
-          for (int uu = 0; uu < 4 / GU; ++uu) sx += xs[m * (kRowsKB * 4) + ((u0 + uu) ^ xs_swz(m))];
+          for (int uu = 1; uu < 4 / GU; ++uu) sx += xs[m * (kRowsKB * 4) + ((u0 + uu) ^ xs_swz(m))];
           out[t] += sc * (acc[gi][t] - zo * sx);
         }
       }
