@@ -33,7 +33,7 @@ __device__ __forceinline__ uint32_t perm(uint32_t hi, uint32_t lo, uint32_t sel)
   return __builtin_amdgcn_perm(hi, lo, sel);
 }
 
-constexpr int kGemvWaves = 4;   // waves per workgroup
+constexpr int kGemvWaves = 2;   // waves per workgroup (2, 4, 8, 16 measured: 2 best by ~1.5%)
 constexpr int kGemvRows = 4;    // weight rows per wave
 
 // x values of 8 consecutive columns c0..c0+7 (4 dwords of bf16 pairs) are
