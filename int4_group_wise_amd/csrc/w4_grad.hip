@@ -295,14 +295,19 @@ __global__ __launch_bounds__(kRParts * kWave) void grad_reduce_kernel(const floa
 // row, and the bf16 values go through an LDS tile (rows padded by 2 bytes)
 // to be written out as rows of wt.
 constexpr int kTT = 64;
+// row strides of the staged tables: an odd number of 4-byte words, so that
+// the 16 rows one wave reads at a time fall on distinct LDS banks
+__host__ __device__ inline int tstab_stride(int64_t NG) { return static_cast<int>(NG | 1); }                   // floats
+__host__ __device__ inline int tztab_stride(int64_t NG) { return 4 * static_cast<int>(((NG + 3) / 4) | 1); }  // bytes
 template <bool ASYM, bool GIDX, bool TAB>
 __global__ __launch_bounds__(kGThreads) void dequantize_t_kernel(DequantArgs a, uint16_t* __restrict__ wt) {
   extern __shared__ __attribute__((aligned(16))) uint8_t tsm[];
   uint16_t (*tile)[kTT + 2] = reinterpret_cast<uint16_t (*)[kTT + 2]>(tsm);     // [k][n]
   int* gsh = reinterpret_cast<int*>(tsm + kTT * (kTT + 2) * 2);                 // [64] group of column
   const int NG = static_cast<int>(a.NG);
-  float* stab = reinterpret_cast<float*>(gsh + kTT);                            // [64 rows][NG]
-  uint8_t* ztab = reinterpret_cast<uint8_t*>(stab + kTT * NG);                  // [64 rows][NG]
+  const int SS = tstab_stride(NG), ZS = tztab_stride(NG);
+  float* stab = reinterpret_cast<float*>(gsh + kTT);                            // [64 rows][SS]
+  uint8_t* ztab = reinterpret_cast<uint8_t*>(stab + kTT * SS);                  // [64 rows][ZS]
   const int64_t n0 = static_cast<int64_t>(blockIdx.y) * kTT;
   const int k0 = blockIdx.x * kTT;
   const int K = static_cast<int>(a.K);
@@ -330,9 +335,10 @@ __global__ __launch_bounds__(kGThreads) void dequantize_t_kernel(DequantArgs a, 
   }
   if constexpr (TAB) {                             // (else the rows' tables are read from memory)
     for (int e = threadIdx.x; e < rows * NG; e += kGThreads) {
-      const int64_t gi = (n0 + e / NG) * a.NG + e % NG;
-      stab[e] = a.scales[gi];
-      if constexpr (ASYM) ztab[e] = a.zeros[gi];
+      const int r = e / NG, g = e % NG;
+      const int64_t gi = (n0 + r) * a.NG + g;
+      stab[r * SS + g] = a.scales[gi];
+      if constexpr (ASYM) ztab[r * ZS + g] = a.zeros[gi];
     }
   }
   __syncthreads();
@@ -343,8 +349,8 @@ __global__ __launch_bounds__(kGThreads) void dequantize_t_kernel(DequantArgs a, 
       for (int e = 0; e < 16; ++e) {
         const uint32_t nib = (d[e >> 3] >> (4 * (e & 7))) & 15u;
         const int gi = gsh[kq + e];
-        const float sc = TAB ? stab[nl * NG + gi] : a.scales[n * a.NG + gi];
-        const int zp = ASYM ? (TAB ? ztab[nl * NG + gi] : a.zeros[n * a.NG + gi]) : 8;
+        const float sc = TAB ? stab[nl * SS + gi] : a.scales[n * a.NG + gi];
+        const int zp = ASYM ? (TAB ? ztab[nl * ZS + gi] : a.zeros[n * a.NG + gi]) : 8;
         const float val = ASYM ? static_cast<float>(static_cast<int>(nib) - zp)
                                : static_cast<float>(static_cast<int>(nib ^ 8u) - 8);
         tile[kq + e][nl] = static_cast<uint16_t>(f32_to_bf16(val * sc));
@@ -440,7 +446,7 @@ hipError_t launch_grad_input(const GradArgs& a, hipStream_t s) {
   uint16_t* wt = reinterpret_cast<uint16_t*>(a.partial);
   const dim3 grid(static_cast<uint32_t>((a.K + kTT - 1) / kTT), static_cast<uint32_t>((a.N + kTT - 1) / kTT));
   const size_t lds0 = kTT * (kTT + 2) * 2 + kTT * 4;
-  const size_t lds = lds0 + static_cast<size_t>(kTT) * a.NG * 5;
+  const size_t lds = lds0 + static_cast<size_t>(kTT) * (4 * tstab_stride(a.NG) + tztab_stride(a.NG));
   if (lds <= 65536) {
     if (a.asym) {
       if (a.g_idx) dequantize_t_kernel<true, true, true><<<grid, dim3(kGThreads), lds, s>>>(d, wt);
