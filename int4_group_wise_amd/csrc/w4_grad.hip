@@ -345,6 +345,7 @@ __global__ __launch_bounds__(kGThreads) void dequantize_t_kernel(DequantArgs a, 
   {
     if (nl < rows) {
       const int64_t n = n0 + nl;
+      float w[16];
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         const uint32_t nib = (d[e >> 3] >> (4 * (e & 7))) & 15u;
@@ -353,7 +354,15 @@ __global__ __launch_bounds__(kGThreads) void dequantize_t_kernel(DequantArgs a, 
         const int zp = ASYM ? (TAB ? ztab[nl * ZS + gi] : a.zeros[n * a.NG + gi]) : 8;
         const float val = ASYM ? static_cast<float>(static_cast<int>(nib) - zp)
                                : static_cast<float>(static_cast<int>(nib ^ 8u) - 8);
-        tile[kq + e][nl] = static_cast<uint16_t>(f32_to_bf16(val * sc));
+        w[e] = val * sc;
+      }
+      // round to bf16 in pairs (v_cvt_pk_bf16_f32: nearest, ties to even) and
+      // store each half in its own tile row
+#pragma unroll
+      for (int e = 0; e < 16; e += 2) {
+        const uint32_t p = __builtin_bit_cast(uint32_t, bf16x2_t{static_cast<__bf16>(w[e]), static_cast<__bf16>(w[e + 1])});
+        tile[kq + e][nl] = static_cast<uint16_t>(p);
+        tile[kq + e + 1][nl] = static_cast<uint16_t>(p >> 16);
       }
     }
   }
