@@ -131,6 +131,24 @@ __device__ __forceinline__ void lds_dma16(const void* gsrc, void* ldst) {
                                        reinterpret_cast<uintptr_t>(ldst)), 16, 0, 0);
 }
 
+// Tile (row tile tm, column tile tn) of workgroup b.  Workgroups are dealt to
+// the 8 XCDs round-robin (b % 8) and each XCD has its own L2, so when the tile
+// count divides by 8 each XCD's share is made a contiguous run of positions,
+// and positions are walked in groups of 4 row tiles across all column tiles:
+// on a 8 x 32 tile grid every XCD takes a 4 x 8 block (16 MB of operands per
+// L2 instead of 20 MB with row-major order; the GEMM 84.5 -> 83.2 us).
+__device__ __forceinline__ void pipe_tile(int b, int tiles_m, int tiles_n, int& tm, int& tn) {
+  const int nt = tiles_m * tiles_n;
+  const int p = nt % 8 == 0 ? (b % 8) * (nt / 8) + b / 8 : b;
+  constexpr int kGroupM = 4;
+  const int gsz = kGroupM * tiles_n;
+  const int first = (p / gsz) * kGroupM;
+  const int rows = min(kGroupM, tiles_m - first);
+  const int r = p % gsz;
+  tm = first + r % rows;
+  tn = r / rows;
+}
+
 __global__ __launch_bounds__(kThreads) void gemm_bf16_pipe_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ wd,
     const uint16_t* __restrict__ bias, uint16_t* __restrict__ y,
@@ -141,8 +159,10 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_pipe_kernel(
   const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wid >> 1, wn = wid & 1;
   const int tiles_n = (N + PN - 1) / PN;
-  const int m0 = (blockIdx.x / tiles_n) * PM;
-  const int n0 = (blockIdx.x % tiles_n) * PN;
+  int tm, tn;
+  pipe_tile(blockIdx.x, (M + PM - 1) / PM, tiles_n, tm, tn);
+  const int m0 = tm * PM;
+  const int n0 = tn * PN;
 
   // loads: wave wid fills A rows [64 wid, 64 wid + 64) (8 instructions of 8
   // rows) and B rows [32 wid, 32 wid + 32) (4 instructions); lane i of an
