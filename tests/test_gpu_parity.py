@@ -183,6 +183,7 @@ CASES = [
     (33, 64, 1088, 256, "sym", False, "f32", "none"),
     (64, 256, 2048, 128, "asym", False, "bf16", "randn"),
     (300, 520, 512, 128, "sym", False, "f32", "randn"),
+    (1300, 500, 256, 128, "asym", False, "f32", "randn"),  # 6 x 4 GEMM tiles: per-XCD runs, last row group partial
     (96, 80, 1024, -1, "sym", False, "f32", "none"),
     # per-channel (G = -1, or any G >= K): one scale per row
     (1, 40, 100, -1, "sym", False, "f32", "randn"),
