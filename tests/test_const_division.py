@@ -12,9 +12,10 @@ fp32, a double rounding that cannot change the result here: the significand
 of x / D is a multiple of 1 / D away from an integer, so it stays at least
 1 / (2 D) of a unit in the last place (about 2^-28 to 2^-29 relative) from
 every fp32 rounding midpoint, far beyond the ~2^-47 by which q0 + e * r
-differs from x / D (the residual x - q0 * D is exact in fp32).  By default four full binades, the whole subnormal range and the top
-binade are checked (a few seconds); W4_EXHAUSTIVE=1 checks all 2^31 - 2^23
-finite non-negative values (about a minute per divisor).
+differs from x / D (the residual x - q0 * D is exact in fp32).  By default
+four full binades, the whole subnormal range and the top binade are checked
+(a few seconds); W4_EXHAUSTIVE=1 checks all 2^31 - 2^23 finite non-negative
+values (about a minute per divisor).
 """
 import os
 
