@@ -240,9 +240,11 @@ w4_status w4_pack_zeros(const uint8_t* zeros, int64_t N, int64_t NG, uint8_t* pa
 w4_status w4_unpack_zeros(const uint8_t* packed, int64_t N, int64_t NG, uint8_t* zeros, void* stream);
 
 /*
- * w4_q4_0_quantize / w4_q4_0_dequantize — the GGUF Q4_0 block format
+ * w4_q4_0_quantize / w4_q4_0_dequantize — Q4_0 blocks
  * (Modular MAX quantization.py page: QuantizationEncoding Q4_0, 32 weights
- * per block in 2 + 16 bytes, the scale d then the 4-bit codes).
+ * per block in 2 + 16 bytes, the scale d then the 4-bit codes).  The page
+ * fixes only that block size and byte count; the fp16 d, the +8 offset, the
+ * nibble placement and the quantizer below are this library's reading.
  *   Block layout: bytes 0..1 the fp16 scale d (little-endian); byte 2 + i
  *   holds q[i] + 8 in its low nibble and q[i + 16] + 8 in its high nibble;
  *   weight i of the block reads as fp32(q[i] - 8) * d.

@@ -1,10 +1,11 @@
 // Storage formats next to the packed layout:
 //
-// GGUF Q4_0 blocks (Modular MAX quantization.py page: QuantizationEncoding,
-// Q4_0 = 32 weights per block in 2 + 16 bytes, the scale d then 4-bit codes).
+// Q4_0 blocks (Modular MAX quantization.py page: QuantizationEncoding,
+// Q4_0 = 32 weights per block in 2 + 16 bytes, the scale d then 4-bit codes;
+// the page fixes nothing more, so the rest is this library's reading).
 // A block is the fp16 scale d (little-endian) followed by 16 bytes; byte i
-// holds code q[i] + 8 in its low nibble and q[i + 16] + 8 in its high nibble
-// (the GGUF placement); a weight reads as (q - 8) * d.  Quantization is the
+// holds code q[i] + 8 in its low nibble and q[i + 16] + 8 in its high nibble;
+// a weight reads as (q - 8) * d.  Quantization is the
 // signed absmax rule of the packed format taken against the stored scale:
 // d = fp16(fp32(amax / 7)), q = clamp(rint(fp32(w / d)), -7, 7), all codes 0
 // when d is 0.

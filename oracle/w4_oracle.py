@@ -52,12 +52,13 @@ Readings taken where the pages leave a step open:
       weight is quantized again with the layer's group size, mode and g_idx.
   R10 Packed zero-points: the zero-points are 4-bit values, stored two per
       byte with the codes' nibble order (group 2j low, 2j+1 high).
-  R11 GGUF Q4_0 ([MAX] gives only the block: 32 weights in 18 bytes, the
-      scale d then 4-bit codes): d is fp16; codes are stored as q + 8 and
-      read as (q - 8) * d; weight i of a block sits in the low nibble of byte
-      i for i < 16 and in the high nibble of byte i - 16 otherwise (the GGUF
-      layout); the quantizer is the signed group-32 rule R3 taken against the
-      stored fp16 scale.
+  R11 GGUF Q4_0.  [MAX] fixes only the block: 32 weights in 2 + 16 bytes,
+      the scale d then the 4-bit codes.  Everything else is a reading, not
+      the page: d is fp16 (2 bytes, little-endian); codes are stored as
+      q + 8 and read as (q - 8) * d; weight i of a block sits in the low
+      nibble of byte i for i < 16 and in the high nibble of byte i - 16
+      otherwise; the quantizer is the signed group-32 rule R3 taken against
+      the stored fp16 scale.
 """
 from __future__ import annotations
 
@@ -200,35 +201,43 @@ def quantize(w, G: int, mode: str, g_idx=None):
 # pack / unpack ([LoopQ] ``pack_weight``, ``_dequantize_validated``)
 # ---------------------------------------------------------------------------
 def pack_nibbles(q) -> np.ndarray:
-    """Two codes per byte along the row: nibble = q & 15 (two's complement for
-    negative codes); column 2j goes to the low nibble of byte j and column
-    2j+1 to the high nibble; an odd row is padded with a 0 nibble
-    ([LoopQ] ``pack_weight``, nibble order 'even_column_low')."""
+    """Two codes per byte along the row ([LoopQ] ``pack_weight``, nibble
+    order 'even_column_low'; the format, not the listing): a code's nibble is
+    its 4-bit two's-complement pattern (q & 15); byte j of a row holds column
+    2j in bits 0..3 and column 2j+1 in bits 4..7; when K is odd the last
+    byte's bits 4..7 are 0.  Written byte by byte."""
     q = np.asarray(q)
     N, K = q.shape
-    u = (q.astype(np.int16) & 15).astype(np.uint8)
-    if K % 2:
-        u = np.concatenate([u, np.zeros((N, 1), np.uint8)], axis=1)
-    return (u[:, 0::2] | (u[:, 1::2] << 4)).astype(np.uint8)
+    nib = (q.astype(np.int16) & 15).astype(np.uint8)
+    out = np.zeros((N, (K + 1) // 2), dtype=np.uint8)
+    for j in range(out.shape[1]):
+        low = nib[:, 2 * j]
+        high = nib[:, 2 * j + 1] if 2 * j + 1 < K else np.zeros(N, np.uint8)
+        out[:, j] = low | (high << np.uint8(4))
+    return out
 
 
 def unpack_nibbles(codes, K: int) -> np.ndarray:
-    """Inverse of ``pack_nibbles``: uint8 [N, K] nibble values 0..15
-    ([LoopQ] ``_dequantize_validated``: low nibble first, then slice to
-    width)."""
+    """Inverse of ``pack_nibbles``: uint8 [N, K] nibble values 0..15; column
+    k is bits 0..3 of byte k // 2 for even k and bits 4..7 for odd k
+    ([LoopQ] ``_dequantize_validated``)."""
     c = np.asarray(codes, dtype=np.uint8)
     N = c.shape[0]
-    pairs = np.stack([c & 15, c >> 4], axis=-1).reshape(N, -1)
-    return pairs[:, :K].astype(np.uint8)
+    out = np.zeros((N, K), dtype=np.uint8)
+    for k in range(K):
+        byte = c[:, k // 2]
+        out[:, k] = (byte >> np.uint8(4)) if k % 2 else (byte & np.uint8(15))
+    return out
 
 
 def decode(u, mode: str, zeros=None, gid=None) -> np.ndarray:
-    """Integer value of each nibble.  Sym: two's complement, v = u - 16 for
-    u >= 8 ([LoopQ] ``_dequantize_validated``).  Asym: v = u - z[n, gid(k)]
-    (R4), exact in integers."""
+    """Integer value of each nibble.  Sym: 4-bit two's complement, bit 3
+    weighs -8 and bits 0..2 weigh 4, 2, 1 ([LoopQ] ``_dequantize_validated``:
+    values from 8 up read as negative).  Asym: v = u - z[n, gid(k)] (R4),
+    exact in integers."""
     u = np.asarray(u).astype(np.int32)
     if mode == SYM:
-        return np.where(u >= 8, u - 16, u)
+        return -8 * ((u >> 3) & 1) + (u & 7)
     return u - np.asarray(zeros).astype(np.int32)[:, gid]
 
 
