@@ -180,14 +180,16 @@ __device__ __forceinline__ void quant8_redo(const float v[8], float sc, float qf
   }
 }
 
-// unsigned nibbles as bytes: q + z (zero-point), or q + 8 for signed codes
-// (|w| <= 7 s there, so q is already in [-7, 7]; flipped back below)
+// unsigned nibbles as bytes: clamp(q + z, 0, 15) (zero-point), or
+// clamp(q, -7, 7) + 8 for signed codes, flipped back below.  The signed clamp
+// acts only when the scale is subnormal: amax / 7 then rounds with a large
+// relative error (amax = 17 * 2^-149 gives s = 2 * 2^-149 and a quotient 8.5)
 template <bool ASYM>
 __device__ __forceinline__ uint32_t pack8(const float qf[8], float zf, int cnt) {
   uint32_t ev = 0, od = 0;
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
-    const float x = ASYM ? fminf(fmaxf(qf[e] + zf, 0.0f), 15.0f) : qf[e] + 8.0f;
+    const float x = ASYM ? fminf(fmaxf(qf[e] + zf, 0.0f), 15.0f) : fminf(fmaxf(qf[e], -7.0f), 7.0f) + 8.0f;
     if (e & 1) od = __builtin_amdgcn_cvt_pk_u8_f32(x, e >> 1, od);
     else ev = __builtin_amdgcn_cvt_pk_u8_f32(x, e >> 1, ev);
   }

@@ -294,6 +294,57 @@ def test_codec_degenerate_values():
             _check_codec(x.to(torch.bfloat16), G, mode, label=f"degenerate{lab} bf16 {mode}")
 
 
+def _subnormal_scale_rows(K, G):
+    """fp32 rows whose groups have max|w| = 10 * 2^-149 or 17 * 2^-149: the
+    signed scale amax / 7 is then a subnormal rounded far from the quotient
+    (17 * 2^-149 gives s = 2 * 2^-149 and w / s = 8.5), so only the clamp to
+    [-7, 7] keeps the codes in range."""
+    u = 2.0 ** -149
+    pattern = torch.tensor([17.0, -17.0, 10.0, -10.0, 5.0, 3.0, -1.0, 0.0, 8.0, -9.0, 16.0, 2.0], dtype=torch.float64)
+    rows = []
+    for amax in (10.0, 17.0):
+        r = pattern.clamp(-amax, amax).repeat(-(-K // len(pattern)))[:K].clone()
+        r[::G] = amax                                        # every group reaches amax
+        rows += [r, -r, r.roll(5)]
+    return (torch.stack(rows) * u).to(torch.float32)
+
+
+def test_codec_subnormal_scale_clamp():
+    """Regression: signed codes stay in [-7, 7] when the group scale is a
+    subnormal (the fast row quantizer, the general one, and act-order)."""
+    for K, G in ((64, 32), (2048, 32), (4096, 128), (72, 8)):
+        w = _subnormal_scale_rows(K, G)
+        assert w.abs().max().item() > 0 and w.abs().max().item() < 1e-43
+        _check_codec(w, G, "sym", label=f"subnormal K={K} G={G}")
+        _check_codec(w, G, "asym", label=f"subnormal asym K={K} G={G}")
+    w = _subnormal_scale_rows(1024, 64)
+    g_idx = (torch.randperm(1024, generator=torch.Generator().manual_seed(9)) // 64).to(torch.int32)
+    _check_codec(w, 64, "sym", g_idx=g_idx, label="subnormal act-order")
+
+
+def test_lora_requantize_subnormal_scale_clamp():
+    """Regression: the LoRA merge's requantizer clamps signed codes when the
+    merged weight's group scale is subnormal.  Zero codes plus an update
+    c * A B with c = 2^-140 and A holding multiples of 2^-9 give merged weights
+    that are exact multiples of 2^-149 with max|w| of 10 or 17 units."""
+    N, K, G = 6, 512, 32
+    units = (_subnormal_scale_rows(K, G)[3].double() / 2.0 ** -149).round()   # integers, max |.| = 17
+    A = (units * 2.0 ** -9).to(torch.float32).reshape(K, 1).numpy()
+    B = np.ones((1, N), np.float32)
+    B[0, 1::2] = -1.0
+    oc = np.zeros((N, K // 2), np.uint8)
+    osc = np.ones((N, K // G), np.float32)
+    c, s = torch.from_numpy(oc).to(DEV), torch.from_numpy(osc).to(DEV)
+    scale = 2.0 ** -140
+    c2, s2, _ = w4.lora_merge(c, s, None, None, K, G, "sym", torch.from_numpy(A).to(DEV), torch.from_numpy(B).to(DEV), scale)
+    torch.cuda.synchronize()
+    merged = O.lora_merged_weight(oc, osc, None, None, K, G, O.SYM, A, B, scale)
+    assert np.abs(merged).max() == 17 * 2.0 ** -149
+    ec, es, _ = O.lora_merge(oc, osc, None, None, K, G, O.SYM, A, B, scale)
+    assert np.array_equal(c2.cpu().numpy(), ec), "merged codes differ (subnormal scales)"
+    assert np.array_equal(s2.cpu().numpy().view(np.uint32), es.view(np.uint32)), "merged scales differ (subnormal scales)"
+
+
 @pytest.mark.parametrize("N,K,G,dt,uniform", [(13, 4096, 128, torch.float32, True), (9, 8192, 512, torch.bfloat16, True),
                                                (20, 512, 8, torch.bfloat16, True), (17, 1024, 64, torch.float32, False),
                                                (11, 2048, 256, torch.bfloat16, False)])
