@@ -161,6 +161,11 @@ CASES = [
     (1, 50, 4096, 256, "sym", False, "bf16", "none"),   # staged decode, signed
     (1, 24, 16384, 256, "asym", False, "f32", "randn"), # staged decode, longest row, 64 groups
     (1, 8, 640, 32, "sym", False, "f32", "randn"),      # staged decode, partial round
+    # streaming decode GEMV (M = 1, K = 4096): 2, 4, 8 and 14 rows per wave
+    # pair, a last workgroup with one row set past N, row tails
+    (1, 4097, 4096, 32, "asym", False, "f32", "randn"),
+    (1, 14339, 4096, 64, "sym", False, "f32", "none"),
+    (1, 20001, 4096, 128, "asym", False, "bf16", "randn"),
     (1, 64, 512, 128, "asym", True, "f32", "none"),     # act-order decode
     (16, 48, 1000, 40, "asym", True, "bf16", "none"),
     (17, 130, 200, 8, "asym", False, "f32", "randn"),   # prefill, K % 64 != 0, N tail
