@@ -30,6 +30,7 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 BF16_MFMA_PEAK_TFS = 2516.6    # MI355X dense bf16 matrix cores
 MALL_BYTES = 256 << 20         # Infinity Cache
 FP64_VEC_PEAK_TFS = 78.6       # MI355X fp64 vector
+GPU_LEAD_CYCLES = 200_000      # device-side wait before a timed region (about 0.1 ms)
 
 
 def algorithmic_bytes_linear(M, N, K, G, asym, bias):
@@ -83,6 +84,10 @@ def time_graph(call, n_calls, steps, warmup, rot_count):
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
+    # a short device-side wait ahead of the start event, so that the graph
+    # launches below are already queued when the timed region begins: the
+    # events then time the calls, not the host's first graph submission
+    torch.cuda._sleep(GPU_LEAD_CYCLES)
     e0.record()
     for _ in range(steps // n_calls):
         g.replay()
@@ -133,6 +138,28 @@ def bench_decode_hot(w4, steps=2000):
             "value": round(gbs, 1), "unit": "GB/s", "us_per_call": round(ev_ms * 1e3 / steps, 3),
             "config": {"workload": "decode", "M": wl.M, "N": wl.N, "K": wl.K, "G": wl.G, "mode": wl.mode,
                        "weight_copies_rotated": 1}}
+
+
+def bench_streaming_floor(nbytes, steps=4000):
+    """What one launch of a plain library kernel moving the same number of HBM
+    bytes achieves in this harness: torch's sum and amax reductions over an
+    fp32 buffer of `nbytes` and a device copy of nbytes / 2 bytes (read plus
+    write), each rotated past the Infinity Cache.  The fastest is reported as
+    the practical single-launch streaming rate next to the 8 TB/s peak."""
+    dev = "cuda:0"
+    count = max(2, math.ceil(2 * MALL_BYTES / nbytes))
+    bufs = [torch.empty(nbytes // 4, dtype=torch.float32, device=dev).normal_() for _ in range(count)]
+    halves = [torch.empty(nbytes // 4, dtype=torch.bfloat16, device=dev) for _ in range(count)]
+    res = {}
+    for name, fn in (("torch.sum", lambda i: torch.sum(bufs[i])),
+                     ("torch.amax", lambda i: torch.amax(bufs[i])),
+                     ("copy_ (read + write)", lambda i: halves[i].copy_(bufs[i][: nbytes // 8].view(torch.bfloat16)))):
+        ev_ms, _ = time_graph(fn, count * max(1, 64 // count), steps, count, count)
+        us = ev_ms * 1e3 / steps
+        res[name] = {"us_per_launch": round(us, 3), "GB/s": round(nbytes / us / 1e3, 1)}
+    best = max(res, key=lambda k: res[k]["GB/s"])
+    del bufs, halves
+    return {"GB/s": res[best]["GB/s"], "kernel": best, "bytes_per_launch": nbytes, "measured": res}
 
 
 PROFILES = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles")
@@ -434,56 +461,63 @@ def _repeat(fn, seconds):
             return n, time.perf_counter() - t0
 
 
-def cpu_baseline(seconds=12.0, stage_seconds=4.0):
-    """The oracle, untuned, on a bounded sample of the decode workload: the
-    linear (dequantize to bf16 + fp64 matmul) over the first rows of W,
-    repeated until `seconds` have passed, then its quantize_pack and
-    dequantize stages on the same rows.  One BLAS thread."""
+def cpu_baseline(seconds=10.0, stage_seconds=3.0, prefill_seconds=8.0):
+    """The oracle, untuned, on bounded samples of the two linear workloads,
+    with NumPy's BLAS allowed every core this process may run on:
+
+    * decode: the linear (dequantize to bf16, fp64 matmul, bias) on the first
+      1024 of the 14336 weight rows, repeated for `seconds`; bytes scaled per
+      row.  Its quantize_pack and dequantize stages on the same rows follow.
+    * prefill: the act-order linear on the first 128 of the 4096 weight rows
+      (all 2048 activation rows), repeated for `prefill_seconds`; flops
+      2 M rows K per repetition."""
     from oracle import w4_oracle as O
     from int4_group_wise_amd.workloads import workload, generate, bf16_bits
-    try:
-        from threadpoolctl import threadpool_limits
-    except ImportError:                                    # pragma: no cover
-        threadpool_limits = None
-    wl = workload("decode")
-    t = generate(wl)
-    rows = 1024
-    wr = t["w"][:rows].numpy()
-    codes, sc, z = O.quantize_pack(wr, wl.G, O.ASYM)
-    xb = bf16_bits(t["x"])
-    bb = bf16_bits(t["bias"])[:rows]
-    ctx = threadpool_limits(limits=1) if threadpool_limits else None
-    n = 0
-    t0 = time.perf_counter()
-    try:
-        if ctx:
-            ctx.__enter__()
-        while True:
-            O.linear(xb, codes, sc, z, None, wl.K, wl.G, O.ASYM, bb)
-            n += 1
-            if time.perf_counter() - t0 >= seconds:
-                break
-    finally:
-        if ctx:
-            ctx.__exit__(None, None, None)
-    el = time.perf_counter() - t0
-    per_row = algorithmic_bytes_linear(wl.M, wl.N, wl.K, wl.G, True, True) / wl.N
-    gbs = per_row * rows * n / el / 1e9
-    # stages on the same rows: bytes as the GPU codec counts them
-    ng = (wl.K + wl.G - 1) // wl.G
-    packed = rows * ((wl.K + 1) // 2 + 5 * ng)
-    nq, tq = _repeat(lambda: O.quantize_pack(wr, wl.G, O.ASYM), stage_seconds)
-    nd, td = _repeat(lambda: O.dequantize(codes, sc, z, None, wl.K, wl.G, O.ASYM, "bf16"), stage_seconds)
-    stages = {"quantize_pack": {"GB/s": round((rows * wl.K * 4 + packed) * nq / tq / 1e9, 4), "repetitions": nq,
-                                "seconds": round(tq, 1)},
-              "dequantize_bf16": {"GB/s": round((packed + rows * wl.K * 2) * nd / td / 1e9, 4), "repetitions": nd,
-                                  "seconds": round(td, 1)}}
-    return {"value": round(gbs, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+    from threadpoolctl import threadpool_limits, threadpool_info
+    cores = len(os.sched_getaffinity(0))
+    out = {}
+    with threadpool_limits(limits=cores):
+        blas_threads = max([d.get("num_threads", 1) for d in threadpool_info()] or [1])
+        wl = workload("decode")
+        t = generate(wl)
+        rows = 1024
+        wr = t["w"][:rows].numpy()
+        codes, sc, z = O.quantize_pack(wr, wl.G, O.ASYM)
+        xb = bf16_bits(t["x"])
+        bb = bf16_bits(t["bias"])[:rows]
+        n, el = _repeat(lambda: O.linear(xb, codes, sc, z, None, wl.K, wl.G, O.ASYM, bb), seconds)
+        per_row = algorithmic_bytes_linear(wl.M, wl.N, wl.K, wl.G, True, True) / wl.N
+        gbs = per_row * rows * n / el / 1e9
+        ng = (wl.K + wl.G - 1) // wl.G
+        packed = rows * ((wl.K + 1) // 2 + 5 * ng)
+        nq, tq = _repeat(lambda: O.quantize_pack(wr, wl.G, O.ASYM), stage_seconds)
+        nd, td = _repeat(lambda: O.dequantize(codes, sc, z, None, wl.K, wl.G, O.ASYM, "bf16"), stage_seconds)
+        stages = {"quantize_pack": {"GB/s": round((rows * wl.K * 4 + packed) * nq / tq / 1e9, 4), "repetitions": nq,
+                                    "seconds": round(tq, 1)},
+                  "dequantize_bf16": {"GB/s": round((packed + rows * wl.K * 2) * nd / td / 1e9, 4), "repetitions": nd,
+                                      "seconds": round(td, 1)}}
+        del t
+        # prefill: act-order zero-point weight, 128 output features
+        wp = workload("prefill")
+        tp = generate(wp)
+        prow = 128
+        gnp = tp["g_idx"].numpy()
+        pc, ps, pz = O.quantize_pack(tp["w"][:prow].numpy(), wp.G, O.ASYM, gnp)
+        xp = bf16_bits(tp["x"])
+        npf, tpf = _repeat(lambda: O.linear(xp, pc, ps, pz, gnp, wp.K, wp.G, O.ASYM, None), prefill_seconds)
+        tfs = 2.0 * wp.M * prow * wp.K * npf / tpf / 1e12
+        out["prefill"] = {"value": round(tfs, 5), "unit": "TFLOP/s", "cores": cores, "blas_threads": blas_threads,
+                          "kind": "oracle",
+                          "sample": f"oracle act-order linear (dequantize to bf16 through g_idx, fp64 matmul) on the "
+                                    f"first {prow} of {wp.N} weight rows with all {wp.M} activation rows of the "
+                                    f"prefill workload, {npf} repetitions in {tpf:.1f} s"}
+    return {"value": round(gbs, 4), "unit": "GB/s", "cores": cores, "blas_threads": blas_threads, "kind": "oracle",
             "sample": f"oracle linear (dequantize to bf16, fp64 matmul, bias) on the first {rows} of "
                       f"{wl.N} weight rows of the decode workload, {n} repetitions in {el:.1f} s, "
                       f"bytes scaled per row; stages: quantize_pack (fp32 rows in) and dequantize "
-                      f"(bf16 out) on the same rows",
-            "stages": stages}
+                      f"(bf16 out) on the same rows; NumPy's element-wise steps run on one thread, "
+                      f"the fp64 matmul on blas_threads",
+            "stages": stages, "prefill": out["prefill"]}
 
 
 def main():
@@ -532,9 +566,13 @@ def main():
                    "algorithmic_bytes_per_step": nbytes, "host_ms": round(host_ms, 3)},
         "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": measured_traffic(),
-                     "kernel": "gemv_dot2_kernel<1, true>", "us_per_launch": round(us_per, 3)},
+                     "kernel": "gemv_stream_kernel<7, 1, 2, true>", "us_per_launch": round(us_per, 3)},
     }
     del rot
+    torch.cuda.empty_cache()
+    floor = bench_streaming_floor(nbytes)
+    line["roofline"]["practical_peak"] = floor["GB/s"]
+    line["roofline"]["practical_peak_source"] = floor
     torch.cuda.empty_cache()
     if not args.no_secondary:
         line["secondary"] = {"decode_hot_cache": bench_decode_hot(w4)}

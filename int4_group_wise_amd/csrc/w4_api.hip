@@ -149,6 +149,11 @@ w4_status w4_linear(const void* x, int64_t M, const uint8_t* codes, const float*
   if (N * chunk_blocks > kMaxGrid || gemm_blocks > kMaxGrid)
     return fail(W4_ERR_UNSUPPORTED, "%s: matrix too large for one launch", fn);
   w4::DequantArgs d{codes, scales, zeros, g_idx, N, K, G, NG, mode == W4_ASYM, workspace, 1};
+  if (w4::gemm_tiled_ok(M, N, K) && w4::dequantize_tiled_ok(d)) {
+    // the weight dequantized into the GEMM's fragment-tiled layout
+    if (w4_status st = hip_status(w4::launch_dequantize_tiled(d, s), fn)) return st;
+    return hip_status(w4::launch_gemm_tiled(a.x, static_cast<const uint16_t*>(workspace), a.bias, a.y, M, N, K, s), fn);
+  }
   if (w4_status st = hip_status(w4::launch_dequantize(d, s), fn)) return st;
   return hip_status(w4::launch_gemm_bf16(a.x, static_cast<const uint16_t*>(workspace), a.bias, a.y, M, N, K, s), fn);
 }

@@ -12,6 +12,8 @@
 // This translation unit is compiled with -ffp-contract=off: every division is
 // IEEE round-to-nearest and no multiply-add is fused, so results are
 // bit-identical to the fp32 definition above.
+#include <algorithm>
+
 #include "w4_device.h"
 #include "w4_internal.h"
 
@@ -943,6 +945,149 @@ __global__ __launch_bounds__(kDThreads) void dequantize_act_kernel(DequantArgs a
   }
 }
 
+// ---------------------------------------------------------------------------
+// Dequantize to the fragment-tiled bf16 layout of the prefill GEMM
+// (tiled_unit in w4_internal.h; N % 32 == 0, K % 64 == 0, contiguous groups
+// with G % 32 == 0 or a g_idx).  A workgroup owns one 32-row block and a
+// range of 64-column K-steps.  Every (row, group) pair the range touches gets
+// a 16-entry table of its bf16 values fp32(v) * s (the same values as the row
+// dequantizers), so a nibble becomes one LDS read.  Thread t serves row
+// rr = t % 32, K-step half h = (t / 32) % 2 and K-steps kq = t / 64 + 4 i: it
+// loads the 16 code bytes of its 32 columns, looks up 32 values and writes
+// four 16-byte units; the 64 lanes of a wave write 1 KB contiguously.
+// ---------------------------------------------------------------------------
+constexpr int kTiledRows = 32;
+
+struct TiledPlan {
+  int kt_per_block, blocks_k, groups;   // K-steps per workgroup, workgroups along K, table groups per row
+  size_t lds;
+};
+
+__host__ __device__ inline int tiled_table_stride(int groups) {   // bytes per row: 32 per group, +4 against bank conflicts
+  return groups * 32 + 4;
+}
+
+template <bool ASYM, bool GIDX>
+__global__ __launch_bounds__(kDThreads) void dequantize_tiled_kernel(DequantArgs a, int kt_per_block, int groups) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t tsm[];
+  const int K = static_cast<int>(a.K);
+  const int KT = K / 64;
+  const int NG = static_cast<int>(a.NG);
+  const int G = static_cast<int>(a.G);
+  const int64_t row0 = static_cast<int64_t>(blockIdx.x) * kTiledRows;
+  const int kt0 = blockIdx.y * kt_per_block;
+  const int kt1 = min(KT, kt0 + kt_per_block);
+  // groups of the table: all of them with a g_idx, else those the K range covers
+  const int g_first = GIDX ? 0 : (64 * kt0) / G;
+  const int stride = tiled_table_stride(groups);
+  // with a g_idx: the table byte offset of each column's group, uint16 per
+  // column of the range, after the value table
+  uint16_t* gtab = reinterpret_cast<uint16_t*>(tsm + kTiledRows * stride);
+
+  // 0. this thread's code words: K-steps kq + 4 i of the range, 16 bytes
+  //    (32 columns) each, issued first so that the table work overlaps them
+  const int rr = threadIdx.x % 32, h = (threadIdx.x / 32) % 2, kq = threadIdx.x / 64;
+  const int64_t n = row0 + rr;
+  const int64_t KB = a.K / 2;
+  constexpr int kIt = 4;   // K-steps per thread and batch
+  u32x4 cw[kIt];
+  auto load_batch = [&](int ktb) {
+#pragma unroll
+    for (int i = 0; i < kIt; ++i) {
+      const int kt = min(ktb + 4 * i, kt1 - 1);   // past the range: the last again, not stored
+      cw[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(a.codes + n * KB + 32 * kt + 16 * h));
+    }
+  };
+  load_batch(kt0 + kq);
+
+  // 1. tables: values, entry (row r, group g_first + gl, nibble u) at
+  //    r * stride + gl * 32 + 2 u; group offsets of the range's columns
+  for (int p = threadIdx.x; p < kTiledRows * groups; p += kDThreads) {
+    const int r = p / groups, gl = p % groups;
+    const int g = min(g_first + gl, NG - 1);
+    const int64_t gi = (row0 + r) * a.NG + g;
+    const float sc = a.scales[gi];
+    const int z = ASYM ? static_cast<int>(a.zeros[gi]) : 8;
+    uint32_t wv[8];
+#pragma unroll
+    for (int u = 0; u < 16; u += 2) {
+      // value formed in integers (signed codes: (u ^ 8) - 8), then one fp32 multiply
+      const float v0 = static_cast<float>((ASYM ? u : (u ^ 8)) - z) * sc;
+      const float v1 = static_cast<float>((ASYM ? u + 1 : ((u + 1) ^ 8)) - z) * sc;
+      wv[u / 2] = f32_to_bf16(v0) | (f32_to_bf16(v1) << 16);
+    }
+    uint32_t* dst = reinterpret_cast<uint32_t*>(tsm + r * stride + gl * 32);
+#pragma unroll
+    for (int q = 0; q < 8; ++q) dst[q] = wv[q];
+  }
+  if constexpr (GIDX) {
+    const int ncols = 64 * (kt1 - kt0);
+    for (int c = threadIdx.x; c < ncols; c += kDThreads)
+      gtab[c] = static_cast<uint16_t>(min(max(a.g_idx[64 * kt0 + c], 0), NG - 1) * 32);
+  }
+  __syncthreads();
+
+  // 2. lookups and tiled stores
+  const uint8_t* trow = tsm + rr * stride;
+  uint16_t* out = static_cast<uint16_t*>(a.out);
+  for (int ktb = kt0 + kq; ktb < kt1; ktb += 4 * kIt) {
+#pragma unroll
+    for (int i = 0; i < kIt; ++i) {
+      const int kt = ktb + 4 * i;
+      if (kt >= kt1) break;
+      const int c0 = 64 * kt + 32 * h;   // first of the thread's 32 columns
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        // unit (ks, h): columns c0 + 8 ks .. + 7, code word ks
+        uint32_t goff[8];
+        if constexpr (GIDX) {
+          const u32x4 gq = *reinterpret_cast<const u32x4*>(gtab + (c0 - 64 * kt0) + 8 * ks);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            goff[2 * e] = gq[e] & 0xFFFFu;
+            goff[2 * e + 1] = gq[e] >> 16;
+          }
+        } else {
+          const uint32_t go = static_cast<uint32_t>(c0 / G - g_first) * 32;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) goff[e] = go;
+        }
+        const uint32_t d = cw[i][ks];
+        uint32_t o[4];
+#pragma unroll
+        for (int e = 0; e < 8; e += 2) {
+          const uint32_t u0 = (d >> (4 * e)) & 15u, u1 = (d >> (4 * e + 4)) & 15u;
+          const uint32_t lo = *reinterpret_cast<const uint16_t*>(trow + goff[e] + 2 * u0);
+          const uint32_t hi = *reinterpret_cast<const uint16_t*>(trow + goff[e + 1] + 2 * u1);
+          o[e / 2] = lo | (hi << 16);
+        }
+        const int64_t unit = ((static_cast<int64_t>(blockIdx.x) * KT + kt) * 4 + ks) * 64 + 32 * h + rr;
+        __builtin_nontemporal_store(u32x4{o[0], o[1], o[2], o[3]}, reinterpret_cast<u32x4*>(out + 8 * unit));
+      }
+    }
+    if (ktb + 4 * kIt < kt1) load_batch(ktb + 4 * kIt);
+  }
+}
+
+TiledPlan tiled_plan(const DequantArgs& a) {
+  TiledPlan p{};
+  const int64_t KT = a.K / 64;
+  const int64_t row_blocks = a.N / kTiledRows;
+  // about 512 workgroups (two per CU), at least 4 K-steps each
+  int64_t per = std::max<int64_t>(4, (KT * row_blocks + 511) / 512);
+  per = std::min(per, KT);
+  p.kt_per_block = static_cast<int>(per);
+  p.blocks_k = static_cast<int>((KT + per - 1) / per);
+  if (a.g_idx) {
+    p.groups = static_cast<int>(a.NG);
+  } else {
+    // groups a range of `per` K-steps can touch (start anywhere)
+    p.groups = static_cast<int>(std::min<int64_t>(a.NG, (64 * per + a.G - 1) / a.G + 1));
+  }
+  p.lds = static_cast<size_t>(kTiledRows) * tiled_table_stride(p.groups) + (a.g_idx ? 2 * 64 * per : 0);
+  return p;
+}
+
 template <bool OUT_BF16, bool ASYM, int GIDX>
 hipError_t launch_d3(const DequantArgs& a, hipStream_t s) {
   const int64_t nchunks = (a.K + 7) / 8;
@@ -983,6 +1128,26 @@ hipError_t launch_d2(const DequantArgs& a, hipStream_t s) {
 hipError_t launch_quantize_pack(const QuantArgs& a, hipStream_t s) {
   if (a.w_bf16) return a.asym ? launch_q2<true, true>(a, s) : launch_q2<true, false>(a, s);
   return a.asym ? launch_q2<false, true>(a, s) : launch_q2<false, false>(a, s);
+}
+
+bool dequantize_tiled_ok(const DequantArgs& a) {
+  if (!a.out_bf16 || a.N % 128 != 0 || a.K % 64 != 0 || a.N / kTiledRows > 65535) return false;
+  if (!a.g_idx && a.G % 32 != 0) return false;
+  return tiled_plan(a).lds <= 65536;
+}
+
+hipError_t launch_dequantize_tiled(const DequantArgs& a, hipStream_t s) {
+  if (!dequantize_tiled_ok(a)) return hipErrorInvalidValue;
+  const TiledPlan p = tiled_plan(a);
+  const dim3 grid(static_cast<uint32_t>(a.N / kTiledRows), static_cast<uint32_t>(p.blocks_k));
+  if (a.g_idx) {
+    if (a.asym) dequantize_tiled_kernel<true, true><<<grid, dim3(kDThreads), p.lds, s>>>(a, p.kt_per_block, p.groups);
+    else dequantize_tiled_kernel<false, true><<<grid, dim3(kDThreads), p.lds, s>>>(a, p.kt_per_block, p.groups);
+  } else {
+    if (a.asym) dequantize_tiled_kernel<true, false><<<grid, dim3(kDThreads), p.lds, s>>>(a, p.kt_per_block, p.groups);
+    else dequantize_tiled_kernel<false, false><<<grid, dim3(kDThreads), p.lds, s>>>(a, p.kt_per_block, p.groups);
+  }
+  return hipGetLastError();
 }
 
 hipError_t launch_dequantize(const DequantArgs& a, hipStream_t s) {

@@ -9,6 +9,11 @@
 // workgroup computes a 128 x 128 tile of y as a 2 x 2 grid of waves with
 // 64 x 64 each (4 x 4 MFMA tiles of 16 x 16), stepping K by 64 through LDS with
 // the next K-step prefetched into registers while the current one is used.
+#include <mutex>
+#include <set>
+#include <type_traits>
+#include <utility>
+
 #include "w4_device.h"
 #include "w4_internal.h"
 
@@ -268,6 +273,153 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_pipe_kernel(
   }
 }
 
+// ---------------------------------------------------------------------------
+// GEMM with a fragment-tiled weight (N % 128 == 0, K % 64 == 0): the same
+// 256 x 128 x 64 workgroup tile, 2 x 2 waves of 128 x 64 and
+// v_mfma_f32_32x32x16_bf16 as gemm_bf16_pipe_kernel, but only the activation
+// tile goes through LDS (a 3-stage ring of 32 KB stages filled by direct
+// loads).  The weight comes from the tiled layout written by the dequantizer
+// (w4_internal.h, tiled_unit): every 16-byte piece a lane needs for one MFMA
+// sits at consecutive addresses across the wave, so a wave reads its weight
+// fragments with fully coalesced 1 KB loads straight into registers, two
+// K-steps ahead.  Per K-step a CU then moves 32 KB of direct-load writes and
+// 64 KB of fragment reads through LDS instead of 48 KB and 96 KB.
+//
+// K order inside a K-step: lane half h of an MFMA operand holds columns
+// 32 h + 8 ks .. 32 h + 8 ks + 7 for MFMA ks (activations: LDS chunk 4 h + ks
+// of the row; weight: the tiled unit (ks, h)); both operands agree, so the
+// MFMA sums the same products as with the natural order.
+// ---------------------------------------------------------------------------
+constexpr int TM = 256, TN = 128, TK = 64, TSTAGES = 3;
+constexpr int kTStageBytes = TM * TK * 2;                // 32 KB: activations only
+constexpr int kTLdsBytes = TSTAGES * kTStageBytes;       // 96 KB
+
+__global__ __launch_bounds__(kThreads) void gemm_tiled_kernel(
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ wt,
+    const uint16_t* __restrict__ bias, uint16_t* __restrict__ y,
+    int M, int N, int K) {
+  extern __shared__ __attribute__((aligned(1024))) uint8_t tsm[];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wid >> 1, wn = wid & 1;
+  const int tiles_n = N / TN;
+  int tm, tn;
+  pipe_tile(blockIdx.x, (M + TM - 1) / TM, tiles_n, tm, tn);
+  const int m0 = tm * TM;
+  const int n0 = tn * TN;
+  const int KT = K / TK;
+
+  // activation loads: as in gemm_bf16_pipe_kernel (wave wid fills rows
+  // [64 wid, 64 wid + 64), lane i of an 8-row instruction slot i)
+  const int lr = lane >> 3, ls = lane & 7;
+  const uint16_t* asrc[8];
+#pragma unroll
+  for (int p = 0; p < 8; ++p) {
+    const int r = 64 * wid + 8 * p + lr;
+    const int gm = min(m0 + r, M - 1);    // rows past M load a valid row; never stored
+    asrc[p] = x + static_cast<int64_t>(gm) * K + 8 * (ls ^ swz(r));
+  }
+  // weight: this wave's two 32-row blocks; unit (nb, kt, ks) starts at
+  // ((nb KT + kt) 4 + ks) 64 units of 8 bf16, lane l at + l
+  const int nb0 = (n0 + 64 * wn) / 32;
+  const uint16_t* bsrc0 = wt + (static_cast<int64_t>(nb0) * KT * 4 * 64 + lane) * 8;
+  const int64_t bstride_nb = static_cast<int64_t>(KT) * 4 * 64 * 8;   // bf16 per 32-row block
+  u32x4 breg[TSTAGES][2][4];
+
+  auto issue = [&](auto stage, int kt) {
+    constexpr int S = decltype(stage)::value;
+    uint8_t* st = tsm + S * kTStageBytes;
+    const int k0 = kt * TK;
+#pragma unroll
+    for (int p = 0; p < 8; ++p) lds_dma16(asrc[p] + k0, st + (64 * wid + 8 * p) * 128);
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks)
+        breg[S][j][ks] = *reinterpret_cast<const u32x4*>(bsrc0 + j * bstride_nb + (static_cast<int64_t>(kt) * 4 + ks) * 512);
+  };
+
+  f32x16_t acc[4][2];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
+
+  const int fr = lane & 31, fh = lane >> 5;
+  auto step = [&](auto stage, int kt) {
+    constexpr int S = decltype(stage)::value;
+    // this thread's loads of stage kt are done once at most the next stage's
+    // 16 loads (8 direct, 8 weight) are outstanding; then the barrier covers
+    // every thread's direct loads.  s_waitcnt: vmcnt in bits 3:0 and 15:14,
+    // 0x4F70 = vmcnt(16), 0x0F70 = vmcnt(0), expcnt and lgkmcnt not waited on.
+    // Every step issues the loads of step kt + 2 (the last step's again near
+    // the end: the stage they fill is no longer read), so the count of loads
+    // in flight is the same at every step.
+    __builtin_amdgcn_s_waitcnt(0x4F70);
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    issue(std::integral_constant<int, (S + 2) % TSTAGES>{}, min(kt + 2, KT - 1));
+    __builtin_amdgcn_sched_barrier(0);   // the loads go out before this step's arithmetic
+    const uint8_t* sa = tsm + S * kTStageBytes + (wm * 128) * 128;
+    bf16x8_t af[4][4];
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const int chunk = 4 * fh + ks;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = 32 * i + fr;
+        af[ks][i] = *reinterpret_cast<const bf16x8_t*>(sa + r * 128 + 16 * (chunk ^ swz(r)));
+      }
+    }
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+              af[ks][i], __builtin_bit_cast(bf16x8_t, breg[S][j][ks]), acc[i][j], 0, 0, 0);
+    // order: the 16 fragment reads first (all in flight together), then the
+    // 32 MFMAs, so that later sub-steps' reads overlap earlier MFMAs
+    __builtin_amdgcn_sched_group_barrier(0x100, 16, 0);   // DS read
+    __builtin_amdgcn_sched_group_barrier(0x008, 32, 0);   // MFMA
+  };
+
+  issue(std::integral_constant<int, 0>{}, 0);
+  issue(std::integral_constant<int, 1>{}, min(1, KT - 1));
+  int kt = 0;
+  for (; kt + TSTAGES <= KT; kt += TSTAGES) {
+    step(std::integral_constant<int, 0>{}, kt);
+    step(std::integral_constant<int, 1>{}, kt + 1);
+    step(std::integral_constant<int, 2>{}, kt + 2);
+  }
+  if (kt < KT) step(std::integral_constant<int, 0>{}, kt);
+  if (kt + 1 < KT) step(std::integral_constant<int, 1>{}, kt + 1);
+  // the direct loads of the last issues must land before the workgroup's LDS
+  // is released
+  __builtin_amdgcn_s_waitcnt(0x0F70);
+
+  // 32 x 32 accumulator layout: register v of lane l holds row
+  // 8 (v / 4) + 4 (l / 32) + v % 4, column l % 32.
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int n = n0 + wn * 64 + j * 32 + fr;
+    const float b = bias ? bf16_to_f32(bias[n]) : 0.0f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int m = m0 + wm * 128 + i * 32 + 8 * (v / 4) + 4 * fh + (v % 4);
+        if (m < M) y[static_cast<int64_t>(m) * N + n] = static_cast<uint16_t>(f32_to_bf16(acc[i][j][v] + b));
+      }
+    }
+  }
+}
+
 // Any K (rows not 16-byte aligned): one thread per output, fp32 accumulation.
 __global__ __launch_bounds__(256) void gemm_bf16_nt_simple_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ wd,
@@ -284,16 +436,44 @@ __global__ __launch_bounds__(256) void gemm_bf16_nt_simple_kernel(
 
 }  // namespace
 
+// Dynamic LDS above the default limit must be allowed per kernel; the call is
+// made once per (kernel, device) and remembered under a lock.
+hipError_t ensure_lds_attribute(const void* kernel, int bytes, int dev) {
+  static std::mutex mu;
+  static std::set<std::pair<const void*, int>> done;
+  std::lock_guard<std::mutex> lock(mu);
+  if (done.count({kernel, dev})) return hipSuccess;
+  const hipError_t e = hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+  if (e == hipSuccess) done.insert({kernel, dev});
+  return e;
+}
+
+
+bool gemm_tiled_ok(int64_t M, int64_t N, int64_t K) {
+  return M >= 1 && N % TN == 0 && K % TK == 0 && M <= INT32_MAX && N <= INT32_MAX && K <= INT32_MAX;
+}
+
+hipError_t launch_gemm_tiled(const uint16_t* x, const uint16_t* wt, const uint16_t* bias, uint16_t* y,
+                             int64_t M, int64_t N, int64_t K, hipStream_t s) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  e = ensure_lds_attribute(reinterpret_cast<const void*>(gemm_tiled_kernel), kTLdsBytes, dev);
+  if (e != hipSuccess) return e;
+  const int64_t tiles = ((M + TM - 1) / TM) * (N / TN);
+  gemm_tiled_kernel<<<dim3(static_cast<uint32_t>(tiles)), dim3(kThreads), kTLdsBytes, s>>>(
+      x, wt, bias, y, static_cast<int>(M), static_cast<int>(N), static_cast<int>(K));
+  return hipGetLastError();
+}
+
 hipError_t launch_gemm_bf16(const uint16_t* x, const uint16_t* wd, const uint16_t* bias,
                             uint16_t* y, int64_t M, int64_t N, int64_t K, hipStream_t s) {
   if (K % PK == 0 && M <= INT32_MAX && N <= INT32_MAX && K <= INT32_MAX) {
-    static bool attr_set = false;   // once per process: allow the 144 KB LDS ring
-    if (!attr_set) {
-      hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(gemm_bf16_pipe_kernel),
-                                         hipFuncAttributeMaxDynamicSharedMemorySize, kPLdsBytes);
-      if (e != hipSuccess) return e;
-      attr_set = true;
-    }
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    e = ensure_lds_attribute(reinterpret_cast<const void*>(gemm_bf16_pipe_kernel), kPLdsBytes, dev);   // the 144 KB ring
+    if (e != hipSuccess) return e;
     const int64_t tiles = ((M + PM - 1) / PM) * ((N + PN - 1) / PN);
     gemm_bf16_pipe_kernel<<<dim3(static_cast<uint32_t>(tiles)), dim3(kThreads), kPLdsBytes, s>>>(
         x, wd, bias, y, static_cast<int>(M), static_cast<int>(N), static_cast<int>(K));

@@ -115,6 +115,27 @@ hipError_t launch_linear_skinny(const LinearArgs& a, hipStream_t s);
 // decode kernel; 0 when it runs in one pass).
 size_t skinny_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t G, bool has_g_idx);
 
+// Allow `bytes` of dynamic LDS for `kernel` on device `dev` (once per pair,
+// thread-safe).
+hipError_t ensure_lds_attribute(const void* kernel, int bytes, int dev);
+
+// Fragment-tiled bf16 weight for the prefill GEMM (N % 128 == 0, K % 64 == 0):
+// the 8 columns k .. k + 7 (k % 8 == 0) of row n form one 16-byte unit at
+// unit index ((nb KT + kt) 4 + ks) 64 + 32 h + rr, where nb = n / 32,
+// rr = n % 32, KT = K / 64, kt = k / 64, c = (k % 64) / 8, h = c / 4,
+// ks = c % 4.  One MFMA operand fragment of a wave is then 1 KB contiguous.
+__host__ __device__ inline int64_t tiled_unit(int64_t n, int64_t k, int64_t K) {
+  const int64_t c = (k % 64) / 8;
+  return (((n / 32) * (K / 64) + k / 64) * 4 + (c % 4)) * 64 + 32 * (c / 4) + n % 32;
+}
+bool gemm_tiled_ok(int64_t M, int64_t N, int64_t K);
+hipError_t launch_gemm_tiled(const uint16_t* x, const uint16_t* wt, const uint16_t* bias, uint16_t* y,
+                             int64_t M, int64_t N, int64_t K, hipStream_t s);
+// Dequantize to the tiled bf16 layout; false when the shape is not covered
+// (then the plain row-major dequantize and GEMM run).
+bool dequantize_tiled_ok(const DequantArgs& a);
+hipError_t launch_dequantize_tiled(const DequantArgs& a, hipStream_t s);
+
 // Dense bf16 GEMM  y = x . wd^T + bias  (x [M, K], wd [N, K], y [M, N]).
 hipError_t launch_gemm_bf16(const uint16_t* x, const uint16_t* wd,
                             const uint16_t* bias, uint16_t* y, int64_t M,

@@ -45,15 +45,11 @@ constexpr int64_t kLComputeUnits = 256;   // MI355X
 // LDS a workgroup may use: the device's per-block limit, at most one CU's LDS
 // (the rank-64 A^T tile plus one 32-row B block needs 148 KB)
 size_t lora_lds_limit() {
-  static size_t limit = 0;
-  if (!limit) {
-    int dev = 0, v = 0;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&v, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess || v <= 0)
-      return 0;
-    limit = std::min(kLLdsCap, static_cast<size_t>(v));
-  }
-  return limit;
+  int dev = 0, v = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&v, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess || v <= 0)
+    return 0;
+  return std::min(kLLdsCap, static_cast<size_t>(v));
 }
 
 __device__ __forceinline__ uint32_t load_code_word(const uint8_t* __restrict__ codes, int64_t off, int cnt,
@@ -268,12 +264,13 @@ __global__ __launch_bounds__(kLThreads) void lora_merge_kernel(LoraArgs a, int r
 template <bool ASYM, bool GIDX, bool QUANT, int LPG>
 hipError_t launch_lora3(const LoraArgs& a, hipStream_t s) {
   const size_t lds_max = lora_lds_limit();
-  static bool attr_set = false;   // once per process: the tiles may pass 64 KB
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(lora_merge_kernel<ASYM, GIDX, QUANT, LPG>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds_max));
+  {   // the tiles may pass 64 KB
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return e;
-    attr_set = true;
+    e = ensure_lds_attribute(reinterpret_cast<const void*>(lora_merge_kernel<ASYM, GIDX, QUANT, LPG>),
+                             static_cast<int>(lds_max), dev);
+    if (e != hipSuccess) return e;
   }
   // Row blocks: a multiple of the workgroup's 32-row step, small enough that
   // A^T and B fit in LDS, and sized so that the workgroups fill whole rounds

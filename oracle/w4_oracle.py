@@ -208,26 +208,26 @@ def pack_nibbles(q) -> np.ndarray:
     byte's bits 4..7 are 0.  Written byte by byte."""
     q = np.asarray(q)
     N, K = q.shape
-    nib = (q.astype(np.int16) & 15).astype(np.uint8)
-    out = np.zeros((N, (K + 1) // 2), dtype=np.uint8)
-    for j in range(out.shape[1]):
-        low = nib[:, 2 * j]
-        high = nib[:, 2 * j + 1] if 2 * j + 1 < K else np.zeros(N, np.uint8)
-        out[:, j] = low | (high << np.uint8(4))
-    return out
+    nib_t = np.ascontiguousarray((q.astype(np.int16) & 15).astype(np.uint8).T)   # [K, N]: column k of every row
+    out_t = np.zeros(((K + 1) // 2, N), dtype=np.uint8)                           # [byte j, row]
+    for j in range(out_t.shape[0]):
+        low = nib_t[2 * j]
+        high = nib_t[2 * j + 1] if 2 * j + 1 < K else np.zeros(N, np.uint8)
+        out_t[j] = low | (high << np.uint8(4))
+    return np.ascontiguousarray(out_t.T)
 
 
 def unpack_nibbles(codes, K: int) -> np.ndarray:
     """Inverse of ``pack_nibbles``: uint8 [N, K] nibble values 0..15; column
     k is bits 0..3 of byte k // 2 for even k and bits 4..7 for odd k
     ([LoopQ] ``_dequantize_validated``)."""
-    c = np.asarray(codes, dtype=np.uint8)
-    N = c.shape[0]
-    out = np.zeros((N, K), dtype=np.uint8)
+    c_t = np.ascontiguousarray(np.asarray(codes, dtype=np.uint8).T)   # [byte j, row]
+    N = c_t.shape[1]
+    out_t = np.zeros((K, N), dtype=np.uint8)                          # [column k, row]
     for k in range(K):
-        byte = c[:, k // 2]
-        out[:, k] = (byte >> np.uint8(4)) if k % 2 else (byte & np.uint8(15))
-    return out
+        byte = c_t[k // 2]
+        out_t[k] = (byte >> np.uint8(4)) if k % 2 else (byte & np.uint8(15))
+    return np.ascontiguousarray(out_t.T)
 
 
 def decode(u, mode: str, zeros=None, gid=None) -> np.ndarray:

@@ -190,6 +190,12 @@ CASES = [
     (300, 520, 512, 128, "sym", False, "f32", "randn"),
     (1300, 500, 256, 128, "asym", False, "f32", "randn"),  # 6 x 4 GEMM tiles: per-XCD runs, last row group partial
     (96, 80, 1024, -1, "sym", False, "f32", "none"),
+    # prefill with the fragment-tiled weight (N % 128 == 0, K % 64 == 0):
+    # act-order, G = 32 with 128 groups, G = 512, per-channel, M tails
+    (257, 384, 640, 64, "asym", True, "f32", "randn"),
+    (129, 256, 4096, 32, "sym", False, "bf16", "none"),
+    (65, 128, 1024, 512, "asym", False, "f32", "randn"),
+    (33, 128, 1024, -1, "sym", False, "f32", "none"),
     # per-channel (G = -1, or any G >= K): one scale per row
     (1, 40, 100, -1, "sym", False, "f32", "randn"),
     (4, 33, 4096, -1, "sym", False, "bf16", "none"),     # matrix-core decode
@@ -424,6 +430,30 @@ def test_identity_activation_is_exact(M, K, G, mode):
     ref = O.dequantize(oc, osc, oz, None, K, G, _mode(mode), "bf16")[:, cols].T
     assert np.array_equal(_bits(y.cpu()), ref)
     assert np.array_equal(_bits(wd.cpu())[:, cols].T, ref)
+
+
+@pytest.mark.parametrize("M,K,G,mode,act", [(130, 1024, 128, "asym", True), (256, 640, 64, "sym", False),
+                                            (40, 4096, 32, "asym", False), (300, 2048, 128, "sym", True)])
+def test_identity_activation_is_exact_tiled_prefill(M, K, G, mode, act):
+    """The prefill path with the fragment-tiled weight (N % 128 == 0,
+    K % 64 == 0): unit activation rows return the bf16 dequantized weight bit
+    for bit, which pins the tiled layout, the K order inside a K-step and the
+    act-order table lookups."""
+    N = 256
+    gen = torch.Generator().manual_seed(M + K + G)
+    w = torch.randn(N, K, generator=gen) * 0.02
+    g_idx = (torch.randperm(K, generator=gen) // G).to(torch.int32) if act else None
+    cols = np.sort(np.random.default_rng(M + 1).choice(K, size=min(M, K), replace=False))
+    x = torch.zeros(len(cols), K)
+    x[torch.arange(len(cols)), torch.from_numpy(cols)] = 1.0
+    gi = None if g_idx is None else g_idx.to(DEV)
+    codes, scales, zeros = w4.quantize_pack(w.to(DEV), G, mode, gi)
+    y = w4.linear(x.to(torch.bfloat16).to(DEV), codes, scales, zeros, gi, K, G, mode)
+    torch.cuda.synchronize()
+    gnp = None if g_idx is None else g_idx.numpy()
+    oc, osc, oz = O.quantize_pack(w.numpy(), G, _mode(mode), gnp)
+    ref = O.dequantize(oc, osc, oz, gnp, K, G, _mode(mode), "bf16")[:, cols].T
+    assert np.array_equal(_bits(y.cpu()), ref)
 
 
 def test_empty_batch_and_errors():
