@@ -152,6 +152,27 @@ w4_status w4_linear(const void* x, int64_t M,
                     void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * w4_linear_noalloc — w4_linear for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc): the same operation, arguments and results as w4_linear,
+ * without the workspace.  Scratch the kernels need (the split-K partial sums
+ * of the batched decode path, the staged weight of the prefill path) lives in
+ * a fixed device array of w4_linear_noalloc_max_scratch_bytes() bytes that
+ * every GPU the library runs on holds until the process ends; the call
+ * allocates and frees nothing.  A shape whose w4_linear_workspace_bytes
+ * exceeds that size returns W4_ERR_UNSUPPORTED and launches nothing.
+ * Every call on one GPU shares that GPU's array: calls that overlap on one
+ * GPU (on different streams, or from different host threads without ordering)
+ * race on it.  No contents carry over from one call to the next.
+ */
+size_t w4_linear_noalloc_max_scratch_bytes(void);
+w4_status w4_linear_noalloc(const void* x, int64_t M,
+                            const uint8_t* codes, const float* scales,
+                            const uint8_t* zeros, const int32_t* g_idx,
+                            int64_t N, int64_t K, int64_t G, int mode,
+                            const void* bias, void* y, void* stream);
+
+/*
  * w4_linear_grad_input_workspace_bytes — device scratch w4_linear_grad_input
  * needs for this shape: fp32 partial sums of row slices for M <= 16, the
  * transposed bf16 dequantized weight [K, N] for M > 16.

@@ -2,6 +2,7 @@
 // dispatch to the gfx950 kernels.  Nothing here allocates device memory.
 #include <cstdarg>
 #include <cstdio>
+#include <mutex>
 #include <string>
 
 #include "w4.h"
@@ -118,12 +119,15 @@ size_t w4_linear_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t G, int
   return static_cast<size_t>(N) * static_cast<size_t>(K) * 2u;   // bf16 dequantized weight
 }
 
-w4_status w4_linear(const void* x, int64_t M, const uint8_t* codes, const float* scales,
-                    const uint8_t* zeros, const int32_t* g_idx, int64_t N, int64_t K, int64_t G,
-                    int mode, const void* bias, void* y, void* workspace, size_t workspace_bytes,
-                    void* stream) {
-  g_last_error.clear();
-  const char* fn = "w4_linear";
+}  // extern "C"
+
+namespace {
+
+// The body of w4_linear; `fn` names the entry point in error messages.
+w4_status linear_impl(const void* x, int64_t M, const uint8_t* codes, const float* scales,
+                      const uint8_t* zeros, const int32_t* g_idx, int64_t N, int64_t K, int64_t G,
+                      int mode, const void* bias, void* y, void* workspace, size_t workspace_bytes,
+                      void* stream, const char* fn) {
   if (w4_status st = check_format(N, K, G, mode, zeros, g_idx, fn)) return st;
   G = kernel_group(K, G);
   if (M < 0) return fail(W4_ERR_INVALID_ARG, "%s: M must be >= 0", fn);
@@ -156,6 +160,70 @@ w4_status w4_linear(const void* x, int64_t M, const uint8_t* codes, const float*
   }
   if (w4_status st = hip_status(w4::launch_dequantize(d, s), fn)) return st;
   return hip_status(w4::launch_gemm_bf16(a.x, static_cast<const uint16_t*>(workspace), a.bias, a.y, M, N, K, s), fn);
+}
+
+// Scratch of w4_linear_noalloc: device memory of fixed size that every GPU
+// the library runs on holds until the process ends.  Host code uses the
+// per-device address from hipGetSymbolAddress, never the array's name.
+constexpr size_t kNoAllocScratchBytes = size_t(16) << 20;
+__device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// This device's scratch address, looked up once per device with that device
+// current.
+w4_status scratch_address(void** out, const char* fn) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e, fn);
+  if (dev < 0 || dev >= kMaxDevices) return fail(W4_ERR_UNSUPPORTED, "%s: device %d out of range", fn, dev);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_status(e, fn);
+    if (!p) return fail(W4_ERR_HIP, "%s: no device address for the scratch array", fn);
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return W4_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t w4_linear_noalloc_max_scratch_bytes(void) { return kNoAllocScratchBytes; }
+
+w4_status w4_linear_noalloc(const void* x, int64_t M, const uint8_t* codes, const float* scales,
+                            const uint8_t* zeros, const int32_t* g_idx, int64_t N, int64_t K, int64_t G,
+                            int mode, const void* bias, void* y, void* stream) {
+  g_last_error.clear();
+  const char* fn = "w4_linear_noalloc";
+  if (M > 0 && N >= 1 && K >= 1 && (G >= 1 || G == W4_PER_CHANNEL)) {
+    const size_t need = w4_linear_workspace_bytes(M, N, K, G, mode, g_idx != nullptr);
+    if (need > kNoAllocScratchBytes)
+      return fail(W4_ERR_UNSUPPORTED, "%s: this shape needs %zu bytes of scratch, more than the %zu this entry point holds",
+                  fn, need, kNoAllocScratchBytes);
+    if (need) {
+      void* ws = nullptr;
+      if (w4_status st = scratch_address(&ws, fn)) return st;
+      return linear_impl(x, M, codes, scales, zeros, g_idx, N, K, G, mode, bias, y, ws, kNoAllocScratchBytes,
+                         stream, fn);
+    }
+  }
+  return linear_impl(x, M, codes, scales, zeros, g_idx, N, K, G, mode, bias, y, nullptr, 0, stream, fn);
+}
+
+w4_status w4_linear(const void* x, int64_t M, const uint8_t* codes, const float* scales,
+                    const uint8_t* zeros, const int32_t* g_idx, int64_t N, int64_t K, int64_t G,
+                    int mode, const void* bias, void* y, void* workspace, size_t workspace_bytes,
+                    void* stream) {
+  g_last_error.clear();
+  return linear_impl(x, M, codes, scales, zeros, g_idx, N, K, G, mode, bias, y, workspace, workspace_bytes,
+                     stream, "w4_linear");
 }
 
 size_t w4_linear_grad_input_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t G, int mode,

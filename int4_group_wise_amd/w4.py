@@ -62,6 +62,10 @@ def load() -> ctypes.CDLL:
     lib.w4_linear_workspace_bytes.argtypes = [I64, I64, I64, I64, I32, I32]
     lib.w4_linear.restype = I32
     lib.w4_linear.argtypes = [P, I64, P, P, P, P, I64, I64, I64, I32, P, P, P, SZ, P]
+    lib.w4_linear_noalloc_max_scratch_bytes.restype = SZ
+    lib.w4_linear_noalloc_max_scratch_bytes.argtypes = []
+    lib.w4_linear_noalloc.restype = I32
+    lib.w4_linear_noalloc.argtypes = [P, I64, P, P, P, P, I64, I64, I64, I32, P, P, P]
     lib.w4_linear_grad_input_workspace_bytes.restype = SZ
     lib.w4_linear_grad_input_workspace_bytes.argtypes = [I64, I64, I64, I64, I32, I32]
     lib.w4_linear_grad_input.restype = I32
@@ -218,6 +222,28 @@ def linear(x, codes, scales, zeros, g_idx, K: int, G: int, mode="sym", bias=None
     _check(lib, lib.w4_linear(_ptr(x), M, _ptr(codes), _ptr(scales), _ptr(zeros), _ptr(g_idx),
                               N, K, G, mode, _ptr(bias), _ptr(out), _ptr(workspace), ws_bytes,
                               _stream(x.device)))
+    return out
+
+
+def linear_noalloc(x, codes, scales, zeros, g_idx, K: int, G: int, mode="sym", bias=None, out=None) -> torch.Tensor:
+    """``linear`` through w4_linear_noalloc: the library's fixed per-device
+    scratch array instead of a workspace (calls that overlap on one GPU race
+    on it)."""
+    lib = load()
+    mode = _mode(mode)
+    N = codes.shape[0]
+    _format_args(N, K, G, mode, codes, scales, zeros, g_idx)
+    if x.dim() != 2 or x.shape[1] != K:
+        raise ValueError(f"x must be [M, {K}]")
+    _dev(x, "x", torch.bfloat16)
+    M = x.shape[0]
+    if bias is not None:
+        _dev(bias, "bias", torch.bfloat16, (N,))
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
+    _dev(out, "out", torch.bfloat16, (M, N))
+    _check(lib, lib.w4_linear_noalloc(_ptr(x), M, _ptr(codes), _ptr(scales), _ptr(zeros), _ptr(g_idx),
+                                      N, K, G, mode, _ptr(bias), _ptr(out), _stream(x.device)))
     return out
 
 

@@ -120,6 +120,17 @@ def test_linear_rejects_and_workspace(lib):
     assert "workspace" in lib.w4_last_error().decode()
 
 
+def test_linear_noalloc_rejects_before_any_launch(lib):
+    # the scratch array's size is fixed; shapes needing more are refused on the host
+    cap = lib.w4_linear_noalloc_max_scratch_bytes()
+    assert cap == 16 << 20
+    assert lib.w4_linear_workspace_bytes(64, 8192, 8192, 128, 0, 0) > cap
+    assert lib.w4_linear_noalloc(FAKE, 64, FAKE, FAKE, None, None, 8192, 8192, 128, 0, None, FAKE, None) == 2
+    assert "scratch" in lib.w4_last_error().decode()
+    assert lib.w4_linear_noalloc(FAKE, 0, FAKE, FAKE, None, None, 4, 16, 8, 0, None, FAKE, None) == 0
+    assert lib.w4_linear_noalloc(FAKE, 2, FAKE, FAKE, None, None, 4, 16, 8, 3, None, FAKE, None) == 1
+
+
 def test_grad_input_rejects_and_workspace(lib):
     f = lib.w4_linear_grad_input
     assert f(FAKE, 0, FAKE, FAKE, None, None, 4, 16, 8, 0, FAKE, None, 0, None) == 0
