@@ -99,12 +99,17 @@ def time_graph(call, n_calls, steps, warmup, rot_count):
     return e0.elapsed_time(e1), (t1 - t0) * 1e3
 
 
-def bench_decode(w4, steps, warmup):
+def bench_decode(w4, steps, warmup, packed_zeros=False):
+    """The decode workload; with packed_zeros the zero-points are stored two
+    per byte (W4_ASYM_PACKED) and read that way by the kernel."""
     from int4_group_wise_amd.workloads import workload, generate
     wl = workload("decode")
     t = generate(wl)
     dev = "cuda:0"
     codes, scales, zeros = w4.quantize_pack(t["w"].to(dev), wl.G, wl.mode)
+    mode = wl.mode
+    if packed_zeros:
+        zeros, mode = w4.pack_zeros(zeros), "asym_packed"
     x = t["x"].to(dev)
     bias = t["bias"].to(dev)
     rot = Rotation([codes, scales, zeros, bias], 2 * MALL_BYTES)
@@ -113,11 +118,14 @@ def bench_decode(w4, steps, warmup):
 
     def call(i):
         c, s, z, b = rot.sets[i]
-        w4.linear(x, c, s, z, None, wl.K, wl.G, wl.mode, b, out=ys[i])
+        w4.linear(x, c, s, z, None, wl.K, wl.G, mode, b, out=ys[i])
 
     n_calls = rot.count * max(1, 128 // rot.count)
     ev_ms, host_ms = time_graph(call, n_calls, steps, warmup, rot.count)
     nbytes = algorithmic_bytes_linear(wl.M, wl.N, wl.K, wl.G, True, True)
+    if packed_zeros:
+        ng = -(-wl.K // wl.G)
+        nbytes -= wl.N * (ng - (ng + 1) // 2)
     return wl, nbytes, ev_ms, host_ms, rot
 
 
@@ -261,6 +269,19 @@ def bench_secondary(w4):
     from int4_group_wise_amd.workloads import workload, generate
     dev = "cuda:0"
     out = {}
+
+    # decode with the zero-points packed two per byte
+    wl, nb, ev_ms, _, rot = bench_decode(w4, 4000, 400, packed_zeros=True)
+    gbs = nb * 4000 / (ev_ms * 1e-3) / 1e9
+    out["decode_packed_zeros"] = {"metric": "W4A16 linear HBM GB/s M=1, zero-points packed two per byte",
+                                  "value": round(gbs, 1), "unit": "GB/s", "us_per_call": round(ev_ms * 1e3 / 4000, 3),
+                                  "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
+                                               "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4)},
+                                  "config": {"workload": "decode", "M": wl.M, "N": wl.N, "K": wl.K, "G": wl.G,
+                                             "mode": "asym_packed", "algorithmic_bytes": nb,
+                                             "weight_copies_rotated": rot.count}}
+    del rot
+    torch.cuda.empty_cache()
 
     # prefill: M = 2048, act-order zero-point weights
     wl = workload("prefill")

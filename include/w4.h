@@ -12,8 +12,9 @@
  *           nibble order 'even_column_low'.)
  *   scales  fp32 [N, ceil(K/G)], row-major: one multiplicative scale per row
  *           and group (same page: _dequantize_validated multiplies).
- *   zeros   uint8 [N, ceil(K/G)] zero-points 0..15, one per byte (W4_ASYM
- *           only; the keras dense.py diff page stores a kernel_zero per group).
+ *   zeros   uint8 [N, ceil(K/G)] zero-points 0..15, one per byte (W4_ASYM;
+ *           the keras dense.py diff page stores a kernel_zero per group), or
+ *           uint8 [N, ceil(ceil(K/G)/2)] two per byte (W4_ASYM_PACKED).
  *   G       group size: a multiple of 8 (>= 8), or per-channel, one group per
  *           row, given as W4_PER_CHANNEL (-1) or any G >= K (keras dense.py
  *           diff page: block size -1, one scale per output unit).  Below,
@@ -31,6 +32,15 @@
  *            Quantizer: lo = min(0, min w), hi = max(0, max w),
  *            s = (hi - lo) / 15, z = clamp(rint(-lo / s), 0, 15),
  *            c = clamp(rint(w / s) + z, 0, 15).
+ *   W4_ASYM_PACKED  W4_ASYM with the zero-points stored two per byte:
+ *            zeros uint8 [N, ceil(NG/2)], group 2j in the low nibble of byte
+ *            j and group 2j+1 in the high nibble (the keras dense.py diff page
+ *            keeps kernel_zero as 4-bit values; the nibble order is the codes'
+ *            order of the LoopQ page; the layout w4_pack_zeros writes).
+ *            Accepted wherever zero-points are read: w4_dequantize,
+ *            w4_linear, w4_linear_noalloc, w4_linear_grad_input.
+ *            w4_quantize_pack and w4_lora_merge write one zero-point per byte
+ *            and return W4_ERR_UNSUPPORTED for this mode.
  *   Both: a group whose computed scale is 0 gets scale 1.  Divisions are IEEE
  *   fp32 round-to-nearest, rint rounds half to even.
  *
@@ -71,7 +81,7 @@ typedef enum {
 } w4_status;
 
 typedef enum { W4_F32 = 0, W4_BF16 = 1 } w4_dtype;
-typedef enum { W4_SYM = 0, W4_ASYM = 1 } w4_mode;
+typedef enum { W4_SYM = 0, W4_ASYM = 1, W4_ASYM_PACKED = 2 } w4_mode;
 
 /* Version of this ABI (W4_ABI_VERSION). */
 int w4_abi_version(void);

@@ -5,7 +5,7 @@ The compute path is the HIP library ``libw4.so`` (C ABI declared in
 Its names are re-exported here on first access, so importing the package (or
 its ``workloads`` module) does not load the library.
 """
-_EXPORTS = ("SYM", "ASYM", "W4Error", "library_path", "load", "quantize_pack",
+_EXPORTS = ("SYM", "ASYM", "ASYM_PACKED", "W4Error", "library_path", "load", "quantize_pack",
             "dequantize", "linear", "linear_workspace_bytes", "linear_noalloc", "linear_grad_input",
             "linear_grad_input_workspace_bytes", "lora_merge",
             "lora_merge_workspace_bytes", "PER_CHANNEL", "n_groups", "pack_zeros",

@@ -40,8 +40,9 @@ w4_status check_format(int64_t N, int64_t K, int64_t G, int mode, const void* ze
   if (G != W4_PER_CHANNEL && G < K && (G < 8 || G % 8 != 0))
     return fail(W4_ERR_INVALID_ARG, "%s: group size G must be a multiple of 8 (>= 8), >= K, or W4_PER_CHANNEL (got %lld)",
                 fn, (long long)G);
-  if (mode != W4_SYM && mode != W4_ASYM) return fail(W4_ERR_INVALID_ARG, "%s: mode must be W4_SYM or W4_ASYM", fn);
-  if (mode == W4_ASYM && zeros == nullptr) return fail(W4_ERR_INVALID_ARG, "%s: W4_ASYM needs zero-points", fn);
+  if (mode != W4_SYM && mode != W4_ASYM && mode != W4_ASYM_PACKED)
+    return fail(W4_ERR_INVALID_ARG, "%s: mode must be W4_SYM, W4_ASYM or W4_ASYM_PACKED", fn);
+  if (mode != W4_SYM && zeros == nullptr) return fail(W4_ERR_INVALID_ARG, "%s: zero-point modes need zero-points", fn);
   if (mode == W4_SYM && zeros != nullptr) return fail(W4_ERR_INVALID_ARG, "%s: W4_SYM takes no zero-points (pass NULL)", fn);
   if (zeros && !aligned16(zeros)) return fail(W4_ERR_INVALID_ARG, "%s: zeros must be 16-byte aligned", fn);
   if (g_idx && !aligned16(g_idx)) return fail(W4_ERR_INVALID_ARG, "%s: g_idx must be 16-byte aligned", fn);
@@ -80,6 +81,8 @@ w4_status w4_quantize_pack(const void* w, int w_dtype, int64_t N, int64_t K, int
   g_last_error.clear();
   const char* fn = "w4_quantize_pack";
   if (w4_status st = check_format(N, K, G, mode, zeros, g_idx, fn)) return st;
+  if (mode == W4_ASYM_PACKED)
+    return fail(W4_ERR_UNSUPPORTED, "%s: writes one zero-point per byte (W4_ASYM); pack them with w4_pack_zeros", fn);
   G = kernel_group(K, G);
   if (w_dtype != W4_F32 && w_dtype != W4_BF16) return fail(W4_ERR_INVALID_ARG, "%s: w_dtype must be W4_F32 or W4_BF16", fn);
   if (!w || !codes || !scales) return fail(W4_ERR_INVALID_ARG, "%s: w, codes and scales must be non-NULL", fn);
@@ -107,7 +110,8 @@ w4_status w4_dequantize(const uint8_t* codes, const float* scales, const uint8_t
   const int64_t NG = (K + G - 1) / G;
   const int64_t chunk_blocks = ((K + 7) / 8 + 255) / 256;
   if (N * chunk_blocks > kMaxGrid) return fail(W4_ERR_UNSUPPORTED, "%s: matrix too large for one launch", fn);
-  w4::DequantArgs a{codes, scales, zeros, g_idx, N, K, G, NG, mode == W4_ASYM, out, out_dtype == W4_BF16};
+  w4::DequantArgs a{codes, scales, zeros, g_idx, N, K, G, NG, mode != W4_SYM, out, out_dtype == W4_BF16,
+                    mode == W4_ASYM_PACKED};
   return hip_status(w4::launch_dequantize(a, static_cast<hipStream_t>(stream)), fn);
 }
 
@@ -139,7 +143,8 @@ w4_status linear_impl(const void* x, int64_t M, const uint8_t* codes, const floa
   const int64_t NG = (K + G - 1) / G;
   hipStream_t s = static_cast<hipStream_t>(stream);
   w4::LinearArgs a{static_cast<const uint16_t*>(x), M, codes, scales, zeros, g_idx, N, K, G, NG,
-                   mode == W4_ASYM, static_cast<const uint16_t*>(bias), static_cast<uint16_t*>(y)};
+                   mode != W4_SYM, static_cast<const uint16_t*>(bias), static_cast<uint16_t*>(y), nullptr,
+                   mode == W4_ASYM_PACKED};
   const size_t need = w4_linear_workspace_bytes(M, N, K, G, mode, g_idx != nullptr);
   if (workspace_bytes < need || (need && !workspace))
     return fail(W4_ERR_INVALID_ARG, "%s: workspace of %zu bytes needed (got %zu)", fn, need, workspace_bytes);
@@ -152,7 +157,7 @@ w4_status linear_impl(const void* x, int64_t M, const uint8_t* codes, const floa
   const int64_t gemm_blocks = K % 8 == 0 ? ((M + 127) / 128) * ((N + 127) / 128) : (M * N + 255) / 256;
   if (N * chunk_blocks > kMaxGrid || gemm_blocks > kMaxGrid)
     return fail(W4_ERR_UNSUPPORTED, "%s: matrix too large for one launch", fn);
-  w4::DequantArgs d{codes, scales, zeros, g_idx, N, K, G, NG, mode == W4_ASYM, workspace, 1};
+  w4::DequantArgs d{codes, scales, zeros, g_idx, N, K, G, NG, mode != W4_SYM, workspace, 1, mode == W4_ASYM_PACKED};
   if (w4::gemm_tiled_ok(M, N, K) && w4::dequantize_tiled_ok(d)) {
     // the weight dequantized into the GEMM's fragment-tiled layout
     if (w4_status st = hip_status(w4::launch_dequantize_tiled(d, s), fn)) return st;
@@ -264,7 +269,7 @@ w4_status w4_linear_grad_input(const void* dy, int64_t M, const uint8_t* codes, 
   }
   const int64_t NG = (K + G - 1) / G;
   w4::GradArgs a{static_cast<const uint16_t*>(dy), M, codes, scales, zeros, g_idx, N, K, G, NG,
-                 mode == W4_ASYM, static_cast<uint16_t*>(dx), static_cast<float*>(workspace)};
+                 mode != W4_SYM, static_cast<uint16_t*>(dx), static_cast<float*>(workspace), mode == W4_ASYM_PACKED};
   return hip_status(w4::launch_grad_input(a, static_cast<hipStream_t>(stream)), fn);
 }
 
@@ -282,6 +287,8 @@ w4_status w4_lora_merge(const uint8_t* codes, const float* scales, const uint8_t
   g_last_error.clear();
   const char* fn = "w4_lora_merge";
   if (w4_status st = check_format(N, K, G, mode, zeros, g_idx, fn)) return st;
+  if (mode == W4_ASYM_PACKED)
+    return fail(W4_ERR_UNSUPPORTED, "%s: takes one zero-point per byte (W4_ASYM); unpack them with w4_unpack_zeros", fn);
   const int64_t Gk = kernel_group(K, G);
   if (rank < 1) return fail(W4_ERR_INVALID_ARG, "%s: rank must be >= 1", fn);
   if (rank > w4::kLoraMaxRank) return fail(W4_ERR_UNSUPPORTED, "%s: rank must be <= %d", fn, w4::kLoraMaxRank);

@@ -252,7 +252,7 @@ __global__ __launch_bounds__(kDThreads) void dequantize_kernel(DequantArgs a, in
   if constexpr (GIDX == 1) {
     for (int g = threadIdx.x; g < NG; g += kDThreads) {
       st[g] = a.scales[n * a.NG + g];
-      if constexpr (ASYM) zt[g] = a.zeros[n * a.NG + g];
+      if constexpr (ASYM) zt[g] = static_cast<uint8_t>(zero_row(a.zeros, n, a.NG, a.zpk)[g]);
     }
     __syncthreads();
   }
@@ -271,7 +271,7 @@ __global__ __launch_bounds__(kDThreads) void dequantize_kernel(DequantArgs a, in
 
   float o[8];
   const float* srow = a.scales + n * a.NG;
-  const uint8_t* zrow = ASYM ? a.zeros + n * a.NG : nullptr;
+  const ZeroRow zrow = zero_row(ASYM ? a.zeros : nullptr, n, a.NG, a.zpk);
   if constexpr (GIDX == 0) {
     const int g = k0 / static_cast<int>(a.G);
     const float s = srow[g];
@@ -702,7 +702,7 @@ __device__ __forceinline__ void dequantize_row(const DequantArgs& a, int64_t n, 
   const int64_t total = a.N * KB;
   const bool last = n == a.N - 1;
   const float* srow = a.scales + n * a.NG;
-  const uint8_t* zrow = ASYM ? a.zeros + n * a.NG : nullptr;
+  const ZeroRow zrow = zero_row(ASYM ? a.zeros : nullptr, n, a.NG, a.zpk);
   const int lane = lane_id();
   const int wave = threadIdx.x / kWave;
   constexpr int kWaves = kDThreads / kWave;
@@ -891,7 +891,7 @@ __global__ __launch_bounds__(kDThreads) void dequantize_act_kernel(DequantArgs a
   for (int p = threadIdx.x; p < nrows * NG; p += kDThreads) {
     const int64_t gi = (row0 + p / NG) * a.NG + p % NG;
     const float s = a.scales[gi];
-    const int z = ASYM ? static_cast<int>(a.zeros[gi]) : 8;
+    const int z = ASYM ? static_cast<int>(zero_row(a.zeros, row0 + p / NG, a.NG, a.zpk)[p % NG]) : 8;
     uint32_t wv[16 * kEB / 4];
 #pragma unroll
     for (int u = 0; u < 16; u += 2) {
@@ -1007,7 +1007,7 @@ __global__ __launch_bounds__(kDThreads) void dequantize_tiled_kernel(DequantArgs
     const int g = min(g_first + gl, NG - 1);
     const int64_t gi = (row0 + r) * a.NG + g;
     const float sc = a.scales[gi];
-    const int z = ASYM ? static_cast<int>(a.zeros[gi]) : 8;
+    const int z = ASYM ? static_cast<int>(zero_row(a.zeros, row0 + r, a.NG, a.zpk)[g]) : 8;
     uint32_t wv[8];
 #pragma unroll
     for (int u = 0; u < 16; u += 2) {

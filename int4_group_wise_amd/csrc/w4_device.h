@@ -39,6 +39,21 @@ __device__ __forceinline__ float wave_sum(float v) {
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
 
+// Zero-points of one weight row: one per byte ([N, NG]), or packed two per
+// byte ([N, ceil(NG/2)], group 2j in the low nibble of byte j, group 2j + 1 in
+// the high nibble).
+struct ZeroRow {
+  const uint8_t* p;
+  bool packed;
+  __device__ __forceinline__ uint32_t operator[](int64_t g) const {
+    return packed ? (static_cast<uint32_t>(p[g >> 1]) >> (4 * (g & 1))) & 15u : static_cast<uint32_t>(p[g]);
+  }
+};
+__device__ __forceinline__ ZeroRow zero_row(const uint8_t* z, int64_t n, int64_t NG, int packed) {
+  if (!z) return ZeroRow{nullptr, false};
+  return ZeroRow{z + n * (packed ? (NG + 1) / 2 : NG), packed != 0};
+}
+
 // 0x0F0F0F0F in a VGPR, hidden from the compiler.  After `d & 0x0F0F0F0F`
 // with the constant it knows every byte's high nibble is zero and extracts
 // bytes 1..3 with v_bfe_u32 before converting; with the mask in a register

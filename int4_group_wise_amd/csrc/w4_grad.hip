@@ -125,7 +125,7 @@ __global__ __launch_bounds__(kGThreads) void grad_split_kernel(GradArgs a, int r
 #pragma unroll
       for (int e = 0; e < kNGrp; ++e) {
         s[u][e] = a.scales[n * NG + g[e]];
-        z[u][e] = ASYM ? static_cast<float>(a.zeros[n * NG + g[e]]) : 8.0f;
+        z[u][e] = ASYM ? static_cast<float>(zero_row(a.zeros, n, NG, a.zpk)[g[e]]) : 8.0f;
       }
 #pragma unroll
       for (int m = 0; m < MT; ++m) dyr[u][m] = load_bf16_uniform(a.dy, static_cast<int64_t>(min(m, M - 1)) * a.N + n);
@@ -338,7 +338,7 @@ __global__ __launch_bounds__(kGThreads) void dequantize_t_kernel(DequantArgs a, 
       const int r = e / NG, g = e % NG;
       const int64_t gi = (n0 + r) * a.NG + g;
       stab[r * SS + g] = a.scales[gi];
-      if constexpr (ASYM) ztab[r * ZS + g] = a.zeros[gi];
+      if constexpr (ASYM) ztab[r * ZS + g] = static_cast<uint8_t>(zero_row(a.zeros, n0 + r, a.NG, a.zpk)[g]);
     }
   }
   __syncthreads();
@@ -351,7 +351,7 @@ __global__ __launch_bounds__(kGThreads) void dequantize_t_kernel(DequantArgs a, 
         const uint32_t nib = (d[e >> 3] >> (4 * (e & 7))) & 15u;
         const int gi = gsh[kq + e];
         const float sc = TAB ? stab[nl * SS + gi] : a.scales[n * a.NG + gi];
-        const int zp = ASYM ? (TAB ? ztab[nl * ZS + gi] : a.zeros[n * a.NG + gi]) : 8;
+        const int zp = ASYM ? (TAB ? ztab[nl * ZS + gi] : static_cast<int>(zero_row(a.zeros, n, a.NG, a.zpk)[gi])) : 8;
         const float val = ASYM ? static_cast<float>(static_cast<int>(nib) - zp)
                                : static_cast<float>(static_cast<int>(nib ^ 8u) - 8);
         w[e] = val * sc;
@@ -451,7 +451,7 @@ hipError_t launch_grad_input(const GradArgs& a, hipStream_t s) {
     return hipGetLastError();
   }
   // transposed weight into the workspace, then the bf16 GEMM
-  DequantArgs d{a.codes, a.scales, a.zeros, a.g_idx, a.N, a.K, a.G, a.NG, a.asym, nullptr, 1};
+  DequantArgs d{a.codes, a.scales, a.zeros, a.g_idx, a.N, a.K, a.G, a.NG, a.asym, nullptr, 1, a.zpk};
   uint16_t* wt = reinterpret_cast<uint16_t*>(a.partial);
   const dim3 grid(static_cast<uint32_t>((a.K + kTT - 1) / kTT), static_cast<uint32_t>((a.N + kTT - 1) / kTT));
   const size_t lds0 = kTT * (kTT + 2) * 2 + kTT * 4;

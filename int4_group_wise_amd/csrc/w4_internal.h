@@ -28,6 +28,7 @@ struct DequantArgs {
   int asym;
   void* out;
   int out_bf16;         // 0: fp32 output, 1: bf16 output
+  int zpk;              // zero-points packed two per byte [N, ceil(NG/2)]
 };
 
 struct LinearArgs {
@@ -42,6 +43,7 @@ struct LinearArgs {
   const uint16_t* bias; // bf16 [N] or NULL
   uint16_t* y;          // bf16 [M, N]
   float* partial;       // workspace for split-K partial sums (batched decode), or NULL
+  int zpk;              // zero-points packed two per byte [N, ceil(NG/2)]
 };
 
 struct GradArgs {
@@ -55,6 +57,7 @@ struct GradArgs {
   int asym;
   uint16_t* dx;         // bf16 [M, K]
   float* partial;       // workspace: fp32 slice partials (M <= 16) or bf16 Wd^T (M > 16)
+  int zpk;              // zero-points packed two per byte [N, ceil(NG/2)]
 };
 
 // Input-gradient plan: M <= kGradSkinnyMax splits the rows of W into `slices`

@@ -101,7 +101,7 @@ __device__ __forceinline__ void load_slice(const LinearArgs& a, int64_t row0, in
     const u32x4 t = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(crow + coff));
     s.cw[r] = make_uint4(t[0], t[1], t[2], t[3]);
     s.sc[r] = (a.scales + n * a.NG)[g];
-    s.zb[r] = ASYM ? (a.zeros + n * a.NG)[g] : 8u;
+    s.zb[r] = ASYM ? zero_row(a.zeros, n, a.NG, a.zpk)[g] : 8u;
   }
 }
 
@@ -315,7 +315,7 @@ __global__ __launch_bounds__(kStreamWG * kWave) void gemv_stream_kernel(LinearAr
 #pragma unroll
     for (int j = 0; j < S; ++j) {
       sc[r][j] = a.scales[n * a.NG + g[j]];
-      zb[r][j] = ASYM ? a.zeros[n * a.NG + g[j]] : 8u;
+      zb[r][j] = ASYM ? zero_row(a.zeros, n, a.NG, a.zpk)[g[j]] : 8u;
     }
     __builtin_amdgcn_sched_barrier(0);   // issue order = use order, row by row
   }
@@ -528,7 +528,6 @@ __global__ __launch_bounds__(kTileWaves * kWave, 4) void skinny_mfma_kernel(Line
   const uint32_t rload = static_cast<uint32_t>(min(static_cast<int64_t>(rq), a.N - 1 - n0));
   const uint8_t* cbase = a.codes + n0 * KB;
   const float* sbase = a.scales + n0 * a.NG;
-  const uint8_t* zbase = ASYM ? a.zeros + n0 * a.NG : nullptr;
   u32x4 cw[KR];
   // table loads: lane quad r covers row r, lane cq takes groups cq, cq + 4, ...
   constexpr int kTG = GU == 1 ? KR + 1 : KR * GU;     // groups per row per round, at most
@@ -545,7 +544,7 @@ __global__ __launch_bounds__(kTileWaves * kWave, 4) void skinny_mfma_kernel(Line
     for (int j = 0; j < kTabLoads; ++j) {
       const uint32_t gg = static_cast<uint32_t>(min(4 * j + static_cast<int>(cq), ngt - 1));
       tabs[j] = sbase[trow + gg];
-      tabz[j] = ASYM ? zbase[trow + gg] : 8u;
+      tabz[j] = ASYM ? zero_row(a.zeros, n0 + rload, a.NG, a.zpk)[g_first + gg] : 8u;
     }
 #pragma unroll
     for (int j = 0; j < KR; ++j) {
@@ -736,7 +735,7 @@ __device__ __forceinline__ void rows_issue(const LinearArgs& a, int b, int nkb, 
   for (int i = 0; i < 4; ++i) {
     const uint32_t gg = static_cast<uint32_t>(min(4 * i + static_cast<int>(cq), ngt - 1));
     R.ts[i] = a.scales[trow + gg];
-    R.tz[i] = ASYM ? a.zeros[trow + gg] : 8u;
+    R.tz[i] = ASYM ? zero_row(a.zeros, n0 + rload, a.NG, a.zpk)[g_first + gg] : 8u;
   }
   __builtin_amdgcn_sched_barrier(0);
   // code words
@@ -935,7 +934,7 @@ __global__ __launch_bounds__(kGemvWaves * kWave) void gemv_generic_kernel(Linear
   const int G = static_cast<int>(a.G);
   const uint8_t* crow = a.codes + n * static_cast<int64_t>(KB);
   const float* srow = a.scales + n * a.NG;
-  const uint8_t* zrow = ASYM ? a.zeros + n * a.NG : nullptr;
+  const ZeroRow zrow = zero_row(ASYM ? a.zeros : nullptr, n, a.NG, a.zpk);
   float acc[16];
 #pragma unroll
   for (int m = 0; m < 16; ++m) acc[m] = 0.0f;

@@ -15,6 +15,7 @@ import torch
 
 SYM = 0    # W4_SYM: signed two's-complement nibbles
 ASYM = 1   # W4_ASYM: unsigned nibbles with per-group zero-points
+ASYM_PACKED = 2   # W4_ASYM_PACKED: the same, zero-points packed two per byte
 _F32, _BF16 = 0, 1
 
 _STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported", 3: "HIP error"}
@@ -115,7 +116,9 @@ def _mode(mode) -> int:
         return SYM
     if mode in (ASYM, "asym"):
         return ASYM
-    raise ValueError("mode must be 'sym' or 'asym'")
+    if mode in (ASYM_PACKED, "asym_packed"):
+        return ASYM_PACKED
+    raise ValueError("mode must be 'sym', 'asym' or 'asym_packed'")
 
 
 PER_CHANNEL = -1   # group size: one group per row (W4_PER_CHANNEL)
@@ -132,10 +135,10 @@ def _format_args(N, K, G, mode, codes, scales, zeros, g_idx):
     NG = n_groups(K, G)
     _dev(codes, "codes", torch.uint8, (N, (K + 1) // 2))
     _dev(scales, "scales", torch.float32, (N, NG))
-    if mode == ASYM:
+    if mode in (ASYM, ASYM_PACKED):
         if zeros is None:
             raise ValueError("zero-point mode needs zeros")
-        _dev(zeros, "zeros", torch.uint8, (N, NG))
+        _dev(zeros, "zeros", torch.uint8, (N, NG) if mode == ASYM else (N, (NG + 1) // 2))
     elif zeros is not None:
         raise ValueError("signed mode takes no zeros")
     if g_idx is not None:
