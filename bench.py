@@ -283,6 +283,35 @@ def bench_secondary(w4):
     del rot
     torch.cuda.empty_cache()
 
+    # act-order decode: the decode shape with g_idx = perm // 128 (a scattered
+    # group per column, as in the prefill workload's weight)
+    wl = workload("decode", act_order=True)
+    t = generate(wl)
+    gi = t["g_idx"].to(dev)
+    c, s, z = w4.quantize_pack(t["w"].to(dev), wl.G, wl.mode, gi)
+    x, b = t["x"].to(dev), t["bias"].to(dev)
+    del t
+    rot = Rotation([c, s, z], 2 * MALL_BYTES)
+    del c, s, z
+    ys = [torch.empty(wl.M, wl.N, dtype=torch.bfloat16, device=dev) for _ in range(rot.count)]
+
+    def call_a(i):
+        cc, ss, zz = rot.sets[i]
+        w4.linear(x, cc, ss, zz, gi, wl.K, wl.G, wl.mode, b, out=ys[i])
+
+    steps = 2000
+    ev_ms, _ = time_graph(call_a, rot.count * 4, steps, rot.count * 4, rot.count)
+    nb = algorithmic_bytes_linear(wl.M, wl.N, wl.K, wl.G, True, True) + wl.K * 4   # + g_idx
+    gbs = nb * steps / (ev_ms * 1e-3) / 1e9
+    out["decode_act_order"] = {"metric": "W4A16 linear HBM GB/s M=1, act-order g_idx", "value": round(gbs, 1),
+                               "unit": "GB/s", "us_per_call": round(ev_ms * 1e3 / steps, 3),
+                               "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
+                                            "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4)},
+                               "config": {"workload": "decode", "M": wl.M, "N": wl.N, "K": wl.K, "G": wl.G,
+                                          "mode": wl.mode, "act_order": True, "weight_copies_rotated": rot.count}}
+    del rot, ys, x, b, gi
+    torch.cuda.empty_cache()
+
     # prefill: M = 2048, act-order zero-point weights
     wl = workload("prefill")
     t = generate(wl)

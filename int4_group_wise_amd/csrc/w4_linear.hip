@@ -376,6 +376,165 @@ __global__ __launch_bounds__(kStreamWG * kWave) void gemv_stream_kernel(LinearAr
 }
 
 // ---------------------------------------------------------------------------
+// Decode GEMV with an act-order g_idx (M <= 4; K = 2048 S P): the columns of
+// a group are scattered over the row, so every weight needs its own group's
+// scale and zero-point.  The workgroup's rows get a table in LDS holding, for
+// every (row, group), the 16 possible bf16 values fp32(v) * s of a nibble (the
+// values every other path dequantizes to); a weight is then one LDS read at
+// the byte offset of its column's group (from g_idx, computed once per wave
+// for all rows) plus its nibble.  Two adjacent columns' values form one bf16
+// pair for v_dot2_f32_bf16 against the activations' natural pairs.  Rows,
+// slices and the load order are as in the streaming GEMV: a set of P waves
+// owns R rows, lane l of wave h takes slices l + 64 (P j + h), every load is
+// issued before the table is built.
+// ---------------------------------------------------------------------------
+constexpr int kActWG = 4;   // waves per workgroup
+
+
+template <int R, int S, int P, int MT, bool ASYM>
+__global__ __launch_bounds__(kActWG * kWave) void gemv_act_kernel(LinearArgs a) {
+  static_assert(R >= 1 && R <= 16 && (P == 1 || P == 2), "row set shape");
+  constexpr int H = (R + 3) / 4;
+  constexpr int SETS = kActWG / P;
+  extern __shared__ __attribute__((aligned(16))) uint8_t asm_[];
+  __shared__ float red[kActWG][MT][4 * H];
+  const int lane = lane_id();
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int h = w % P, set = w / P;
+  const int64_t set0 = static_cast<int64_t>(blockIdx.x) * SETS;   // first row set of the workgroup
+  const int64_t row0 = (set0 + set) * R;                          // rows past N: computed, not stored
+  const int M = static_cast<int>(a.M);
+  const int NG = static_cast<int>(a.NG);
+  const int64_t KB = a.K / 2;
+  auto slice = [&](int j) -> uint32_t { return static_cast<uint32_t>(lane) + 64u * (P * j + h); };
+
+  // 1. loads: activations, group indices and every row's code words of the lane's slices
+  u32x4 xr[MT][S][4];
+#pragma unroll
+  for (int m = 0; m < MT; ++m)
+#pragma unroll
+    for (int j = 0; j < S; ++j)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        xr[m][j][i] = *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint8_t*>(a.x + static_cast<int64_t>(min(m, M - 1)) * a.K) +
+                                                      64u * slice(j) + 16 * i);
+  u32x4 gq[S][8];
+#pragma unroll
+  for (int j = 0; j < S; ++j)
+#pragma unroll
+    for (int q = 0; q < 8; ++q) gq[j][q] = *reinterpret_cast<const u32x4*>(a.g_idx + 32 * slice(j) + 4 * q);
+  uint32_t braw[H];
+#pragma unroll
+  for (int hh = 0; hh < H; ++hh) {
+    const int64_t n = min(row0 + 4 * hh + (lane >> 4), a.N - 1);
+    braw[hh] = a.bias ? a.bias[n] : a.x[0];
+  }
+  u32x4 cw[R][S];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int64_t n = min(row0 + r, a.N - 1);
+#pragma unroll
+    for (int j = 0; j < S; ++j)
+      cw[r][j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(a.codes + n * KB + 16u * slice(j)));
+  }
+
+  // 2. the value tables of the workgroup's rows: entry (set, group g, row r,
+  //    nibble u) at set NG R 32 + g R 32 + r 32 + 2 u, so that a weight's
+  //    address is its column's group offset plus a per-row constant plus 2 u
+  constexpr int kGroupBytes = R * 32;
+  const int entries = SETS * R * NG;
+  for (int e = threadIdx.x; e < entries; e += kActWG * kWave) {
+    const int st = e / (R * NG), g = (e / R) % NG, r = e % R;
+    const int64_t n = min((set0 + st) * R + r, a.N - 1);
+    const float sc = a.scales[n * a.NG + g];
+    const int z = ASYM ? static_cast<int>(zero_row(a.zeros, n, a.NG, a.zpk)[g]) : 8;
+    uint32_t wv[8];
+#pragma unroll
+    for (int u = 0; u < 16; u += 2) {
+      // value formed in integers (signed codes: (u ^ 8) - 8), one fp32
+      // multiply, then bf16 pairs rounded to nearest even (v_cvt_pk_bf16_f32)
+      const float v0 = static_cast<float>((ASYM ? u : (u ^ 8)) - z) * sc;
+      const float v1 = static_cast<float>((ASYM ? u + 1 : ((u + 1) ^ 8)) - z) * sc;
+      wv[u / 2] = __builtin_bit_cast(uint32_t, bf16x2_t{static_cast<__bf16>(v0), static_cast<__bf16>(v1)});
+    }
+    u32x4* dst = reinterpret_cast<u32x4*>(asm_ + (st * NG + g) * kGroupBytes + 32 * r);
+    dst[0] = u32x4{wv[0], wv[1], wv[2], wv[3]};
+    dst[1] = u32x4{wv[4], wv[5], wv[6], wv[7]};
+  }
+  __syncthreads();
+
+  // 3. byte offset of each column's group in this set's table
+  const uint32_t set_base = static_cast<uint32_t>(set * NG * kGroupBytes);
+  uint32_t goff[S][32];
+#pragma unroll
+  for (int j = 0; j < S; ++j)
+#pragma unroll
+    for (int q = 0; q < 8; ++q)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        goff[j][4 * q + e] = set_base + static_cast<uint32_t>(min(max(static_cast<int>(gq[j][q][e]), 0), NG - 1)) * kGroupBytes;
+
+  // 4. rows: one lookup per weight, a dot2 per column pair and activation row
+  float tot[MT][4 * H];
+#pragma unroll
+  for (int m = 0; m < MT; ++m)
+#pragma unroll
+    for (int r = 0; r < 4 * H; ++r) tot[m][r] = 0.0f;
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const uint8_t* trow = asm_ + 32 * r;
+#pragma unroll
+    for (int j = 0; j < S; ++j)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t d = cw[r][j][i];
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+          const uint32_t u0 = __builtin_amdgcn_ubfe(d, 8 * p, 4), u1 = __builtin_amdgcn_ubfe(d, 8 * p + 4, 4);
+          const uint32_t lo = *reinterpret_cast<const uint16_t*>(trow + goff[j][8 * i + 2 * p] + 2 * u0);
+          const uint32_t hi = *reinterpret_cast<const uint16_t*>(trow + goff[j][8 * i + 2 * p + 1] + 2 * u1);
+          const uint32_t wp = lo | (hi << 16);
+#pragma unroll
+          for (int m = 0; m < MT; ++m) tot[m][r] = dot2_bf16(wp, xr[m][j][i][p], tot[m][r]);
+        }
+      }
+  }
+
+  // 5. wave sums (lane l: row row0 + 4 hh + l / 16), the two waves of a set
+  //    added in a fixed order, bias, store
+  float v[MT][H];
+#pragma unroll
+  for (int m = 0; m < MT; ++m)
+#pragma unroll
+    for (int hh = 0; hh < H; ++hh)
+      v[m][hh] = wave_sum4(tot[m][4 * hh], tot[m][4 * hh + 1], tot[m][4 * hh + 2], tot[m][4 * hh + 3]);
+  if constexpr (P == 2) {
+    if (h == 1 && (lane & 15) == 0) {
+#pragma unroll
+      for (int m = 0; m < MT; ++m)
+#pragma unroll
+        for (int hh = 0; hh < H; ++hh) red[w][m][4 * hh + (lane >> 4)] = v[m][hh];
+    }
+    __syncthreads();
+    if (h == 1) return;
+#pragma unroll
+    for (int m = 0; m < MT; ++m)
+#pragma unroll
+      for (int hh = 0; hh < H; ++hh) v[m][hh] += red[w + 1][m][4 * hh + (lane >> 4)];
+  }
+#pragma unroll
+  for (int hh = 0; hh < H; ++hh) {
+    const int64_t n = row0 + 4 * hh + (lane >> 4);
+    const float bias = a.bias ? bf16_to_f32(braw[hh]) : 0.0f;
+    if ((lane & 15) == 0 && 4 * hh + (lane >> 4) < R && n < a.N) {
+#pragma unroll
+      for (int m = 0; m < MT; ++m)
+        if (m < M) a.y[static_cast<int64_t>(m) * a.N + n] = static_cast<uint16_t>(f32_to_bf16(v[m][hh] + bias));
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Matrix-core decode kernel (M <= 4): v_mfma_f32_16x16x32_bf16 with the
 // activations as the 16-row A operand (rows m >= M are padding) and 16 weight
 // rows as the B operand.  The only per-weight VALU work is the nibble -> bf16
@@ -1011,6 +1170,49 @@ hipError_t launch_stream(const LinearArgs& a, hipStream_t s) {
   return a.asym ? launch_stream2<true>(a, s) : launch_stream2<false>(a, s);
 }
 
+// Act-order decode: rows per set as the streaming GEMV; P = 2 waves per set
+// when K is a multiple of 4096 (S = K / 4096 slices per wave), else P = 1
+// with K = 2048 (one slice).
+template <int R, int S, int P, int MT>
+hipError_t launch_act4(const LinearArgs& a, hipStream_t s) {
+  constexpr int sets_per_wg = kActWG / P;
+  const int64_t sets = (a.N + R - 1) / R;
+  const size_t lds = static_cast<size_t>(sets_per_wg) * R * 32 * a.NG;
+  const dim3 grid(static_cast<uint32_t>((sets + sets_per_wg - 1) / sets_per_wg)), block(kActWG * kWave);
+  if (a.asym) gemv_act_kernel<R, S, P, MT, true><<<grid, block, lds, s>>>(a);
+  else gemv_act_kernel<R, S, P, MT, false><<<grid, block, lds, s>>>(a);
+  return hipGetLastError();
+}
+
+template <int S, int P, int MT>
+hipError_t launch_act3(const LinearArgs& a, hipStream_t s) {
+  switch (stream_rows(a.N)) {
+    case 2: return launch_act4<2, S, P, MT>(a, s);
+    case 4: return launch_act4<4, S, P, MT>(a, s);
+    case 7: return launch_act4<7, S, P, MT>(a, s);
+    default: return launch_act4<8, S, P, MT>(a, s);
+  }
+}
+
+template <int MT>
+hipError_t launch_act2(const LinearArgs& a, hipStream_t s) {
+  if (a.K == 2048) return launch_act3<1, 1, MT>(a, s);
+  if (a.K == 4096) return launch_act3<1, 2, MT>(a, s);
+  return launch_act3<2, 2, MT>(a, s);   // K = 8192
+}
+
+// Act-order decode kernel: g_idx, M <= 4, K of 2048, 4096 or 8192, and a
+// value table of at most 128 groups per row (LDS: 4 sets x 8 rows x 4 KB).
+bool act_ok(const LinearArgs& a) {
+  return a.g_idx != nullptr && a.M <= 4 && (a.K == 2048 || a.K == 4096 || a.K == 8192) && a.NG <= 128;
+}
+
+hipError_t launch_act(const LinearArgs& a, hipStream_t s) {
+  if (a.M == 1) return launch_act2<1>(a, s);
+  if (a.M == 2) return launch_act2<2>(a, s);
+  return launch_act2<4>(a, s);
+}
+
 // The streaming decode GEMV: M = 1, K = 4096, contiguous groups with G a
 // multiple of 32.
 bool stream_ok(const LinearArgs& a) {
@@ -1113,6 +1315,7 @@ hipError_t launch_linear_skinny(const LinearArgs& a, hipStream_t s) {
     return launch_mfma2<4>(a, s);
   }
   if (stream_ok(a)) return launch_stream(a, s);
+  if (act_ok(a)) return launch_act(a, s);
   if (dot2_ok(a)) {
     if (a.M == 1) return launch_dot2<1>(a, s);
     if (a.M == 2) return launch_dot2<2>(a, s);

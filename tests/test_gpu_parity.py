@@ -167,6 +167,13 @@ CASES = [
     (1, 14339, 4096, 64, "sym", False, "f32", "none"),
     (1, 20001, 4096, 128, "asym", False, "bf16", "randn"),
     (1, 64, 512, 128, "asym", True, "f32", "none"),     # act-order decode
+    # act-order decode with LDS value tables (M <= 4; K = 2048, 4096, 8192):
+    # 2, 4, 7 and 8 rows per set, one and two waves per set, row tails
+    (1, 300, 4096, 128, "asym", True, "f32", "randn"),
+    (2, 37, 2048, 64, "sym", True, "bf16", "none"),
+    (4, 14339, 4096, 128, "asym", True, "f32", "randn"),
+    (3, 5000, 8192, 64, "sym", True, "f32", "none"),
+    (1, 20000, 2048, 32, "asym", True, "bf16", "randn"),
     (16, 48, 1000, 40, "asym", True, "bf16", "none"),
     (17, 130, 200, 8, "asym", False, "f32", "randn"),   # prefill, K % 64 != 0, N tail
     (40, 70, 99, 16, "sym", False, "f32", "none"),      # prefill, K % 8 != 0
