@@ -3,9 +3,10 @@
 quantize_pack and dequantize must be bit-exact; the linear must reach
 normwise relative error <= 5e-3 and per-element error <= 2e-2 * max|y_ref|
 against the fp64 oracle, and must be exact on an identity activation (one
-non-zero product per output).  Full-size workloads compare sampled rows
-(weight rows and output features are independent), small shapes compare
-everything, including ragged tails and the degenerate cases.
+non-zero product per output).  The five workloads are compared in full at
+their real sizes (every weight row, every output), in the launch
+configuration the benchmark times; small shapes cover ragged tails and the
+degenerate cases.
 """
 import numpy as np
 import pytest
@@ -33,14 +34,6 @@ def _bits(t: torch.Tensor) -> np.ndarray:
 
 def _mode(m):
     return O.SYM if m in ("sym", 0) else O.ASYM
-
-
-def _sample_rows(N, count=256, seed=0):
-    rng = np.random.default_rng(seed)
-    head = np.arange(min(N, 16))
-    tail = np.arange(max(0, N - 16), N)
-    rnd = rng.choice(N, size=min(N, count), replace=False)
-    return np.unique(np.concatenate([head, tail, rnd]))
 
 
 def _check_codec(w, G, mode, g_idx=None, rows=None, label=""):
@@ -101,39 +94,45 @@ def test_tiny_full():
     _check_linear(t["x"], c, s, z, None, wl.K, wl.G, wl.mode, t["bias"], orc, "tiny")
 
 
-def test_decode_full_size_sampled():
+@pytest.mark.timeout(900)
+def test_decode_full_size():
+    """Every one of the 14336 rows: codes, scales, zero-points, both
+    dequantized forms and every output of the linear."""
     wl = workload("decode")
     t = generate(wl)
-    rows = _sample_rows(wl.N, 512, 1)
-    c, s, z, orc = _check_codec(t["w"], wl.G, wl.mode, rows=rows, label="decode")
+    c, s, z, orc = _check_codec(t["w"], wl.G, wl.mode, label="decode")
     _check_linear(t["x"], c, s, z, None, wl.K, wl.G, wl.mode, t["bias"], orc, "decode")
 
 
-def test_batched_decode_full_size_sampled():
+@pytest.mark.timeout(900)
+def test_batched_decode_full_size():
+    """Every one of the 28672 rows, and all 16 x 28672 outputs."""
     wl = workload("batched_decode")
     t = generate(wl)
-    rows = _sample_rows(wl.N, 384, 2)
-    c, s, z, orc = _check_codec(t["w"], wl.G, wl.mode, rows=rows, label="batched_decode")
+    c, s, z, orc = _check_codec(t["w"], wl.G, wl.mode, label="batched_decode")
+    del t["w"]
     _check_linear(t["x"], c, s, z, None, wl.K, wl.G, wl.mode, None, orc, "batched_decode")
 
 
+@pytest.mark.timeout(900)
 def test_prefill_full_size():
+    """Every weight row and all 2048 x 4096 outputs (act-order)."""
     wl = workload("prefill")
     t = generate(wl)
-    rows = _sample_rows(wl.N, 1024, 3)
-    c, s, z, orc = _check_codec(t["w"], wl.G, wl.mode, t["g_idx"], rows=rows, label="prefill")
+    c, s, z, orc = _check_codec(t["w"], wl.G, wl.mode, t["g_idx"], label="prefill")
     _check_linear(t["x"], c, s, z, t["g_idx"], wl.K, wl.G, wl.mode, None, orc, "prefill")
 
 
-def test_codec_full_size_sampled():
+@pytest.mark.timeout(900)
+def test_codec_full_size():
+    """Every one of the 28672 odd-width bf16 rows."""
     wl = workload("codec")
     t = generate(wl)
-    rows = _sample_rows(wl.N, 512, 4)
-    _check_codec(t["w"], wl.G, wl.mode, rows=rows, label="codec")
+    _check_codec(t["w"], wl.G, wl.mode, label="codec")
     # the same codes also drive an odd-K skinny linear (x bf16 [1, 8191] ~ N(0, 1))
     g = torch.Generator().manual_seed(0)
     x = torch.randn(1, wl.K, generator=g).to(torch.bfloat16)
-    c, s, z, orc = _check_codec(t["w"][:2048], wl.G, wl.mode, rows=_sample_rows(2048, 256, 5), label="codec-head")
+    c, s, z, orc = _check_codec(t["w"][:2048], wl.G, wl.mode, label="codec-head")
     _check_linear(x, c, s, z, None, wl.K, wl.G, wl.mode, None, orc, "codec-linear")
 
 
@@ -522,8 +521,9 @@ def test_grad_input_decode_size():
     _check_grad(1, 14336, 4096, 128, "asym", False, seed=30, label="decode-size")
 
 
-def test_grad_input_prefill_size_sampled():
-    _check_grad(2048, 4096, 4096, 128, "asym", True, seed=31, cols=_sample_rows(4096, 256, 6), label="prefill-size")
+@pytest.mark.timeout(900)
+def test_grad_input_prefill_size():
+    _check_grad(2048, 4096, 4096, 128, "asym", True, seed=31, cols=None, label="prefill-size")
 
 
 @pytest.mark.parametrize("M,K,mode", [(3, 520, "sym"), (24, 256, "asym")])
@@ -629,10 +629,11 @@ def test_lora_merge_zero_update():
     _check_lora(40, 512, 32, "sym", False, 4, 0.0, seed=6, label="zero update")
 
 
-def test_lora_merge_decode_layer_sampled():
-    """The decode layer's weight (14336 x 4096, G = 128, zero-points), rank 16."""
-    _check_lora(14336, 4096, 128, "asym", False, 16, 2.0, seed=7, rows=_sample_rows(14336, 128, 8),
-                label="decode-size")
+@pytest.mark.timeout(900)
+def test_lora_merge_decode_layer():
+    """The decode layer's weight (14336 x 4096, G = 128, zero-points), rank 16,
+    every row."""
+    _check_lora(14336, 4096, 128, "asym", False, 16, 2.0, seed=7, rows=None, label="decode-size")
 
 
 # ---------------------------------------------------------------------------
@@ -682,16 +683,16 @@ def test_q4_0_decodes_arbitrary_blocks():
     assert np.array_equal(got.view(np.uint32), O.q4_0_dequantize(blk, "f32").view(np.uint32))
 
 
-def test_q4_0_full_size_sampled():
-    """The codec weight's shape at K = 8192 (bf16 [28672, 8192]), sampled rows."""
+@pytest.mark.timeout(900)
+def test_q4_0_full_size():
+    """The codec weight's shape at K = 8192 (bf16 [28672, 8192]), every block."""
     wl = workload("codec", K=8192)
     t = generate(wl)
     w = t["w"]
     blocks = w4.q4_0_quantize(w.to(DEV))
     torch.cuda.synchronize()
-    rows = _sample_rows(wl.N, 256, 9)
-    ref = O.q4_0_quantize(_np_w(w[torch.from_numpy(rows)]))
-    assert np.array_equal(blocks[torch.from_numpy(rows).to(DEV)].cpu().numpy(), ref)
+    ref = O.q4_0_quantize(_np_w(w))
+    assert np.array_equal(blocks.cpu().numpy(), ref)
 
 
 @pytest.mark.parametrize("N,NG", [(1, 1), (5, 7), (300, 32), (1000, 257), (3, 6), (7, 22), (28672, 256)])
