@@ -828,9 +828,8 @@ __global__ __launch_bounds__(kTileWaves * kWave, 4) void skinny_mfma_kernel(Line
 // activations [16 rows x 512 columns] are staged once in LDS (re-paired, with
 // sums per 32 columns) and read by all 4 waves.  Batches are double-buffered:
 // batch b + 1 is loaded (activations, scale/zero tables, code words, in that
-// order) while batch b is computed.  Code words are loaded by lane quads
-// (64 contiguous bytes of a row) and re-laid out through a 1 KB wave-private
-// LDS scratch, as in the decode kernel.
+// order) while batch b is computed.  Code words are loaded straight into the
+// operand layout (lane l: row l % 16, 16-byte quarter l / 16 of a block).
 // ---------------------------------------------------------------------------
 constexpr int kRowsWaves = 4;
 constexpr int kRowsKB = 4;                      // 128-column blocks per batch
@@ -857,7 +856,7 @@ __host__ __device__ inline RowsLayout rows_layout() {
   L.xs_off = 2 * L.xbuf;
   L.xsbuf = 16 * kRowsKB * 4 * 4;               // [16 rows][kRowsKB * 4 units] floats
   L.wave_off = L.xs_off + 2 * L.xsbuf;
-  L.wave_bytes = 2048 + ((16 * kRowsTS * 4 + 16 * kRowsTS + 15) & ~15);
+  L.wave_bytes = (16 * kRowsTS * 4 + 16 * kRowsTS + 15) & ~15;
   L.bytes = L.wave_off + kRowsWaves * L.wave_bytes;
   return L;
 }
@@ -897,12 +896,16 @@ __device__ __forceinline__ void rows_issue(const LinearArgs& a, int b, int nkb, 
     R.tz[i] = ASYM ? zero_row(a.zeros, n0 + rload, a.NG, a.zpk)[g_first + gg] : 8u;
   }
   __builtin_amdgcn_sched_barrier(0);
-  // code words
-  const uint8_t* crow = a.codes + (n0 + rload) * (a.K / 2);
+  // code words, straight into the operand layout: lane l holds row l % 16,
+  // 16-byte quarter l / 16 of each 128-column block (the 16 rows' 64 bytes
+  // per instruction; an LDS relayout of row-contiguous loads measured 2%
+  // slower)
+  const uint32_t rd = static_cast<uint32_t>(min(static_cast<int64_t>(lane & 15), a.N - 1 - n0));
+  const uint8_t* crow = a.codes + (n0 + rd) * (a.K / 2);
 #pragma unroll
   for (int j = 0; j < kRowsKB; ++j) {
     const uint32_t kb = static_cast<uint32_t>(min(kbf + j, nkb - 1));
-    R.cw[j] = *reinterpret_cast<const u32x4*>(crow + 64u * kb + 16u * cq);
+    R.cw[j] = *reinterpret_cast<const u32x4*>(crow + 64u * kb + 16u * static_cast<uint32_t>(lane >> 4));
   }
   __builtin_amdgcn_sched_barrier(0);
 }
@@ -930,8 +933,8 @@ __device__ __forceinline__ void rows_stage(const LinearArgs& a, int b, int lane,
   }
   reinterpret_cast<float*>(smem + L.xs_off + (b & 1) * L.xsbuf)[m * (kRowsKB * 4) + (uu ^ xs_swz(m))] = live ? sum : 0.0f;
   const int rq = lane >> 2, cq = lane & 3;
-  float* stab = reinterpret_cast<float*>(wave_lds + 2048);
-  uint8_t* ztab = wave_lds + 2048 + 16 * kRowsTS * 4;
+  float* stab = reinterpret_cast<float*>(wave_lds);
+  uint8_t* ztab = wave_lds + 16 * kRowsTS * 4;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     stab[rq * kRowsTS + 4 * i + cq] = R.ts[i];
@@ -945,10 +948,8 @@ __device__ __forceinline__ void rows_compute(const LinearArgs& a, int b, int nkb
                                              uint8_t* wave_lds, float (&out)[4]) {
   const uint32_t G = static_cast<uint32_t>(a.G);
   const int n = lane & 15, q = lane >> 4;
-  const int rq = lane >> 2, cq = lane & 3;
-  u32x4* scratch = reinterpret_cast<u32x4*>(wave_lds);
-  const float* stab = reinterpret_cast<const float*>(wave_lds + 2048);
-  const uint8_t* ztab = wave_lds + 2048 + 16 * kRowsTS * 4;
+  const float* stab = reinterpret_cast<const float*>(wave_lds);
+  const uint8_t* ztab = wave_lds + 16 * kRowsTS * 4;
   const uint8_t* xa = smem + (b & 1) * L.xbuf + n * L.xrow;          // A row n (zero rows for m >= M)
   const float* xs = reinterpret_cast<const float*>(smem + L.xs_off + (b & 1) * L.xsbuf);
   const int kbf = b * kRowsKB;
@@ -957,14 +958,7 @@ __device__ __forceinline__ void rows_compute(const LinearArgs& a, int b, int nkb
 #pragma unroll
   for (int j = 0; j < kRowsKB; ++j) {
     if (kbf + j < nkb) {
-      // the transposed read needs other lanes' writes: wait for the wave's
-      // own LDS writes in between (alternating halves let consecutive blocks
-      // overlap; chunk c of row r sits at slot 4 r + (c ^ ((r >> 1) & 3)), so
-      // that both the write and the transposed read hit distinct banks)
-      u32x4* sc2 = scratch + 64 * (j & 1);
-      sc2[rq * 4 + (cq ^ ((rq >> 1) & 3))] = R.cw[j];
-      __builtin_amdgcn_s_waitcnt(0xc07f);          // lgkmcnt(0)
-      const u32x4 v = sc2[n * 4 + (q ^ ((n >> 1) & 3))];
+      const u32x4 v = R.cw[j];   // row n, columns 32 q .. 32 q + 31 of the block
       uint32_t d[4] = {v[0], v[1], v[2], v[3]};
       if constexpr (!ASYM) {
 #pragma unroll
