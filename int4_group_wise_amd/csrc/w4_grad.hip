@@ -299,7 +299,11 @@ constexpr int kTT = 64;
 // the 16 rows one wave reads at a time fall on distinct LDS banks
 __host__ __device__ inline int tstab_stride(int64_t NG) { return static_cast<int>(NG | 1); }                   // floats
 __host__ __device__ inline int tztab_stride(int64_t NG) { return 4 * static_cast<int>(((NG + 3) / 4) | 1); }  // bytes
-template <bool ASYM, bool GIDX, bool TAB>
+// TILED: wt is written in the fragment-tiled layout of the prefill GEMM
+// (tiled_unit in w4_internal.h) for the [K, N] matrix Wd^T (K % 128 == 0,
+// N % 64 == 0): unit (k, n .. n + 7); the 64 lanes of a wave write two runs
+// of 32 consecutive units.
+template <bool ASYM, bool GIDX, bool TAB, bool TILED = false>
 __global__ __launch_bounds__(kGThreads) void dequantize_t_kernel(DequantArgs a, uint16_t* __restrict__ wt) {
   extern __shared__ __attribute__((aligned(16))) uint8_t tsm[];
   uint16_t (*tile)[kTT + 2] = reinterpret_cast<uint16_t (*)[kTT + 2]>(tsm);     // [k][n]
@@ -367,7 +371,18 @@ __global__ __launch_bounds__(kGThreads) void dequantize_t_kernel(DequantArgs a, 
     }
   }
   __syncthreads();
-  {
+  if constexpr (TILED) {
+    const int kl = threadIdx.x % kTT, nq = (threadIdx.x / kTT) * 16;
+    const int64_t k = k0 + kl;
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2) {
+      u32x4 q;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) q[i] = *reinterpret_cast<const uint32_t*>(&tile[kl][nq + 8 * h2 + 2 * i]);
+      const int64_t unit = tiled_unit(k, n0 + nq + 8 * h2, a.N);
+      __builtin_nontemporal_store(q, reinterpret_cast<u32x4*>(wt + 8 * unit));
+    }
+  } else {
     const int kl = threadIdx.x >> 2, nq = (threadIdx.x & 3) * 16;
     const int k = k0 + kl;
     if (k < K) {
@@ -456,6 +471,19 @@ hipError_t launch_grad_input(const GradArgs& a, hipStream_t s) {
   const dim3 grid(static_cast<uint32_t>((a.K + kTT - 1) / kTT), static_cast<uint32_t>((a.N + kTT - 1) / kTT));
   const size_t lds0 = kTT * (kTT + 2) * 2 + kTT * 4;
   const size_t lds = lds0 + static_cast<size_t>(kTT) * (4 * tstab_stride(a.NG) + tztab_stride(a.NG));
+  if (lds <= 65536 && gemm_tiled_ok(a.M, a.K, a.N) && a.K % 128 == 0 && a.N % 64 == 0) {
+    // Wd^T in the tiled layout, then the GEMM that reads it straight into registers
+    if (a.asym) {
+      if (a.g_idx) dequantize_t_kernel<true, true, true, true><<<grid, dim3(kGThreads), lds, s>>>(d, wt);
+      else dequantize_t_kernel<true, false, true, true><<<grid, dim3(kGThreads), lds, s>>>(d, wt);
+    } else {
+      if (a.g_idx) dequantize_t_kernel<false, true, true, true><<<grid, dim3(kGThreads), lds, s>>>(d, wt);
+      else dequantize_t_kernel<false, false, true, true><<<grid, dim3(kGThreads), lds, s>>>(d, wt);
+    }
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    return launch_gemm_tiled(a.dy, wt, nullptr, a.dx, a.M, a.K, a.N, s);
+  }
   if (lds <= 65536) {
     if (a.asym) {
       if (a.g_idx) dequantize_t_kernel<true, true, true><<<grid, dim3(kGThreads), lds, s>>>(d, wt);

@@ -507,6 +507,8 @@ GRAD_CASES = [
     (48, 64, 256, 64, "asym", False), (300, 130, 200, 8, "sym", True), (40, 96, 512, 128, "asym", False),
     (17, 1, 64, 16, "sym", False), (20, 24, 2048, 8, "asym", True),   # 256 groups: tables read from memory
     (1, 64, 4100, -1, "asym", False), (2, 50, 4096, -1, "sym", False), (20, 40, 300, -1, "sym", False),
+    # transposed weight in the GEMM's tiled layout (N % 64 == 0, K % 128 == 0)
+    (33, 128, 384, 64, "sym", True), (130, 192, 1024, 128, "asym", False),
 ]
 
 
@@ -526,10 +528,12 @@ def test_grad_input_prefill_size():
     _check_grad(2048, 4096, 4096, 128, "asym", True, seed=31, cols=None, label="prefill-size")
 
 
-@pytest.mark.parametrize("M,K,mode", [(3, 520, "sym"), (24, 256, "asym")])
-def test_grad_input_unit_rows_are_exact(M, K, mode):
-    """dy row m = e_{n_m}: dx row m is the bf16 dequantized row n_m, bit for bit."""
-    N, G = 40, 8
+@pytest.mark.parametrize("M,K,mode,N", [(3, 520, "sym", 40), (24, 256, "asym", 40),
+                                        (40, 512, "asym", 128), (64, 256, "sym", 64)])
+def test_grad_input_unit_rows_are_exact(M, K, mode, N):
+    """dy row m = e_{n_m}: dx row m is the bf16 dequantized row n_m, bit for bit
+    (the last two shapes take the tiled transposed weight)."""
+    G = 8
     rng = np.random.default_rng(32)
     w = (rng.standard_normal((N, K)) * 0.02).astype(np.float32)
     oc, osc, oz = O.quantize_pack(w, G, _mode(mode))
