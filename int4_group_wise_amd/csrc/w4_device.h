@@ -42,16 +42,40 @@ __device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
 // Zero-points of one weight row: one per byte ([N, NG]), or packed two per
 // byte ([N, ceil(NG/2)], group 2j in the low nibble of byte j, group 2j + 1 in
 // the high nibble).
+// Branch-free (pk is 0 or 1), so that a zero-point load does not end the
+// basic block it sits in and force a wait for the loads issued before it.
+// byte(g) and of(byte, g) split the read into the load and the extraction,
+// for kernels that issue many loads before using any (as zero_byte/zero_of
+// below).
 struct ZeroRow {
   const uint8_t* p;
-  bool packed;
-  __device__ __forceinline__ uint32_t operator[](int64_t g) const {
-    return packed ? (static_cast<uint32_t>(p[g >> 1]) >> (4 * (g & 1))) & 15u : static_cast<uint32_t>(p[g]);
+  uint32_t pk;   // 1: packed two per byte
+  __device__ __forceinline__ uint32_t byte(int64_t g) const { return p[g >> pk]; }
+  __device__ __forceinline__ uint32_t of(uint32_t b, int64_t g) const {
+    return (b >> (4u * (static_cast<uint32_t>(g) & pk))) & (0xFFu >> (4u * pk));
   }
+  __device__ __forceinline__ uint32_t operator[](int64_t g) const { return of(byte(g), g); }
 };
 __device__ __forceinline__ ZeroRow zero_row(const uint8_t* z, int64_t n, int64_t NG, int packed) {
-  if (!z) return ZeroRow{nullptr, false};
-  return ZeroRow{z + n * (packed ? (NG + 1) / 2 : NG), packed != 0};
+  const uint32_t pk = packed ? 1u : 0u;
+  return ZeroRow{z ? z + n * ((NG + pk) >> pk) : z, pk};
+}
+
+// The same read with the layout fixed at compile time (PK 0: one per byte,
+// PK 1: packed two per byte), for kernels instantiated per layout, in two
+// steps: zero_byte loads the byte holding group g's zero-point, zero_of takes
+// the zero-point out of it.  A kernel that issues many loads before using any
+// calls zero_of at the use, so that no arithmetic on a loaded byte sits among
+// the loads (it would make the wave wait for every load issued before it).
+template <int PK>
+__device__ __forceinline__ uint32_t zero_byte(const uint8_t* z, int64_t n, int64_t NG, int64_t g) {
+  if constexpr (PK == 0) return z[n * NG + g];
+  else return z[n * ((NG + 1) >> 1) + (g >> 1)];
+}
+template <int PK>
+__device__ __forceinline__ uint32_t zero_of(uint32_t byte, uint32_t g) {
+  if constexpr (PK == 0) return byte;
+  else return (byte >> (4u * (g & 1u))) & 0xFu;
 }
 
 // 0x0F0F0F0F in a VGPR, hidden from the compiler.  After `d & 0x0F0F0F0F`

@@ -99,7 +99,7 @@ __global__ __launch_bounds__(kGThreads) void grad_split_kernel(GradArgs a, int r
   for (int64_t n0 = nb + w; n0 < ne; n0 += kGUnroll * kGWaves) {
     uint32_t d[kGUnroll][kW];
     float s[kGUnroll][kNGrp];
-    float z[kGUnroll][kNGrp];
+    uint32_t zb[kGUnroll][kNGrp];   // raw zero-point bytes; the zero-points are taken out at their use
     uint32_t dyr[kGUnroll][MT];   // raw bf16 dy of the block's rows
     // loads of this wave's next kGUnroll rows first (past the slice: reload the last)
 #pragma unroll
@@ -125,7 +125,7 @@ __global__ __launch_bounds__(kGThreads) void grad_split_kernel(GradArgs a, int r
 #pragma unroll
       for (int e = 0; e < kNGrp; ++e) {
         s[u][e] = a.scales[n * NG + g[e]];
-        z[u][e] = ASYM ? static_cast<float>(zero_row(a.zeros, n, NG, a.zpk)[g[e]]) : 8.0f;
+        zb[u][e] = ASYM ? zero_row(a.zeros, n, NG, a.zpk).byte(g[e]) : 8u;
       }
 #pragma unroll
       for (int m = 0; m < MT; ++m) dyr[u][m] = load_bf16_uniform(a.dy, static_cast<int64_t>(min(m, M - 1)) * a.N + n);
@@ -136,6 +136,10 @@ __global__ __launch_bounds__(kGThreads) void grad_split_kernel(GradArgs a, int r
       // m >= M (reading row M - 1) add nothing: their dy factor is 0
       const int64_t n = n0 + u * kGWaves;
       const bool valid = n < ne;
+      float z[kNGrp];
+#pragma unroll
+      for (int e = 0; e < kNGrp; ++e)
+        z[e] = ASYM ? static_cast<float>(zero_row(a.zeros, 0, NG, a.zpk).of(zb[u][e], g[e])) : 8.0f;
       float dm[MT];
 #pragma unroll
       for (int m = 0; m < MT; ++m) {
@@ -148,7 +152,7 @@ __global__ __launch_bounds__(kGThreads) void grad_split_kernel(GradArgs a, int r
           const uint32_t dd = ASYM ? d[u][i] : (d[u][i] ^ 0x88888888u);   // signed q -> q + 8
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
-            const float wv = (static_cast<float>((dd >> (4 * e)) & 15u) - z[u][e]) * s[u][e];
+            const float wv = (static_cast<float>((dd >> (4 * e)) & 15u) - z[e]) * s[u][e];
 #pragma unroll
             for (int m = 0; m < MT; ++m) acc[m][8 * i + e] = __builtin_fmaf(dm[m], wv, acc[m][8 * i + e]);
           }
@@ -160,7 +164,7 @@ __global__ __launch_bounds__(kGThreads) void grad_split_kernel(GradArgs a, int r
 #pragma unroll
         for (int m = 0; m < MT; ++m) {
           cm[m] = dm[m] * s[u][0];
-          corr[m] = __builtin_fmaf(cm[m], z[u][0], corr[m]);
+          corr[m] = __builtin_fmaf(cm[m], z[0], corr[m]);
         }
 #pragma unroll
         for (int i = 0; i < kW; ++i) {

@@ -268,8 +268,9 @@ __global__ __launch_bounds__(kGemvWaves * kWave) void gemv_dot2_kernel(LinearArg
 // waves' row sums meet in LDS and the first wave stores them.
 // ---------------------------------------------------------------------------
 constexpr int kStreamWG = 4;   // waves per workgroup
-template <int R, int S, int P, bool ASYM>
+template <int R, int S, int P, int ZP>   // ZP: 0 no zero-points, 1 one per byte, 2 two per byte
 __global__ __launch_bounds__(kStreamWG * kWave) void gemv_stream_kernel(LinearArgs a) {
+  constexpr bool ASYM = ZP != 0;
   static_assert(R >= 1 && R <= 16, "at most four four-row reductions");
   static_assert(P == 1 || P == 2, "one or two waves per row set");
   constexpr int H = (R + 3) / 4;   // four-row reductions
@@ -315,7 +316,7 @@ __global__ __launch_bounds__(kStreamWG * kWave) void gemv_stream_kernel(LinearAr
 #pragma unroll
     for (int j = 0; j < S; ++j) {
       sc[r][j] = a.scales[n * a.NG + g[j]];
-      zb[r][j] = ASYM ? zero_row(a.zeros, n, a.NG, a.zpk)[g[j]] : 8u;
+      zb[r][j] = ASYM ? zero_byte<ZP == 2>(a.zeros, n, a.NG, g[j]) : 8u;
     }
     __builtin_amdgcn_sched_barrier(0);   // issue order = use order, row by row
   }
@@ -347,7 +348,7 @@ __global__ __launch_bounds__(kStreamWG * kWave) void gemv_stream_kernel(LinearAr
       float acc = 0.0f;
 #pragma unroll
       for (int i = 0; i < 4; ++i) acc = dot8(cw[r][j][i] ^ flip, mask, xp[j][i], acc);
-      tot[r] += sc[r][j] * (acc - (128.0f + static_cast<float>(zb[r][j])) * xsum[j]);
+      tot[r] += sc[r][j] * (acc - (128.0f + static_cast<float>(zero_of<ZP == 2>(zb[r][j], g[j]))) * xsum[j]);
     }
   }
 
@@ -1138,30 +1139,31 @@ int stream_rows(int64_t N) {
   return r <= 2 ? 2 : r <= 4 ? 4 : r <= 7 ? 7 : r <= 8 ? 8 : r <= 14 ? 14 : 16;
 }
 
-template <int R, int S, bool ASYM>
+template <int R, int S, int ZP>
 hipError_t launch_stream3(const LinearArgs& a, hipStream_t s) {
   constexpr int sets_per_wg = kStreamWG / kStreamP;
   const int64_t sets = (a.N + R - 1) / R;
-  gemv_stream_kernel<R, S, kStreamP, ASYM><<<dim3(static_cast<uint32_t>((sets + sets_per_wg - 1) / sets_per_wg)),
+  gemv_stream_kernel<R, S, kStreamP, ZP><<<dim3(static_cast<uint32_t>((sets + sets_per_wg - 1) / sets_per_wg)),
                                              dim3(kStreamWG * kWave), 0, s>>>(a);
   return hipGetLastError();
 }
 
-template <bool ASYM>
+template <int ZP>
 hipError_t launch_stream2(const LinearArgs& a, hipStream_t s) {
   constexpr int S = 2 / kStreamP;   // K = 4096: 128 slices per row
   switch (stream_rows(a.N)) {
-    case 2: return launch_stream3<2, S, ASYM>(a, s);
-    case 4: return launch_stream3<4, S, ASYM>(a, s);
-    case 7: return launch_stream3<7, S, ASYM>(a, s);
-    case 8: return launch_stream3<8, S, ASYM>(a, s);
-    case 14: return launch_stream3<14, S, ASYM>(a, s);
-    default: return launch_stream3<16, S, ASYM>(a, s);
+    case 2: return launch_stream3<2, S, ZP>(a, s);
+    case 4: return launch_stream3<4, S, ZP>(a, s);
+    case 7: return launch_stream3<7, S, ZP>(a, s);
+    case 8: return launch_stream3<8, S, ZP>(a, s);
+    case 14: return launch_stream3<14, S, ZP>(a, s);
+    default: return launch_stream3<16, S, ZP>(a, s);
   }
 }
 
 hipError_t launch_stream(const LinearArgs& a, hipStream_t s) {
-  return a.asym ? launch_stream2<true>(a, s) : launch_stream2<false>(a, s);
+  if (!a.asym) return launch_stream2<0>(a, s);
+  return a.zpk ? launch_stream2<2>(a, s) : launch_stream2<1>(a, s);
 }
 
 // Act-order decode: rows per set as the streaming GEMV; P = 2 waves per set
