@@ -173,8 +173,8 @@ def bench_streaming_floor(nbytes, steps=4000):
 
 
 PROFILES = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles")
-TRAFFIC_FILE = os.path.join(PROFILES, "gemv_dot2_decode_traffic.txt")
-DECODE_SOURCES = ("w4_linear.hip", "w4_device.h", "w4_internal.h")
+TRAFFIC_FILE = os.path.join(PROFILES, "gemv_stream_decode_traffic.txt")
+DECODE_SOURCES = ("w4_stream.hip", "w4_dot.h", "w4_device.h", "w4_internal.h")
 
 
 def decode_source_hash():

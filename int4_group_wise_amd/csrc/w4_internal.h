@@ -114,6 +114,11 @@ hipError_t launch_dequantize(const DequantArgs& a, hipStream_t s);
 // covers the request (the caller then takes the prefill path).
 bool skinny_supported(const LinearArgs& a);
 hipError_t launch_linear_skinny(const LinearArgs& a, hipStream_t s);
+// The streaming decode GEMV (M = 1, K = 4096, contiguous groups, G % 32 == 0)
+// and its rows per row set for N rows (also used by the act-order decode).
+bool stream_ok(const LinearArgs& a);
+hipError_t launch_stream(const LinearArgs& a, hipStream_t s);
+int stream_rows(int64_t N);
 // Workspace the skinny path needs (fp32 split-K partials of the batched
 // decode kernel; 0 when it runs in one pass).
 size_t skinny_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t G, bool has_g_idx);

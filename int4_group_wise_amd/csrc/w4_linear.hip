@@ -15,66 +15,17 @@
 //               c - 16 [c >= 8] == (c ^ 8) - 8).
 //   gemv_generic  any G, K, g_idx: one wave per row, per-element dequantize
 //               to the bf16 weight (as the dense path computes it).
-// Prefill path (M > 16) lives in w4_gemm.hip.
+// The streaming decode GEMV (M = 1, K = 4096) lives in w4_stream.hip, the
+// prefill path (M > 16) in w4_gemm.hip.
 #include "w4_device.h"
+#include "w4_dot.h"
 #include "w4_internal.h"
 
 namespace w4 {
 namespace {
 
-__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
-  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
-                                         __builtin_bit_cast(bf16x2_t, b), c, false);
-}
-
-// Byte selector for v_perm_b32(hi, lo, sel): result byte i = byte sel_i of the
-// 8-byte value {hi:lo} (lo = bytes 0..3).
-__device__ __forceinline__ uint32_t perm(uint32_t hi, uint32_t lo, uint32_t sel) {
-  return __builtin_amdgcn_perm(hi, lo, sel);
-}
-
 constexpr int kGemvWaves = 2;   // waves per workgroup (2, 4, 8, 16 measured: 2 best by ~1.5%)
 constexpr int kGemvRows = 4;    // weight rows per wave
-
-// x values of 8 consecutive columns c0..c0+7 (4 dwords of bf16 pairs) are
-// re-paired to match the nibble pairs (c0, c0+4), (c0+1, c0+5), (c0+2, c0+6),
-// (c0+3, c0+7) produced from one code word.
-__device__ __forceinline__ void pair_x(const uint32_t a[4], uint32_t xp[4]) {
-  xp[0] = perm(a[2], a[0], 0x05040100u);   // (x0, x4)
-  xp[1] = perm(a[2], a[0], 0x07060302u);   // (x1, x5)
-  xp[2] = perm(a[3], a[1], 0x05040100u);   // (x2, x6)
-  xp[3] = perm(a[3], a[1], 0x07060302u);   // (x3, x7)
-}
-
-// (a & m) | e.  Written in C so that the compiler sees the definition: its
-// result often feeds a matrix-core operand, and only instructions the
-// compiler can see get the wait states a VALU write needs before an MFMA
-// reads the same register.
-__device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t m, uint32_t e) {
-  return (a & m) | e;
-}
-
-// The nibble-pair mask 0x000F000F in a VGPR.  Loaded in asm so that the
-// compiler cannot fold it into a constant: with the mask in a register and the
-// exponent pattern in an SGPR, (a & m) | e selects one v_and_or_b32 (a VOP3
-// op here may read one scalar and no literal).  Its only readers are VALU
-// ops, so no matrix-core hazard hides behind the asm.
-__device__ __forceinline__ uint32_t nibble_mask() {
-  uint32_t r;
-  asm volatile("v_mov_b32 %0, 0x000F000F" : "=v"(r));
-  return r;
-}
-
-constexpr uint32_t kMagic = 0x43004300u;   // bf16 pair (128, 128): 0x4300 | u == 128 + u
-
-// sum over 8 columns of x * (128 + u); d holds the 8 nibbles (column j at bits 4j).
-__device__ __forceinline__ float dot8(uint32_t d, uint32_t m, const uint32_t xp[4], float acc) {
-  acc = dot2_bf16(and_or(d, m, kMagic), xp[0], acc);
-  acc = dot2_bf16(and_or(d >> 4, m, kMagic), xp[1], acc);
-  acc = dot2_bf16(and_or(d >> 8, m, kMagic), xp[2], acc);
-  acc = dot2_bf16(and_or(d >> 12, m, kMagic), xp[3], acc);
-  return acc;
-}
 
 // One lane's share of one 2048-column chunk of its wave's rows: the 16 code
 // bytes (32 columns) of each row plus that slice's scale and offset
@@ -165,30 +116,6 @@ __device__ __forceinline__ void use_slice(const Slice& s, const XSlice<MT>& x, b
   }
 }
 
-// Wave sums of four values per lane (one per weight row of the wave), all in
-// VALU cross-lane operations: a 32-lane swap pairs rows 0/2 and 1/3 across the
-// wave halves, a 16-lane swap leaves the partial sums of row r in lanes
-// 16r .. 16r + 15, and four DPP steps (rotate by 8 and 4 within the 16-lane
-// row, then the two quad swaps) finish every row.  Lane l returns the total of
-// row l / 16.  The order of the additions is fixed.
-template <int CTRL>
-__device__ __forceinline__ float dpp_add(float v) {
-  return v + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
-}
-
-__device__ __forceinline__ float wave_sum4(float t0, float t1, float t2, float t3) {
-  const auto a02 = __builtin_amdgcn_permlane32_swap(__float_as_uint(t0), __float_as_uint(t2), false, false);
-  const auto a13 = __builtin_amdgcn_permlane32_swap(__float_as_uint(t1), __float_as_uint(t3), false, false);
-  const float s02 = __uint_as_float(a02[0]) + __uint_as_float(a02[1]);   // lanes 0-31: row 0, 32-63: row 2
-  const float s13 = __uint_as_float(a13[0]) + __uint_as_float(a13[1]);   // lanes 0-31: row 1, 32-63: row 3
-  const auto q = __builtin_amdgcn_permlane16_swap(__float_as_uint(s02), __float_as_uint(s13), false, false);
-  float v = __uint_as_float(q[0]) + __uint_as_float(q[1]);               // lanes 16r..16r+15: row r
-  v = dpp_add<0x128>(v);   // row_ror:8
-  v = dpp_add<0x124>(v);   // row_ror:4
-  v = dpp_add<0x4E>(v);    // quad_perm [2, 3, 0, 1]
-  v = dpp_add<0xB1>(v);    // quad_perm [1, 0, 3, 2]
-  return v;
-}
 
 // Each round covers two 2048-column chunks.  A lane first issues the loads of
 // its activations (L2-resident), then the code words, scales and zero-points
@@ -251,128 +178,6 @@ __global__ __launch_bounds__(kGemvWaves * kWave) void gemv_dot2_kernel(LinearArg
     const float bias = a.bias ? bf16_to_f32(braw) : 0.0f;
     if ((lane & 15) == 0 && n_out < a.N && m < M)
       a.y[static_cast<int64_t>(m) * a.N + n_out] = static_cast<uint16_t>(f32_to_bf16(v + bias));
-  }
-}
-
-// ---------------------------------------------------------------------------
-// Decode GEMV, M = 1, streaming form (K a multiple of 2048, contiguous groups
-// with G % 32 == 0).  A set of P waves owns R consecutive weight rows; in each
-// row the 32-column slices are dealt round-robin: lane l of wave h takes
-// slices l + 64 (P j + h), j < S, so that a load instruction reads 1 KB of a
-// row contiguously.  Every load of the wave is issued before any arithmetic:
-// the activations and the bias first, then row by row the code words, scales
-// and zero-points.  Loads retire in order, so the arithmetic of row r waits
-// only for row r's data and runs while the later rows are still streaming in;
-// only the last row's arithmetic is exposed at the end.  The activations are
-// loaded and re-paired once per wave for all R rows.  With P = 2 the two
-// waves' row sums meet in LDS and the first wave stores them.
-// ---------------------------------------------------------------------------
-constexpr int kStreamWG = 4;   // waves per workgroup
-template <int R, int S, int P, int ZP>   // ZP: 0 no zero-points, 1 one per byte, 2 two per byte
-__global__ __launch_bounds__(kStreamWG * kWave) void gemv_stream_kernel(LinearArgs a) {
-  constexpr bool ASYM = ZP != 0;
-  static_assert(R >= 1 && R <= 16, "at most four four-row reductions");
-  static_assert(P == 1 || P == 2, "one or two waves per row set");
-  constexpr int H = (R + 3) / 4;   // four-row reductions
-  __shared__ float red[kStreamWG][4 * H];
-  const int lane = lane_id();
-  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int h = w % P;
-  const int64_t set = static_cast<int64_t>(blockIdx.x) * (kStreamWG / P) + w / P;
-  const int64_t row0 = set * R;   // rows past N are clamped: computed, not stored
-  const int64_t rowc = min(row0, a.N - 1);
-  const uint32_t mask = nibble_mask();
-  const int64_t KB = a.K / 2;
-  auto slice = [&](int j) -> uint32_t { return static_cast<uint32_t>(lane) + 64u * (P * j + h); };
-
-  // activations of the lane's slices, 64 bytes each
-  u32x4 xr[S][4];
-#pragma unroll
-  for (int j = 0; j < S; ++j)
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      xr[j][i] = *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint8_t*>(a.x) + 64u * slice(j) + 16 * i);
-  // after the reduction lane l holds the sum of row row0 + 4 hh + l / 16
-  uint32_t braw[H];
-#pragma unroll
-  for (int hh = 0; hh < H; ++hh) {
-    const int64_t n = min(row0 + 4 * hh + (lane >> 4), a.N - 1);
-    braw[hh] = a.bias ? a.bias[n] : a.x[0];
-  }
-  __builtin_amdgcn_sched_barrier(0);
-
-  uint32_t g[S];
-#pragma unroll
-  for (int j = 0; j < S; ++j) g[j] = (32u * slice(j)) / static_cast<uint32_t>(a.G);
-  u32x4 cw[R][S];
-  float sc[R][S];
-  uint32_t zb[R][S];
-#pragma unroll
-  for (int r = 0; r < R; ++r) {
-    const int64_t n = min(rowc + r, a.N - 1);
-    const uint8_t* crow = a.codes + n * KB;
-#pragma unroll
-    for (int j = 0; j < S; ++j) cw[r][j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(crow + 16u * slice(j)));
-#pragma unroll
-    for (int j = 0; j < S; ++j) {
-      sc[r][j] = a.scales[n * a.NG + g[j]];
-      zb[r][j] = ASYM ? zero_byte<ZP == 2>(a.zeros, n, a.NG, g[j]) : 8u;
-    }
-    __builtin_amdgcn_sched_barrier(0);   // issue order = use order, row by row
-  }
-
-  // re-pair the activations to the decode's slot order; their sums per slice
-  const uint32_t ones = 0x3F803F80u;   // bf16 pair (1.0, 1.0)
-  uint32_t xp[S][4][4];
-  float xsum[S];
-#pragma unroll
-  for (int j = 0; j < S; ++j) {
-    xsum[j] = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const uint32_t in[4] = {xr[j][i][0], xr[j][i][1], xr[j][i][2], xr[j][i][3]};
-      pair_x(in, xp[j][i]);
-#pragma unroll
-      for (int p = 0; p < 4; ++p) xsum[j] = dot2_bf16(xp[j][i][p], ones, xsum[j]);
-    }
-  }
-
-  float tot[4 * H];
-#pragma unroll
-  for (int r = 0; r < 4 * H; ++r) tot[r] = 0.0f;
-  const uint32_t flip = ASYM ? 0u : 0x88888888u;
-#pragma unroll
-  for (int r = 0; r < R; ++r) {
-#pragma unroll
-    for (int j = 0; j < S; ++j) {
-      float acc = 0.0f;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) acc = dot8(cw[r][j][i] ^ flip, mask, xp[j][i], acc);
-      tot[r] += sc[r][j] * (acc - (128.0f + static_cast<float>(zero_of<ZP == 2>(zb[r][j], g[j]))) * xsum[j]);
-    }
-  }
-
-  float v[H];
-#pragma unroll
-  for (int hh = 0; hh < H; ++hh) v[hh] = wave_sum4(tot[4 * hh], tot[4 * hh + 1], tot[4 * hh + 2], tot[4 * hh + 3]);
-  if constexpr (P == 2) {
-    // the second wave of the set hands its sums to the first, which adds them
-    // (fixed order: first wave + second wave)
-    if (h == 1 && (lane & 15) == 0) {
-#pragma unroll
-      for (int hh = 0; hh < H; ++hh) red[w][4 * hh + (lane >> 4)] = v[hh];
-    }
-    __syncthreads();
-    if (h == 1) return;
-#pragma unroll
-    for (int hh = 0; hh < H; ++hh) v[hh] += red[w + 1][4 * hh + (lane >> 4)];
-  }
-#pragma unroll
-  for (int hh = 0; hh < H; ++hh) {
-    const int64_t n = row0 + 4 * hh + (lane >> 4);
-    const float bias = a.bias ? bf16_to_f32(braw[hh]) : 0.0f;
-    if ((lane & 15) == 0 && 4 * hh + (lane >> 4) < R && n < a.N)
-      a.y[n] = static_cast<uint16_t>(f32_to_bf16(v[hh] + bias));
   }
 }
 
@@ -1130,42 +935,6 @@ hipError_t launch_dot2(const LinearArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-// Rows per wave of the streaming decode GEMV: about two waves per SIMD
-// (2048 waves on 256 CUs) when N allows it.
-constexpr int kStreamP = 2;              // waves per row set
-constexpr int64_t kStreamSets = 2048;    // row sets per launch, about
-int stream_rows(int64_t N) {
-  const int64_t r = (N + kStreamSets - 1) / kStreamSets;
-  return r <= 2 ? 2 : r <= 4 ? 4 : r <= 7 ? 7 : r <= 8 ? 8 : r <= 14 ? 14 : 16;
-}
-
-template <int R, int S, int ZP>
-hipError_t launch_stream3(const LinearArgs& a, hipStream_t s) {
-  constexpr int sets_per_wg = kStreamWG / kStreamP;
-  const int64_t sets = (a.N + R - 1) / R;
-  gemv_stream_kernel<R, S, kStreamP, ZP><<<dim3(static_cast<uint32_t>((sets + sets_per_wg - 1) / sets_per_wg)),
-                                             dim3(kStreamWG * kWave), 0, s>>>(a);
-  return hipGetLastError();
-}
-
-template <int ZP>
-hipError_t launch_stream2(const LinearArgs& a, hipStream_t s) {
-  constexpr int S = 2 / kStreamP;   // K = 4096: 128 slices per row
-  switch (stream_rows(a.N)) {
-    case 2: return launch_stream3<2, S, ZP>(a, s);
-    case 4: return launch_stream3<4, S, ZP>(a, s);
-    case 7: return launch_stream3<7, S, ZP>(a, s);
-    case 8: return launch_stream3<8, S, ZP>(a, s);
-    case 14: return launch_stream3<14, S, ZP>(a, s);
-    default: return launch_stream3<16, S, ZP>(a, s);
-  }
-}
-
-hipError_t launch_stream(const LinearArgs& a, hipStream_t s) {
-  if (!a.asym) return launch_stream2<0>(a, s);
-  return a.zpk ? launch_stream2<2>(a, s) : launch_stream2<1>(a, s);
-}
-
 // Act-order decode: rows per set as the streaming GEMV; P = 2 waves per set
 // when K is a multiple of 4096 (S = K / 4096 slices per wave), else P = 1
 // with K = 2048 (one slice).
@@ -1207,12 +976,6 @@ hipError_t launch_act(const LinearArgs& a, hipStream_t s) {
   if (a.M == 1) return launch_act2<1>(a, s);
   if (a.M == 2) return launch_act2<2>(a, s);
   return launch_act2<4>(a, s);
-}
-
-// The streaming decode GEMV: M = 1, K = 4096, contiguous groups with G a
-// multiple of 32.
-bool stream_ok(const LinearArgs& a) {
-  return a.M == 1 && a.g_idx == nullptr && a.K == 4096 && a.G % 32 == 0;
 }
 
 template <int MT, bool ASYM, bool TR, int GU>
