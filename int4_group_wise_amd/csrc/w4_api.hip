@@ -116,10 +116,9 @@ w4_status w4_dequantize(const uint8_t* codes, const float* scales, const uint8_t
 }
 
 size_t w4_linear_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t G, int mode, int has_g_idx) {
-  (void)mode;
   if (M < 1 || N < 1 || K < 1 || (G < 1 && G != W4_PER_CHANNEL)) return 0;
-  if (M <= 16)   // fp32 split-K partials of the batched decode kernel, if it splits
-    return w4::skinny_workspace_bytes(M, N, K, kernel_group(K, G), has_g_idx != 0);
+  if (M <= 16)   // fp32 split-K partials of the K-split batched decode kernel, if it is the one that runs
+    return w4::skinny_workspace_bytes(M, N, K, kernel_group(K, G), has_g_idx != 0, mode != W4_SYM);
   return static_cast<size_t>(N) * static_cast<size_t>(K) * 2u;   // bf16 dequantized weight
 }
 

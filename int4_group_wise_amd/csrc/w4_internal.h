@@ -119,9 +119,14 @@ hipError_t launch_linear_skinny(const LinearArgs& a, hipStream_t s);
 bool stream_ok(const LinearArgs& a);
 hipError_t launch_stream(const LinearArgs& a, hipStream_t s);
 int stream_rows(int64_t N);
+// The one-launch batched decode (4 < M <= 16, contiguous groups of 32, 64 or a
+// multiple of 128, K % 128 == 0).
+bool batched_shape_ok(int64_t M, int64_t K, int64_t G, bool has_g_idx, bool asym);
+bool batched_ok(const LinearArgs& a);
+hipError_t launch_batched(const LinearArgs& a, hipStream_t s);
 // Workspace the skinny path needs (fp32 split-K partials of the batched
 // decode kernel; 0 when it runs in one pass).
-size_t skinny_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t G, bool has_g_idx);
+size_t skinny_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t G, bool has_g_idx, bool asym);
 
 // Allow `bytes` of dynamic LDS for `kernel` on device `dev` (once per pair,
 // thread-safe).

@@ -20,6 +20,7 @@
 #include "w4_device.h"
 #include "w4_dot.h"
 #include "w4_internal.h"
+#include "w4_mfma.h"
 
 namespace w4 {
 namespace {
@@ -373,24 +374,6 @@ __global__ __launch_bounds__(kActWG * kWave) void gemv_act_kernel(LinearArgs a) 
 
 constexpr int kTileWaves = 4;
 constexpr int kMfmaKR = 8;           // k-blocks (128 columns) per round
-
-// 8 nibbles (column j at bits 4j) -> 8 bf16 values 128 + u in slot order
-// (c0, c4, c1, c5, c2, c6, c3, c7), matching pair_x on the activation side.
-__device__ __forceinline__ bf16x8_t decode_word(uint32_t d, uint32_t m) {
-  const u32x4 v = {and_or(d, m, kMagic), and_or(d >> 4, m, kMagic), and_or(d >> 8, m, kMagic),
-                   and_or(d >> 12, m, kMagic)};
-  return __builtin_bit_cast(bf16x8_t, v);
-}
-
-// Register i of lane quarter q <- register q of lane quarter i (4 x 4
-// transpose across the quarters of the wave).
-__device__ __forceinline__ void transpose_quarters(uint32_t (&d)[4]) {
-  auto r02 = __builtin_amdgcn_permlane32_swap(d[0], d[2], false, false);
-  auto r13 = __builtin_amdgcn_permlane32_swap(d[1], d[3], false, false);
-  auto r01 = __builtin_amdgcn_permlane16_swap(r02[0], r13[0], false, false);
-  auto r23 = __builtin_amdgcn_permlane16_swap(r02[1], r13[1], false, false);
-  d[0] = r01[0]; d[1] = r01[1]; d[2] = r23[0]; d[3] = r23[1];
-}
 
 // Groups one wave's round can touch in a row: KR blocks of 128 columns hold
 // KR * 128 / G groups for G <= 128, at most KR + 1 for G > 128.
@@ -1058,14 +1041,15 @@ bool dot2_ok(const LinearArgs& a) {
 
 bool skinny_supported(const LinearArgs& a) { return a.M >= 1 && a.M <= 16; }
 
-size_t skinny_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t G, bool has_g_idx) {
-  if (!rows_shape_ok(M, K, G, has_g_idx)) return 0;
+size_t skinny_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t G, bool has_g_idx, bool asym) {
+  if (batched_shape_ok(M, K, G, has_g_idx, asym) || !rows_shape_ok(M, K, G, has_g_idx)) return 0;
   const int sp = rows_splits(N, K);
   return sp > 1 ? static_cast<size_t>(sp) * static_cast<size_t>(M) * static_cast<size_t>(N) * sizeof(float) : 0;
 }
 
 hipError_t launch_linear_skinny(const LinearArgs& a, hipStream_t s) {
   if (!skinny_supported(a)) return hipErrorInvalidValue;
+  if (batched_ok(a)) return launch_batched(a, s);
   if (rows_ok(a)) return a.asym ? launch_rows2<true>(a, s) : launch_rows2<false>(a, s);
   // M = 1: the dot-product kernel streams rows fastest; M = 2..4: the
   // matrix-core kernel, whose cost does not grow with M.

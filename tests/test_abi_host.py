@@ -105,18 +105,23 @@ def test_linear_rejects_and_workspace(lib):
     assert lib.w4_linear(FAKE, 64, FAKE, FAKE, None, None, 32, 128, 32, 0, None, FAKE, None, 0, None) == 1
     assert "workspace" in lib.w4_last_error().decode()
     assert lib.w4_linear(FAKE, 64, FAKE, FAKE, None, None, 32, 128, 32, 0, None, FAKE, FAKE, need - 1, None) == 1
-    # batched decode (4 < M <= 16) splits K when the grid would hold fewer than
-    # 4096 waves (16 rows each), doubling within the 512-column batches: fp32
-    # partials [splits, M, N]
-    assert lib.w4_linear_workspace_bytes(16, 28672, 8192, 64, 0, 0) == 4 * 16 * 28672 * 4
-    assert lib.w4_linear_workspace_bytes(16, 64, 8192, 64, 0, 0) == 16 * 16 * 64 * 4
+    # batched decode (4 < M <= 16): the one-launch kernel (K % 1024 == 0, at
+    # most 32 groups, 16 with zero-points, in a quarter of K) needs nothing
+    assert lib.w4_linear_workspace_bytes(16, 28672, 8192, 64, 0, 0) == 0
+    assert lib.w4_linear_workspace_bytes(16, 64, 8192, 64, 0, 0) == 0
+    assert lib.w4_linear_workspace_bytes(8, 256, 4096, 128, 1, 0) == 0
+    # other batched shapes take the K-split kernel, which splits K when the
+    # grid would hold fewer than 4096 waves (16 rows each), doubling within
+    # the 512-column batches: fp32 partials [splits, M, N]
+    assert lib.w4_linear_workspace_bytes(16, 28672, 8192, 32, 0, 0) == 4 * 16 * 28672 * 4   # 64 groups a quarter
+    assert lib.w4_linear_workspace_bytes(16, 64, 8320, 64, 0, 0) == 16 * 16 * 64 * 4        # K % 1024 != 0
     assert lib.w4_linear_workspace_bytes(16, 100, 512, 64, 0, 0) == 0          # one batch: no split
     assert lib.w4_linear_workspace_bytes(4, 28672, 8192, 64, 0, 0) == 0        # M <= 4: other kernels
     assert lib.w4_linear_workspace_bytes(16, 28672, 8192, 64, 0, 1) == 0       # act-order: generic kernel
     assert lib.w4_linear_workspace_bytes(16, 28672, 8192, 48, 0, 0) == 0       # G not 32, 64 or k 128
-    split = lib.w4_linear_workspace_bytes(8, 256, 4096, 128, 1, 0)
+    split = lib.w4_linear_workspace_bytes(8, 256, 4224, 128, 1, 0)
     assert split > 0
-    assert lib.w4_linear(FAKE, 8, FAKE, FAKE, FAKE, None, 256, 4096, 128, 1, None, FAKE, FAKE, split - 1, None) == 1
+    assert lib.w4_linear(FAKE, 8, FAKE, FAKE, FAKE, None, 256, 4224, 128, 1, None, FAKE, FAKE, split - 1, None) == 1
     assert "workspace" in lib.w4_last_error().decode()
 
 

@@ -156,6 +156,16 @@ CASES = [
     (5, 70, 640, 32, "asym", False, "f32", "randn"),     # batch tail (5 blocks of 128 columns)
     (12, 200, 1024, 256, "sym", False, "bf16", "none"),
     (16, 64, 8192, 64, "sym", False, "f32", "none"),
+    # one-launch batched decode (K % 1024 == 0): 1, 3 and 5 batch pairs per
+    # wave (loop, tail, both), G from 32 to 512 (a group wider than a wave's
+    # quarter of K), row tails, zero-points
+    (5, 70, 1024, 32, "asym", False, "f32", "randn"),
+    (9, 64, 3072, 64, "asym", False, "f32", "none"),
+    (16, 1000, 5120, 128, "asym", False, "bf16", "randn"),
+    (6, 65, 2048, 128, "asym", False, "f32", "none"),
+    (7, 300, 1024, 512, "sym", False, "f32", "randn"),
+    (16, 257, 4096, 64, "sym", False, "bf16", "none"),
+    (11, 129, 2048, 32, "sym", False, "f32", "randn"),
     (1, 37, 2048, 64, "asym", False, "f32", "randn"),   # staged decode, row tail
     (1, 50, 4096, 256, "sym", False, "bf16", "none"),   # staged decode, signed
     (1, 24, 16384, 256, "asym", False, "f32", "randn"), # staged decode, longest row, 64 groups
