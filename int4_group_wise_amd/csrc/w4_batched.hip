@@ -195,7 +195,6 @@ __device__ __forceinline__ void b_batch(const BRows<U>& R, uint32_t b, int j, co
 #pragma unroll
       for (int i = 0; i < 4; ++i) d[i] ^= 0x88888888u;   // signed q -> q + 8
     }
-    if constexpr (TR) transpose_quarters(d);
     const int trow = (16 * rb + n) * S + c0;
 #pragma unroll
     for (int u = 0; u < U; ++u) {
@@ -222,8 +221,12 @@ __device__ __forceinline__ void b_batch(const BRows<U>& R, uint32_t b, int j, co
 }
 
 // Batch pair p: the code words of each row block pass through LDS (rows
-// 8 (i % 2) + l / 8, chunk l % 8) into the operand layout (lane (n, q) of
-// batch j: row n, chunk 4 j + q), then the two batches.
+// 8 (i % 2) + l / 8, chunk l % 8) into the operand layout, then the two
+// batches.  Lane (n, q) of batch j reads row n: for U = 1 the 16 bytes of
+// chunk 4 j + q (MFMA step s sums columns 32 q + 8 s .. of the batch); for
+// U > 1 the four dwords at columns 32 s + 8 q (step s sums one group's 32
+// columns), which the reads take straight from the rows, so no cross-lane
+// transpose is needed.
 template <int ZP, int U>
 __device__ __forceinline__ void b_compute(const BRows<U>& R, uint32_t p, const BStage& st, uint32_t mask,
                                           const float* stab, const uint32_t* ztab, int S, uint32_t g_lo, int lane,
@@ -237,9 +240,15 @@ __device__ __forceinline__ void b_compute(const BRows<U>& R, uint32_t p, const B
       *reinterpret_cast<u32x4*>(cl + (8 * h + (lane >> 3)) * kBCRow + 16 * (lane & 7)) = st.cw[2 * rb + h];
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
-      const u32x4 v = *reinterpret_cast<const u32x4*>(cl + n * kBCRow + 16 * (4 * j + q));
+      if constexpr (U > 1) {
+        const uint32_t* crow = reinterpret_cast<const uint32_t*>(cl + n * kBCRow + 64 * j + 4 * q);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) dw[rb][j][i] = v[i];
+        for (int i = 0; i < 4; ++i) dw[rb][j][i] = crow[4 * i];
+      } else {
+        const u32x4 v = *reinterpret_cast<const u32x4*>(cl + n * kBCRow + 16 * (4 * j + q));
+#pragma unroll
+        for (int i = 0; i < 4; ++i) dw[rb][j][i] = v[i];
+      }
     }
   }
 #pragma unroll

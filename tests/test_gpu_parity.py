@@ -166,6 +166,12 @@ CASES = [
     (7, 300, 1024, 512, "sym", False, "f32", "randn"),
     (16, 257, 4096, 64, "sym", False, "bf16", "none"),
     (11, 129, 2048, 32, "sym", False, "f32", "randn"),
+    # 4, 6, 7 and 12 batch pairs per wave: the prefetch rings' rounds of six
+    # pairs and every tail length
+    (16, 130, 4096, 128, "asym", False, "f32", "randn"),
+    (8, 96, 6144, 64, "sym", False, "f32", "none"),
+    (13, 200, 7168, 128, "asym", False, "bf16", "randn"),
+    (16, 64, 12288, 128, "sym", False, "f32", "randn"),
     (1, 37, 2048, 64, "asym", False, "f32", "randn"),   # staged decode, row tail
     (1, 50, 4096, 256, "sym", False, "bf16", "none"),   # staged decode, signed
     (1, 24, 16384, 256, "asym", False, "f32", "randn"), # staged decode, longest row, 64 groups
