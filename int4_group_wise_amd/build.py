@@ -28,7 +28,7 @@ COMMON = ["--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC", "-Wall",
 # Codec units must reproduce the fp32 definition bit for bit: no fused
 # multiply-add contraction (divisions stay IEEE correctly rounded by default).
 EXTRA = {"w4_codec.hip": ["-ffp-contract=off"]}
-SOURCES = ["w4_api.hip", "w4_codec.hip", "w4_linear.hip", "w4_stream.hip", "w4_batched.hip", "w4_gemm.hip", "w4_grad.hip", "w4_lora.hip", "w4_formats.hip"]
+SOURCES = ["w4_api.hip", "w4_codec.hip", "w4_linear.hip", "w4_stream.hip", "w4_batched.hip", "w4_actmma.hip", "w4_gemm.hip", "w4_grad.hip", "w4_lora.hip", "w4_formats.hip"]
 
 
 def hipcc() -> str:

@@ -1058,6 +1058,7 @@ hipError_t launch_linear_skinny(const LinearArgs& a, hipStream_t s) {
     return launch_mfma2<4>(a, s);
   }
   if (stream_ok(a)) return launch_stream(a, s);
+  if (act_mma_ok(a)) return launch_act_mma(a, s);
   if (act_ok(a)) return launch_act(a, s);
   if (dot2_ok(a)) {
     if (a.M == 1) return launch_dot2<1>(a, s);

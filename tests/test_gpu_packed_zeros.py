@@ -46,6 +46,9 @@ LINEAR_CASES = [
     (16, 256, 8192, 64, False),     # batched decode, split K
     (12, 200, 1152, 128, False),    # batched decode, 9 groups
     (4, 64, 512, 128, True),        # act-order decode (generic)
+    (1, 300, 4096, 128, True),      # act-order decode on the matrix cores
+    (1, 70, 2048, 128, True),       # the same, 16 groups (one half)
+    (16, 256, 4096, 128, False),    # one-launch batched decode
     (64, 256, 1024, 128, True),     # prefill, tiled weight, act-order
     (48, 256, 2048, 128, False),    # prefill, tiled weight
     (40, 130, 640, 64, False),      # prefill, row-major weight (N % 128 != 0), 10 groups

@@ -190,6 +190,14 @@ CASES = [
     (3, 5000, 8192, 64, "sym", True, "f32", "none"),
     (1, 20000, 2048, 32, "asym", True, "bf16", "randn"),
     (16, 48, 1000, 40, "asym", True, "bf16", "none"),
+    # act-order decode on the matrix cores (M = 1, at most 32 groups, K % 1024
+    # == 0): one and two 16-group halves, 1, 4 and 8 batch pairs per wave,
+    # row tails, a group size that is not a power of two
+    (1, 4097, 4096, 256, "sym", True, "bf16", "none"),
+    (1, 130, 2048, 64, "asym", True, "f32", "randn"),
+    (1, 1000, 8192, 256, "asym", True, "f32", "none"),
+    (1, 33, 3072, 96, "sym", True, "f32", "randn"),
+    (1, 14336, 4096, 128, "asym", True, "bf16", "randn"),
     (17, 130, 200, 8, "asym", False, "f32", "randn"),   # prefill, K % 64 != 0, N tail
     (40, 70, 99, 16, "sym", False, "f32", "none"),      # prefill, K % 8 != 0
     (300, 260, 1024, 128, "asym", True, "f32", "randn"),
