@@ -35,11 +35,15 @@ __global__ __launch_bounds__(kStreamWG * kWave) void gemv_stream_kernel(LinearAr
   const int lane = lane_id();
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int h = w % P;
-  const int64_t set = static_cast<int64_t>(blockIdx.x) * (kStreamWG / P) + w / P;
-  const int64_t row0 = set * R;   // rows past N are clamped: computed, not stored
-  const int64_t rowc = min(row0, a.N - 1);
+  // 32-bit offsets from the arrays' bases (the launcher checks they fit), so
+  // that every load takes a uniform base and one 32-bit lane offset
+  const uint32_t N1 = static_cast<uint32_t>(a.N - 1);
+  const uint32_t set = blockIdx.x * (kStreamWG / P) + static_cast<uint32_t>(w / P);
+  const uint32_t row0 = set * R;   // rows past N are clamped: computed, not stored
+  const uint32_t rowc = min(row0, N1);
   const uint32_t mask = nibble_mask();
-  const int64_t KB = a.K / 2;
+  const uint32_t KB = static_cast<uint32_t>(a.K / 2);
+  const uint32_t NG = static_cast<uint32_t>(a.NG);
   auto slice = [&](int j) -> uint32_t { return static_cast<uint32_t>(lane) + 64u * (P * j + h); };
 
   // activations of the lane's slices, 64 bytes each
@@ -53,7 +57,7 @@ __global__ __launch_bounds__(kStreamWG * kWave) void gemv_stream_kernel(LinearAr
   uint32_t braw[H];
 #pragma unroll
   for (int hh = 0; hh < H; ++hh) {
-    const int64_t n = min(row0 + 4 * hh + (lane >> 4), a.N - 1);
+    const uint32_t n = min(row0 + 4u * hh + static_cast<uint32_t>(lane >> 4), N1);
     braw[hh] = a.bias ? a.bias[n] : a.x[0];
   }
   __builtin_amdgcn_sched_barrier(0);
@@ -66,14 +70,16 @@ __global__ __launch_bounds__(kStreamWG * kWave) void gemv_stream_kernel(LinearAr
   uint32_t zb[R][S];
 #pragma unroll
   for (int r = 0; r < R; ++r) {
-    const int64_t n = min(rowc + r, a.N - 1);
-    const uint8_t* crow = a.codes + n * KB;
+    const uint32_t n = min(rowc + r, N1);
 #pragma unroll
-    for (int j = 0; j < S; ++j) cw[r][j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(crow + 16u * slice(j)));
+    for (int j = 0; j < S; ++j)
+      cw[r][j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(a.codes + (n * KB + 16u * slice(j))));
 #pragma unroll
     for (int j = 0; j < S; ++j) {
-      sc[r][j] = a.scales[n * a.NG + g[j]];
-      zb[r][j] = ASYM ? zero_byte<ZP == 2>(a.zeros, n, a.NG, g[j]) : 8u;
+      sc[r][j] = *reinterpret_cast<const float*>(reinterpret_cast<const uint8_t*>(a.scales) + 4u * (n * NG + g[j]));
+      if constexpr (ZP == 1) zb[r][j] = a.zeros[n * NG + g[j]];
+      if constexpr (ZP == 2) zb[r][j] = a.zeros[n * ((NG + 1u) >> 1) + (g[j] >> 1)];
+      if constexpr (ZP == 0) zb[r][j] = 8u;
     }
     __builtin_amdgcn_sched_barrier(0);   // issue order = use order, row by row
   }
@@ -126,9 +132,9 @@ __global__ __launch_bounds__(kStreamWG * kWave) void gemv_stream_kernel(LinearAr
   }
 #pragma unroll
   for (int hh = 0; hh < H; ++hh) {
-    const int64_t n = row0 + 4 * hh + (lane >> 4);
+    const uint32_t n = row0 + 4u * hh + static_cast<uint32_t>(lane >> 4);
     const float bias = a.bias ? bf16_to_f32(braw[hh]) : 0.0f;
-    if ((lane & 15) == 0 && 4 * hh + (lane >> 4) < R && n < a.N)
+    if ((lane & 15) == 0 && 4 * hh + (lane >> 4) < R && n <= N1)
       a.y[n] = static_cast<uint16_t>(f32_to_bf16(v[hh] + bias));
   }
 }
@@ -177,9 +183,12 @@ hipError_t launch_stream(const LinearArgs& a, hipStream_t s) {
 }
 
 // The streaming decode GEMV: M = 1, K = 4096, contiguous groups with G a
-// multiple of 32.
+// multiple of 32, and code, scale and zero-point arrays whose byte offsets fit
+// in 31 bits.
 bool stream_ok(const LinearArgs& a) {
-  return a.M == 1 && a.g_idx == nullptr && a.K == 4096 && a.G % 32 == 0;
+  const int64_t lim = int64_t{1} << 31;
+  return a.M == 1 && a.g_idx == nullptr && a.K == 4096 && a.G % 32 == 0 && a.N * (a.K / 2) < lim &&
+         a.N * a.NG * 4 < lim;
 }
 
 }  // namespace w4
