@@ -83,20 +83,26 @@ struct BStage {
 // quarter q, columns
 //   k0 + 32 s + 8 q .. + 7   (U > 1: step s lies in one group), or
 //   k0 + 32 q + 8 s .. + 7   (U = 1: the code word's own order).
+// Offsets are 32-bit from the arrays' bases (the shape check keeps them
+// below 2^31), so that every load takes a uniform base and one lane offset.
 template <int U>
 struct BRows {
-  const uint8_t* x[4];           // activation row 4 s + l / 16 (at most M - 1) + 16 (l % 16)
-  const uint8_t* c[2 * kBRB];    // code row 8 i + l / 8 (at most N - 1) + 16 (l % 8)
+  const uint8_t* xb;             // activations
+  const uint8_t* cb;             // code words
+  uint32_t x[4];                 // byte offset of activation row 4 s + l / 16 (at most M - 1) + 16 (l % 16)
+  uint32_t c[2 * kBRB];          // byte offset of code row 8 i + l / 8 (at most N - 1) + 16 (l % 8)
   uint32_t gdiv;                 // G / 128 for U = 1
 
   __device__ __forceinline__ BRows(const LinearArgs& a, int64_t n0, int lane) {
     const int q = lane >> 4, r = lane & 15;
+    const uint32_t K = static_cast<uint32_t>(a.K), N1 = static_cast<uint32_t>(a.N - 1);
+    xb = reinterpret_cast<const uint8_t*>(a.x);
+    cb = a.codes;
 #pragma unroll
-    for (int s = 0; s < 4; ++s)
-      x[s] = reinterpret_cast<const uint8_t*>(a.x + static_cast<int64_t>(min(4 * s + q, static_cast<int>(a.M) - 1)) * a.K) +
-             16 * r;
+    for (int s = 0; s < 4; ++s) x[s] = static_cast<uint32_t>(min(4 * s + q, static_cast<int>(a.M) - 1)) * 2u * K + 16u * r;
 #pragma unroll
-    for (int i = 0; i < 2 * kBRB; ++i) c[i] = a.codes + min(n0 + 8 * i + (lane >> 3), a.N - 1) * (a.K / 2) + 16 * (lane & 7);
+    for (int i = 0; i < 2 * kBRB; ++i)
+      c[i] = min(static_cast<uint32_t>(n0) + 8u * i + static_cast<uint32_t>(lane >> 3), N1) * (K / 2u) + 16u * (lane & 7);
     gdiv = static_cast<uint32_t>(a.G / 128);
   }
   // first group of batch b
@@ -107,9 +113,9 @@ struct BRows {
 template <int U>
 __device__ __forceinline__ void b_issue(const BRows<U>& R, uint32_t p, BStage& st) {
 #pragma unroll
-  for (int j = 0; j < 8; ++j) st.x[j] = *reinterpret_cast<const u32x4*>(R.x[j & 3] + 512u * p + 256u * (j >> 2));
+  for (int j = 0; j < 8; ++j) st.x[j] = *reinterpret_cast<const u32x4*>(R.xb + (R.x[j & 3] + 512u * p + 256u * (j >> 2)));
 #pragma unroll
-  for (int i = 0; i < 2 * kBRB; ++i) st.cw[i] = *reinterpret_cast<const u32x4*>(R.c[i] + 128u * p);
+  for (int i = 0; i < 2 * kBRB; ++i) st.cw[i] = *reinterpret_cast<const u32x4*>(R.cb + (R.c[i] + 128u * p));
   __builtin_amdgcn_sched_barrier(0);
 }
 
@@ -124,13 +130,15 @@ __device__ __forceinline__ void b_table(const LinearArgs& a, int64_t n0, const B
   const int lr = lane / cnt, c = lane - lr * cnt;
   float sv[kWave / 2];
   uint32_t zv[kWave / 2];
+  const uint32_t NG = static_cast<uint32_t>(a.NG), N1 = static_cast<uint32_t>(a.N - 1);
+  const uint32_t g = static_cast<uint32_t>(br.g_lo) + static_cast<uint32_t>(c);
 #pragma unroll
   for (int p = 0; p < kWave / 2; ++p) {
-    const int r = min(p * per + lr, kBRows - 1);
-    const int64_t n = min(n0 + r, a.N - 1);
-    const int64_t g = br.g_lo + c;
-    sv[p] = a.scales[n * a.NG + g];
-    if constexpr (ZP != 0) zv[p] = zero_byte<ZP == 2>(a.zeros, n, a.NG, g);
+    const uint32_t r = static_cast<uint32_t>(min(p * per + lr, kBRows - 1));
+    const uint32_t n = min(static_cast<uint32_t>(n0) + r, N1);
+    sv[p] = *reinterpret_cast<const float*>(reinterpret_cast<const uint8_t*>(a.scales) + 4u * (n * NG + g));
+    if constexpr (ZP == 1) zv[p] = a.zeros[n * NG + g];
+    if constexpr (ZP == 2) zv[p] = a.zeros[n * ((NG + 1u) >> 1) + (g >> 1)];
   }
 #pragma unroll
   for (int p = 0; p < kWave / 2; ++p) {
@@ -341,15 +349,18 @@ hipError_t launch_batched2(const LinearArgs& a, hipStream_t s) {
 }  // namespace
 
 // Contiguous groups of 32, 64 or a multiple of 128 columns, K a multiple of
-// 1024 (every wave's quarter of K is whole batch pairs), 4 < M <= 16, and at
-// most 32 groups (16 with zero-points) in a quarter of K (the table).
-bool batched_shape_ok(int64_t M, int64_t K, int64_t G, bool has_g_idx, bool asym) {
+// 1024 (every wave's quarter of K is whole batch pairs), 4 < M <= 16, at most
+// 32 groups (16 with zero-points) in a quarter of K (the table), and codes
+// and activations whose byte offsets fit in 31 bits.
+bool batched_shape_ok(int64_t N, int64_t M, int64_t K, int64_t G, bool has_g_idx, bool asym) {
   if (has_g_idx || K % 1024 != 0 || M <= 4 || M > 16 || !(G == 32 || G == 64 || G % 128 == 0)) return false;
+  const int64_t lim = int64_t{1} << 31;   // 32-bit offsets
+  if (N * (K / 2) >= lim || M * K * 2 >= lim || N * ((K + G - 1) / G) * 4 >= lim) return false;
   for (int w = 0; w < kBWaves; ++w)
     if (b_range(w, K, G).count > (asym ? kBMaxGroupsZ : kBMaxGroups)) return false;
   return true;
 }
-bool batched_ok(const LinearArgs& a) { return batched_shape_ok(a.M, a.K, a.G, a.g_idx != nullptr, a.asym != 0); }
+bool batched_ok(const LinearArgs& a) { return batched_shape_ok(a.N, a.M, a.K, a.G, a.g_idx != nullptr, a.asym != 0); }
 
 hipError_t launch_batched(const LinearArgs& a, hipStream_t s) {
   if (!a.asym) return launch_batched2<0>(a, s);

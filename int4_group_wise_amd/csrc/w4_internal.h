@@ -121,7 +121,7 @@ hipError_t launch_stream(const LinearArgs& a, hipStream_t s);
 int stream_rows(int64_t N);
 // The one-launch batched decode (4 < M <= 16, contiguous groups of 32, 64 or a
 // multiple of 128, K % 128 == 0).
-bool batched_shape_ok(int64_t M, int64_t K, int64_t G, bool has_g_idx, bool asym);
+bool batched_shape_ok(int64_t N, int64_t M, int64_t K, int64_t G, bool has_g_idx, bool asym);
 // The act-order decode on the matrix cores (M = 1, g_idx, at most 32 groups
 // per row, K % 1024 == 0).
 bool act_mma_ok(const LinearArgs& a);

@@ -1042,7 +1042,7 @@ bool dot2_ok(const LinearArgs& a) {
 bool skinny_supported(const LinearArgs& a) { return a.M >= 1 && a.M <= 16; }
 
 size_t skinny_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t G, bool has_g_idx, bool asym) {
-  if (batched_shape_ok(M, K, G, has_g_idx, asym) || !rows_shape_ok(M, K, G, has_g_idx)) return 0;
+  if (batched_shape_ok(N, M, K, G, has_g_idx, asym) || !rows_shape_ok(M, K, G, has_g_idx)) return 0;
   const int sp = rows_splits(N, K);
   return sp > 1 ? static_cast<size_t>(sp) * static_cast<size_t>(M) * static_cast<size_t>(N) * sizeof(float) : 0;
 }
