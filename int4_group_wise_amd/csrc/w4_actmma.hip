@@ -50,30 +50,38 @@ struct AStage {
   int32_t gv[2][2];
 };
 
+// Offsets are 32-bit from the arrays' bases (act_mma_ok keeps them below
+// 2^31), so that every load takes a uniform base and one lane offset.
 struct ARows {
-  const uint8_t* c[2 * kARB];     // code row 8 i + l / 8 (at most N - 1) + 16 (l % 8)
-  const uint32_t* x;              // activation pair of columns 2 l, 2 l + 1
-  const int32_t* gi;              // g_idx + 2 l
+  const uint8_t* cb;              // code words
+  const uint8_t* xb;              // activations
+  const uint8_t* gb;              // g_idx
+  uint32_t c[2 * kARB];           // byte offset of code row 8 i + l / 8 (at most N - 1) + 16 (l % 8)
+  uint32_t l4;                    // 4 l: byte offset of the activation pair 2 l, 2 l + 1
 
   __device__ __forceinline__ ARows(const LinearArgs& a, int64_t n0, int lane) {
+    const uint32_t KB = static_cast<uint32_t>(a.K / 2), N1 = static_cast<uint32_t>(a.N - 1);
+    cb = a.codes;
+    xb = reinterpret_cast<const uint8_t*>(a.x);
+    gb = reinterpret_cast<const uint8_t*>(a.g_idx);
 #pragma unroll
-    for (int i = 0; i < 2 * kARB; ++i) c[i] = a.codes + min(n0 + 8 * i + (lane >> 3), a.N - 1) * (a.K / 2) + 16 * (lane & 7);
-    x = reinterpret_cast<const uint32_t*>(a.x) + lane;
-    gi = a.g_idx + 2 * lane;
+    for (int i = 0; i < 2 * kARB; ++i)
+      c[i] = min(static_cast<uint32_t>(n0) + 8u * i + static_cast<uint32_t>(lane >> 3), N1) * KB + 16u * (lane & 7);
+    l4 = 4u * lane;
   }
 };
 
 __device__ __forceinline__ void a_issue(const ARows& R, uint32_t p, AStage& st) {
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
-    const uint32_t k0 = 256u * p + 128u * j;
-    st.xv[j] = R.x[k0 / 2];
-    const int2 g = *reinterpret_cast<const int2*>(R.gi + k0);
+    const uint32_t k0 = 256u * p + 128u * j;   // first column of batch j
+    st.xv[j] = *reinterpret_cast<const uint32_t*>(R.xb + (2u * k0 + R.l4));
+    const int2 g = *reinterpret_cast<const int2*>(R.gb + (4u * k0 + 2u * R.l4));
     st.gv[j][0] = g.x;
     st.gv[j][1] = g.y;
   }
 #pragma unroll
-  for (int i = 0; i < 2 * kARB; ++i) st.cw[i] = *reinterpret_cast<const u32x4*>(R.c[i] + 128u * p);
+  for (int i = 0; i < 2 * kARB; ++i) st.cw[i] = *reinterpret_cast<const u32x4*>(R.cb + (R.c[i] + 128u * p));
   __builtin_amdgcn_sched_barrier(0);
 }
 
@@ -364,9 +372,10 @@ hipError_t launch_act_mma2(const LinearArgs& a, hipStream_t s) {
 }  // namespace
 
 // M = 1 with g_idx, at most 32 groups per row, K a multiple of 1024 (every
-// wave's quarter of K is whole batch pairs).
+// wave's quarter of K is whole batch pairs), code offsets below 2^31.
 bool act_mma_ok(const LinearArgs& a) {
-  return a.M == 1 && a.g_idx != nullptr && a.NG <= kAGroups && a.K % 1024 == 0;
+  return a.M == 1 && a.g_idx != nullptr && a.NG <= kAGroups && a.K % 1024 == 0 &&
+         a.N * (a.K / 2) < (int64_t{1} << 31);
 }
 
 hipError_t launch_act_mma(const LinearArgs& a, hipStream_t s) {
