@@ -209,8 +209,9 @@ def measured_traffic():
 def run_counters(w4):
     """Eager launches for rocprofv3 --pmc: 12 decode calls over 3 weight
     copies, then 3 plain device copies of 256 MiB that calibrate the counters,
-    then 8 batched-decode calls over 2 weight copies, 2 codec round trips
-    (quantize_pack + dequantize) and 3 prefill calls."""
+    then 8 batched-decode calls over 2 weight copies, 8 act-order decode calls
+    over 2 weight copies, 2 codec round trips (quantize_pack + dequantize) and
+    3 prefill calls."""
     from int4_group_wise_amd.workloads import workload, generate
     dev = "cuda:0"
     wl = workload("decode")
@@ -242,6 +243,19 @@ def run_counters(w4):
         w4.linear(x, c, s, None, None, wl.K, wl.G, wl.mode, None, out=y, workspace=ws)
     torch.cuda.synchronize()
     del sets, x, y, ws, t
+    # act-order decode (the decode shape with a permuted g_idx)
+    wl = workload("decode", act_order=True)
+    t = generate(wl)
+    gi = t["g_idx"].to(dev)
+    sets = [w4.quantize_pack(t["w"].to(dev), wl.G, wl.mode, gi) for _ in range(2)]
+    x, b = t["x"].to(dev), t["bias"].to(dev)
+    y = torch.empty(wl.M, wl.N, dtype=torch.bfloat16, device=dev)
+    torch.cuda.synchronize()
+    for i in range(8):
+        c, s, z = sets[i % 2]
+        w4.linear(x, c, s, z, gi, wl.K, wl.G, wl.mode, b, out=y)
+    torch.cuda.synchronize()
+    del sets, x, b, y, t, gi
     # codec round trip
     wl = workload("codec")
     w = generate(wl)["w"].to(dev)
