@@ -136,6 +136,15 @@ __device__ __forceinline__ void lds_dma16(const void* gsrc, void* ldst) {
                                        reinterpret_cast<uintptr_t>(ldst)), 16, 0, 0);
 }
 
+// The same copy through a buffer descriptor (MUBUF with the lds bit): the
+// compiler counts it on vmcnt alone, so fragment reads issued while such loads
+// are in flight keep exact lgkmcnt waits (with the global form it waits for
+// every LDS read), and an offset past the descriptor's size reads zeros.
+__device__ __forceinline__ void lds_buf16(__amdgpu_buffer_rsrc_t r, uint32_t voff, void* ldst) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, reinterpret_cast<__attribute__((address_space(3))) void*>(
+                                               reinterpret_cast<uintptr_t>(ldst)), 16, voff, 0, 0, 0);
+}
+
 // Tile (row tile tm, column tile tn) of workgroup b.  Workgroups are dealt to
 // the 8 XCDs round-robin (b % 8) and each XCD has its own L2, so when the tile
 // count divides by 8 each XCD's share is made a contiguous run of positions,
@@ -277,22 +286,25 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_pipe_kernel(
 // GEMM with a fragment-tiled weight (N % 128 == 0, K % 64 == 0): the same
 // 256 x 128 x 64 workgroup tile, 2 x 2 waves of 128 x 64 and
 // v_mfma_f32_32x32x16_bf16 as gemm_bf16_pipe_kernel, but only the activation
-// tile goes through LDS (a 3-stage ring of 32 KB stages filled by direct
-// loads).  The weight comes from the tiled layout written by the dequantizer
-// (w4_internal.h, tiled_unit): every 16-byte piece a lane needs for one MFMA
-// sits at consecutive addresses across the wave, so a wave reads its weight
-// fragments with fully coalesced 1 KB loads straight into registers, two
-// K-steps ahead.  Per K-step a CU then moves 32 KB of direct-load writes and
-// 64 KB of fragment reads through LDS instead of 48 KB and 96 KB.
+// tile goes through LDS (a 4-stage ring of 32 KB stages filled by direct
+// buffer loads).  The weight comes from the tiled layout written by the
+// dequantizer (w4_internal.h, tiled_unit): every 16-byte piece a lane needs for
+// one MFMA sits at consecutive addresses across the wave, so a wave reads its
+// weight fragments with fully coalesced 1 KB loads straight into registers.
+// Both are issued three K-steps ahead: the operands come from the L2 or past
+// it, and with one wave per SIMD nothing else hides their latency (two steps
+// ahead took 2.5 us more per call at the prefill shape, four 1 us less).  Per
+// K-step a CU moves 32 KB of direct-load writes and 64 KB of fragment reads
+// through LDS instead of 48 KB and 96 KB.
 //
 // K order inside a K-step: lane half h of an MFMA operand holds columns
 // 32 h + 8 ks .. 32 h + 8 ks + 7 for MFMA ks (activations: LDS chunk 4 h + ks
 // of the row; weight: the tiled unit (ks, h)); both operands agree, so the
 // MFMA sums the same products as with the natural order.
 // ---------------------------------------------------------------------------
-constexpr int TM = 256, TN = 128, TK = 64, TSTAGES = 3;
+constexpr int TM = 256, TN = 128, TK = 64, TSTAGES = 4;
 constexpr int kTStageBytes = TM * TK * 2;                // 32 KB: activations only
-constexpr int kTLdsBytes = TSTAGES * kTStageBytes;       // 96 KB
+constexpr int kTLdsBytes = TSTAGES * kTStageBytes;       // 128 KB
 
 __global__ __launch_bounds__(kThreads) void gemm_tiled_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ wt,
@@ -313,12 +325,15 @@ __global__ __launch_bounds__(kThreads) void gemm_tiled_kernel(
   // activation loads: as in gemm_bf16_pipe_kernel (wave wid fills rows
   // [64 wid, 64 wid + 64), lane i of an 8-row instruction slot i)
   const int lr = lane >> 3, ls = lane & 7;
-  const uint16_t* asrc[8];
+  // byte offsets from x (the launcher checks that x fits in 31 bits)
+  const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(x), 0, M * K * 2, 0x00020000);
+  uint32_t aoff[8];
 #pragma unroll
   for (int p = 0; p < 8; ++p) {
     const int r = 64 * wid + 8 * p + lr;
     const int gm = min(m0 + r, M - 1);    // rows past M load a valid row; never stored
-    asrc[p] = x + static_cast<int64_t>(gm) * K + 8 * (ls ^ swz(r));
+    aoff[p] = (static_cast<uint32_t>(gm) * static_cast<uint32_t>(K) + 8u * (ls ^ swz(r))) * 2u;
   }
   // weight: this wave's two 32-row blocks; unit (nb, kt, ks) starts at
   // ((nb KT + kt) 4 + ks) 64 units of 8 bf16, lane l at + l
@@ -327,17 +342,18 @@ __global__ __launch_bounds__(kThreads) void gemm_tiled_kernel(
   const int64_t bstride_nb = static_cast<int64_t>(KT) * 4 * 64 * 8;   // bf16 per 32-row block
   u32x4 breg[TSTAGES][2][4];
 
-  auto issue = [&](auto stage, int kt) {
+  // loads of K-step kt into stage S, half H: activation instruction slots
+  // 4H .. 4H + 3 and the weight block j = H
+  auto issue_half = [&](auto stage, auto half, int kt) {
     constexpr int S = decltype(stage)::value;
+    constexpr int H = decltype(half)::value;
     uint8_t* st = tsm + S * kTStageBytes;
     const int k0 = kt * TK;
 #pragma unroll
-    for (int p = 0; p < 8; ++p) lds_dma16(asrc[p] + k0, st + (64 * wid + 8 * p) * 128);
+    for (int p = 4 * H; p < 4 * H + 4; ++p) lds_buf16(xr, aoff[p] + 2u * k0, st + (64 * wid + 8 * p) * 128);
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks)
-        breg[S][j][ks] = *reinterpret_cast<const u32x4*>(bsrc0 + j * bstride_nb + (static_cast<int64_t>(kt) * 4 + ks) * 512);
+    for (int ks = 0; ks < 4; ++ks)
+      breg[S][H][ks] = *reinterpret_cast<const u32x4*>(bsrc0 + H * bstride_nb + (static_cast<int64_t>(kt) * 4 + ks) * 512);
   };
 
   f32x16_t acc[4][2];
@@ -349,58 +365,108 @@ __global__ __launch_bounds__(kThreads) void gemm_tiled_kernel(
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
 
   const int fr = lane & 31, fh = lane >> 5;
+  bf16x8_t af[4][4];   // [k-slice][row block] activation fragments
+  auto read_frag = [&](auto stage, auto slice) {
+    constexpr int S = decltype(stage)::value;
+    constexpr int KS = decltype(slice)::value;
+    const uint8_t* sa = tsm + S * kTStageBytes + (wm * 128) * 128;
+    const int chunk = 4 * fh + KS;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = 32 * i + fr;
+      af[KS][i] = *reinterpret_cast<const bf16x8_t*>(sa + r * 128 + 16 * (chunk ^ swz(r)));
+    }
+  };
+  auto mma = [&](auto stage, int ks) {
+    constexpr int S = decltype(stage)::value;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            af[ks][i], __builtin_bit_cast(bf16x8_t, breg[S][j][ks]), acc[i][j], 0, 0, 0);
+  };
+  // one half-step's order: the 8 fragment reads spread over its first 8
+  // MFMAs, the 8 loads over all 16
+  auto order = [&]() {
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);   // DS read
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // VMEM read
+    }
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+    }
+  };
+
+  // K-step kt (stage S): the first half runs the MFMAs of k-slices 0 and 1
+  // (fragments read during the previous step) while it reads slices 2 and 3;
+  // then, once every wave's loads of stage S + 1 have landed (one barrier per
+  // step), the second half runs slices 2 and 3 while it reads slices 0 and 1
+  // of stage S + 1.  Both halves issue half of the loads of step kt + 3 (the
+  // last steps' clamped to step KT - 1 again: the stage they fill is no longer
+  // read), so the count of loads in flight is the same at every barrier: 8 of
+  // step kt + 3 after the 16 each of steps kt + 1 and kt + 2.  The stage those
+  // loads fill was last read in step kt - 1, whose reads every wave finished
+  // before the barrier of step kt - 1 (lgkmcnt(0) there).
   auto step = [&](auto stage, int kt) {
     constexpr int S = decltype(stage)::value;
-    // this thread's loads of stage kt are done once at most the next stage's
-    // 16 loads (8 direct, 8 weight) are outstanding; then the barrier covers
-    // every thread's direct loads.  s_waitcnt: vmcnt in bits 3:0 and 15:14,
-    // 0x4F70 = vmcnt(16), 0x0F70 = vmcnt(0), expcnt and lgkmcnt not waited on.
-    // Every step issues the loads of step kt + 2 (the last step's again near
-    // the end: the stage they fill is no longer read), so the count of loads
-    // in flight is the same at every step.
-    __builtin_amdgcn_s_waitcnt(0x4F70);
+    constexpr int SN = (S + 1) % TSTAGES;
+    constexpr int SL = (S + 3) % TSTAGES;
+    const int kl = min(kt + 3, KT - 1);
+    issue_half(std::integral_constant<int, SL>{}, std::integral_constant<int, 0>{}, kl);
+    read_frag(std::integral_constant<int, S>{}, std::integral_constant<int, 2>{});
+    read_frag(std::integral_constant<int, S>{}, std::integral_constant<int, 3>{});
+    mma(std::integral_constant<int, S>{}, 0);
+    mma(std::integral_constant<int, S>{}, 1);
+    order();
+    __builtin_amdgcn_sched_barrier(0);
+    // s_waitcnt: vmcnt in bits 3:0 and 15:14, lgkmcnt in 11:8, expcnt in 6:4;
+    // 0x4078 = vmcnt(24) lgkmcnt(0)
+    __builtin_amdgcn_s_waitcnt(0x4078);
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
-    issue(std::integral_constant<int, (S + 2) % TSTAGES>{}, min(kt + 2, KT - 1));
-    __builtin_amdgcn_sched_barrier(0);   // the loads go out before this step's arithmetic
-    const uint8_t* sa = tsm + S * kTStageBytes + (wm * 128) * 128;
-    bf16x8_t af[4][4];
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      const int chunk = 4 * fh + ks;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = 32 * i + fr;
-        af[ks][i] = *reinterpret_cast<const bf16x8_t*>(sa + r * 128 + 16 * (chunk ^ swz(r)));
-      }
-    }
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks)
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-              af[ks][i], __builtin_bit_cast(bf16x8_t, breg[S][j][ks]), acc[i][j], 0, 0, 0);
-    // order: the 16 fragment reads first (all in flight together), then the
-    // 32 MFMAs, so that later sub-steps' reads overlap earlier MFMAs
-    __builtin_amdgcn_sched_group_barrier(0x100, 16, 0);   // DS read
-    __builtin_amdgcn_sched_group_barrier(0x008, 32, 0);   // MFMA
+    __builtin_amdgcn_sched_barrier(0);
+    issue_half(std::integral_constant<int, SL>{}, std::integral_constant<int, 1>{}, kl);
+    read_frag(std::integral_constant<int, SN>{}, std::integral_constant<int, 0>{});
+    read_frag(std::integral_constant<int, SN>{}, std::integral_constant<int, 1>{});
+    mma(std::integral_constant<int, S>{}, 2);
+    mma(std::integral_constant<int, S>{}, 3);
+    order();
+    __builtin_amdgcn_sched_barrier(0);
   };
 
-  issue(std::integral_constant<int, 0>{}, 0);
-  issue(std::integral_constant<int, 1>{}, min(1, KT - 1));
+  issue_half(std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{}, 0);
+  issue_half(std::integral_constant<int, 0>{}, std::integral_constant<int, 1>{}, 0);
+  issue_half(std::integral_constant<int, 1>{}, std::integral_constant<int, 0>{}, min(1, KT - 1));
+  issue_half(std::integral_constant<int, 1>{}, std::integral_constant<int, 1>{}, min(1, KT - 1));
+  issue_half(std::integral_constant<int, 2>{}, std::integral_constant<int, 0>{}, min(2, KT - 1));
+  issue_half(std::integral_constant<int, 2>{}, std::integral_constant<int, 1>{}, min(2, KT - 1));
+  // stage 0 landed in every wave (0x8F70 = vmcnt(32)); its slices 0 and 1
+  __builtin_amdgcn_s_waitcnt(0x8F70);
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+  read_frag(std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{});
+  read_frag(std::integral_constant<int, 0>{}, std::integral_constant<int, 1>{});
+  __builtin_amdgcn_sched_barrier(0);
   int kt = 0;
   for (; kt + TSTAGES <= KT; kt += TSTAGES) {
     step(std::integral_constant<int, 0>{}, kt);
     step(std::integral_constant<int, 1>{}, kt + 1);
     step(std::integral_constant<int, 2>{}, kt + 2);
+    step(std::integral_constant<int, 3>{}, kt + 3);
   }
   if (kt < KT) step(std::integral_constant<int, 0>{}, kt);
   if (kt + 1 < KT) step(std::integral_constant<int, 1>{}, kt + 1);
+  if (kt + 2 < KT) step(std::integral_constant<int, 2>{}, kt + 2);
   // the direct loads of the last issues must land before the workgroup's LDS
-  // is released
+  // is released (0x0F70 = vmcnt(0))
   __builtin_amdgcn_s_waitcnt(0x0F70);
 
   // 32 x 32 accumulator layout: register v of lane l holds row
@@ -450,7 +516,7 @@ hipError_t ensure_lds_attribute(const void* kernel, int bytes, int dev) {
 
 
 bool gemm_tiled_ok(int64_t M, int64_t N, int64_t K) {
-  return M >= 1 && N % TN == 0 && K % TK == 0 && M <= INT32_MAX && N <= INT32_MAX && K <= INT32_MAX;
+  return M >= 1 && N % TN == 0 && K % TK == 0 && M * K * 2 < (int64_t{1} << 31) && N <= INT32_MAX && K <= INT32_MAX;
 }
 
 hipError_t launch_gemm_tiled(const uint16_t* x, const uint16_t* wt, const uint16_t* bias, uint16_t* y,
