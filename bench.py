@@ -150,25 +150,50 @@ def bench_decode_hot(w4, steps=2000):
                        "weight_copies_rotated": 1}}
 
 
+def stream_read_lib():
+    """The streaming-read probe (libw4_bench.so, built next to libw4.so)."""
+    import ctypes
+    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "int4_group_wise_amd", "libw4_bench.so")
+    lib = ctypes.CDLL(path)
+    lib.w4bench_stream_read.restype = ctypes.c_int
+    lib.w4bench_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    return lib
+
+
 def bench_streaming_floor(nbytes, steps=4000):
-    """What one launch of a plain library kernel moving the same number of HBM
-    bytes achieves in this harness: torch's sum and amax reductions over an
-    fp32 buffer of `nbytes` and a device copy of nbytes / 2 bytes (read plus
-    write), each rotated past the Infinity Cache.  The fastest is reported as
-    the practical single-launch streaming rate next to the 8 TB/s peak."""
+    """What one launch moving the same number of HBM bytes achieves in this
+    harness: a plain streaming read of `nbytes` (16-byte non-temporal loads,
+    U per thread issued together, a workgroup reading U x 4 KB contiguously;
+    libw4_bench.so), torch's sum and amax reductions over the same fp32
+    buffer, and a device copy of nbytes / 2 bytes (read plus write), each
+    rotated past the Infinity Cache.  The fastest is reported as the practical
+    single-launch rate next to the 8 TB/s peak."""
     dev = "cuda:0"
     count = max(2, math.ceil(2 * MALL_BYTES / nbytes))
     bufs = [torch.empty(nbytes // 4, dtype=torch.float32, device=dev).normal_() for _ in range(count)]
     halves = [torch.empty(nbytes // 4, dtype=torch.bfloat16, device=dev) for _ in range(count)]
+    sink = torch.zeros(max(1, nbytes // 8192), dtype=torch.int32, device=dev)
+    lib = stream_read_lib()
+
+    def read(u):
+        def fn(i):
+            err = lib.w4bench_stream_read(bufs[i].data_ptr(), nbytes, u, sink.data_ptr(),
+                                          torch.cuda.current_stream().cuda_stream)
+            if err:
+                raise RuntimeError(f"stream_read U={u}: HIP error {err}")
+        return fn
+
+    cases = [(f"stream_read U={u}", read(u)) for u in (4, 8, 16) if nbytes % (4096 * u) == 0]
     res = {}
-    for name, fn in (("torch.sum", lambda i: torch.sum(bufs[i])),
+    for name, fn in (*cases,
+                     ("torch.sum", lambda i: torch.sum(bufs[i])),
                      ("torch.amax", lambda i: torch.amax(bufs[i])),
                      ("copy_ (read + write)", lambda i: halves[i].copy_(bufs[i][: nbytes // 8].view(torch.bfloat16)))):
         ev_ms, _ = time_graph(fn, count * max(1, 64 // count), steps, count, count)
         us = ev_ms * 1e3 / steps
         res[name] = {"us_per_launch": round(us, 3), "GB/s": round(nbytes / us / 1e3, 1)}
     best = max(res, key=lambda k: res[k]["GB/s"])
-    del bufs, halves
+    del bufs, halves, sink
     return {"GB/s": res[best]["GB/s"], "kernel": best, "bytes_per_launch": nbytes, "measured": res}
 
 
