@@ -384,7 +384,9 @@ __global__ __launch_bounds__(kGThreads) void dequantize_t_kernel(DequantArgs a, 
 #pragma unroll
       for (int i = 0; i < 4; ++i) q[i] = *reinterpret_cast<const uint32_t*>(&tile[kl][nq + 8 * h2 + 2 * i]);
       const int64_t unit = tiled_unit(k, n0 + nq + 8 * h2, a.N);
-      __builtin_nontemporal_store(q, reinterpret_cast<u32x4*>(wt + 8 * unit));
+      // a plain store: the workspace is read back by the GEMM right after,
+      // from the Infinity Cache when it is still there
+      *reinterpret_cast<u32x4*>(wt + 8 * unit) = q;
     }
   } else {
     const int kl = threadIdx.x >> 2, nq = (threadIdx.x & 3) * 16;
