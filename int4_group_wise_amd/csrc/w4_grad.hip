@@ -450,6 +450,138 @@ GradPlan grad_plan(int64_t M, int64_t N, int64_t K, int64_t G, bool has_g_idx) {
   return p;
 }
 
+namespace {
+
+// Transposed dequantize into the tiled layout with value tables: a workgroup
+// owns 64 weight rows and a run of 128-column sub-tiles.  It builds once, in
+// LDS, the 16 bf16 values each (row, group) can decode to (one fp32 multiply
+// and one rounding each, as w4_dequantize), then per sub-tile stages the
+// 64 x 64 code bytes and the columns' group offsets in LDS (double-buffered,
+// the next sub-tile's loads in flight) and turns every weight into one table
+// read.  A lane writes two adjacent 16-byte units of Wd^T (8 consecutive rows
+// n at columns k and k + 1, the two nibbles of one code byte per row), so each
+// half of a wave writes 1 KB contiguously.  Tables of up to 32 groups per row.
+constexpr int kTVRows = 64;     // weight rows per workgroup
+constexpr int kTVCols = 128;    // columns per sub-tile
+constexpr int kTVCodeRow = 80;  // LDS bytes per staged code row (64 + 16 of padding)
+constexpr int kTVMaxGroups = 32;
+__host__ __device__ inline int tv_table_stride(int64_t NG) { return static_cast<int>(NG) * 32 + 4; }
+size_t tv_lds_bytes(int64_t NG) {
+  return static_cast<size_t>(kTVRows) * tv_table_stride(NG) + 2 * kTVRows * kTVCodeRow + 2 * kTVCols * 2;
+}
+
+template <bool ASYM, bool GIDX>
+__global__ __launch_bounds__(kGThreads) void dequantize_tv_kernel(DequantArgs a, uint16_t* __restrict__ wt, int ksub) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t vsm[];
+  const int NG = static_cast<int>(a.NG);
+  const int stride = tv_table_stride(NG);
+  uint8_t* vt = vsm;                                                   // [64 rows][stride]
+  uint8_t* ct = vsm + kTVRows * stride;                                // [2][64 rows][kTVCodeRow]
+  uint16_t* gs = reinterpret_cast<uint16_t*>(ct + 2 * kTVRows * kTVCodeRow);   // [2][128] group byte offsets
+  const int t = threadIdx.x;
+  const int64_t n0 = static_cast<int64_t>(blockIdx.y) * kTVRows;
+  const int K = static_cast<int>(a.K);
+  const int64_t KB = a.K / 2;
+  const int sub0 = blockIdx.x * ksub;
+  const int nsub = min(ksub, K / kTVCols - sub0);
+
+  // loads: table inputs first (they gate the build), then sub-tile 0's code
+  // bytes (thread t: row t / 4, 16 bytes at 16 (t % 4)) and group indices
+  const int entries = kTVRows * NG;                    // <= 64 * 32: 8 per thread
+  float tsc[8];
+  int tz[8];
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    const int e = min(t + kGThreads * q, entries - 1);
+    const int r = e / NG, g = e % NG;
+    tsc[q] = a.scales[(n0 + r) * a.NG + g];
+    tz[q] = ASYM ? static_cast<int>(zero_row(a.zeros, n0 + r, a.NG, a.zpk)[g]) : 8;
+  }
+  const uint8_t* crow = a.codes + (n0 + (t >> 2)) * KB + 16 * (t & 3);
+  auto load_codes = [&](int sub) -> u32x4 {
+    return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(crow + static_cast<int64_t>(sub0 + sub) * (kTVCols / 2)));
+  };
+  auto load_group = [&](int sub) -> int {
+    const int k = (sub0 + sub) * kTVCols + (t & (kTVCols - 1));
+    return GIDX ? min(max(a.g_idx[k], 0), NG - 1) : k / static_cast<int>(a.G);
+  };
+  u32x4 cnext = load_codes(0);
+  int gnext = load_group(0);
+
+  // value table: entry (row r, group g, nibble u) at r * stride + 32 g + 2 u
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    const int e = t + kGThreads * q;
+    if (e >= entries) break;
+    const int r = e / NG, g = e % NG;
+    uint32_t* dst = reinterpret_cast<uint32_t*>(vt + r * stride + 32 * g);
+#pragma unroll
+    for (int u = 0; u < 16; u += 2) {
+      const float v0 = static_cast<float>((ASYM ? u : (u ^ 8)) - tz[q]) * tsc[q];
+      const float v1 = static_cast<float>((ASYM ? u + 1 : ((u + 1) ^ 8)) - tz[q]) * tsc[q];
+      dst[u / 2] = __builtin_bit_cast(uint32_t, bf16x2_t{static_cast<__bf16>(v0), static_cast<__bf16>(v1)});
+    }
+  }
+  auto stage = [&](int buf) {
+    *reinterpret_cast<u32x4*>(ct + (buf * kTVRows + (t >> 2)) * kTVCodeRow + 16 * (t & 3)) = cnext;
+    if (t < kTVCols) gs[buf * kTVCols + t] = static_cast<uint16_t>(32 * gnext);
+  };
+  stage(0);
+  if (nsub > 1) {
+    cnext = load_codes(1);
+    gnext = load_group(1);
+  }
+  __syncthreads();
+
+  // lane (kb2, h, kp) of wave w: rows 8 c .. 8 c + 7 with c = 4 h + w (unit
+  // slot w = c % 4, half h = c / 4), columns 32 kb + 2 kp and + 1 of the
+  // sub-tile for the 32-column blocks kb = 2 kbt + kb2, kbt = 0, 1
+  const int lane = lane_id();
+  const int w = t >> 6;
+  const int kb2 = lane >> 5, h = (lane >> 4) & 1, kp = lane & 15;
+  const int c = 4 * h + w;
+  uint32_t rbase[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) rbase[i] = static_cast<uint32_t>((8 * c + i) * stride);
+  const int64_t NB = a.N / 64;
+  for (int j = 0; j < nsub; ++j) {
+    const int buf = j & 1;
+    const uint8_t* cb = ct + buf * kTVRows * kTVCodeRow;
+    const int kcol0 = (sub0 + j) * kTVCols;
+#pragma unroll
+    for (int kbt = 0; kbt < 2; ++kbt) {
+      const int kb = 2 * kbt + kb2;
+      uint32_t b[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) b[i] = cb[(8 * c + i) * kTVCodeRow + 16 * kb + kp];
+      const uint32_t go = *reinterpret_cast<const uint32_t*>(gs + buf * kTVCols + 32 * kb + 2 * kp);
+      const uint32_t go0 = go & 0xFFFFu, go1 = go >> 16;
+      uint32_t v0[8], v1[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        v0[i] = *reinterpret_cast<const uint16_t*>(vt + rbase[i] + go0 + 2 * (b[i] & 15u));
+        v1[i] = *reinterpret_cast<const uint16_t*>(vt + rbase[i] + go1 + 2 * (b[i] >> 4));
+      }
+      const int64_t kg = kcol0 + 32 * kb + 2 * kp;     // even column of the pair
+      const int64_t unit = (((kg / 32) * NB + n0 / 64) * 4 + w) * 64 + 32 * h + (kg & 31);
+      u32x4* dst = reinterpret_cast<u32x4*>(wt + 8 * unit);
+      // plain stores: the GEMM reads the workspace right after
+      dst[0] = u32x4{v0[0] | (v0[1] << 16), v0[2] | (v0[3] << 16), v0[4] | (v0[5] << 16), v0[6] | (v0[7] << 16)};
+      dst[1] = u32x4{v1[0] | (v1[1] << 16), v1[2] | (v1[3] << 16), v1[4] | (v1[5] << 16), v1[6] | (v1[7] << 16)};
+    }
+    if (j + 1 < nsub) {
+      stage(buf ^ 1);
+      if (j + 2 < nsub) {
+        cnext = load_codes(j + 2);
+        gnext = load_group(j + 2);
+      }
+    }
+    __syncthreads();
+  }
+}
+
+}  // namespace
+
 hipError_t launch_grad_input(const GradArgs& a, hipStream_t s) {
   if (a.M <= 0) return hipSuccess;
   const GradPlan p = grad_plan(a.M, a.N, a.K, a.G, a.g_idx != nullptr);
@@ -477,6 +609,35 @@ hipError_t launch_grad_input(const GradArgs& a, hipStream_t s) {
   const dim3 grid(static_cast<uint32_t>((a.K + kTT - 1) / kTT), static_cast<uint32_t>((a.N + kTT - 1) / kTT));
   const size_t lds0 = kTT * (kTT + 2) * 2 + kTT * 4;
   const size_t lds = lds0 + static_cast<size_t>(kTT) * (4 * tstab_stride(a.NG) + tztab_stride(a.NG));
+  if (gemm_tiled_ok(a.M, a.K, a.N) && a.K % 128 == 0 && a.N % 64 == 0 && a.NG <= kTVMaxGroups &&
+      a.N / kTVRows <= 65535) {
+    // Wd^T in the tiled layout through per-(row, group) value tables, then the GEMM
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    const size_t tlds = tv_lds_bytes(a.NG);
+    const void* kern = a.asym ? (a.g_idx ? reinterpret_cast<const void*>(dequantize_tv_kernel<true, true>)
+                                         : reinterpret_cast<const void*>(dequantize_tv_kernel<true, false>))
+                              : (a.g_idx ? reinterpret_cast<const void*>(dequantize_tv_kernel<false, true>)
+                                         : reinterpret_cast<const void*>(dequantize_tv_kernel<false, false>));
+    // the attribute is set once per kernel and device: allow the largest table
+    e = ensure_lds_attribute(kern, static_cast<int>(tv_lds_bytes(kTVMaxGroups)), dev);
+    if (e != hipSuccess) return e;
+    // about 512 workgroups: runs of sub-tiles along K
+    const int64_t subs = a.K / kTVCols, rblk = a.N / kTVRows;
+    const int ksub = static_cast<int>(std::max<int64_t>(1, (subs * rblk + 511) / 512));
+    const dim3 tgrid(static_cast<uint32_t>((subs + ksub - 1) / ksub), static_cast<uint32_t>(rblk));
+    if (a.asym) {
+      if (a.g_idx) dequantize_tv_kernel<true, true><<<tgrid, dim3(kGThreads), tlds, s>>>(d, wt, ksub);
+      else dequantize_tv_kernel<true, false><<<tgrid, dim3(kGThreads), tlds, s>>>(d, wt, ksub);
+    } else {
+      if (a.g_idx) dequantize_tv_kernel<false, true><<<tgrid, dim3(kGThreads), tlds, s>>>(d, wt, ksub);
+      else dequantize_tv_kernel<false, false><<<tgrid, dim3(kGThreads), tlds, s>>>(d, wt, ksub);
+    }
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    return launch_gemm_tiled(a.dy, wt, nullptr, a.dx, a.M, a.K, a.N, s);
+  }
   if (lds <= 65536 && gemm_tiled_ok(a.M, a.K, a.N) && a.K % 128 == 0 && a.N % 64 == 0) {
     // Wd^T in the tiled layout, then the GEMM that reads it straight into registers
     if (a.asym) {

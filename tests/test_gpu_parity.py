@@ -531,8 +531,14 @@ GRAD_CASES = [
     (48, 64, 256, 64, "asym", False), (300, 130, 200, 8, "sym", True), (40, 96, 512, 128, "asym", False),
     (17, 1, 64, 16, "sym", False), (20, 24, 2048, 8, "asym", True),   # 256 groups: tables read from memory
     (1, 64, 4100, -1, "asym", False), (2, 50, 4096, -1, "sym", False), (20, 40, 300, -1, "sym", False),
-    # transposed weight in the GEMM's tiled layout (N % 64 == 0, K % 128 == 0)
+    # transposed weight in the GEMM's tiled layout (N % 64 == 0, K % 128 == 0), through value
+    # tables (at most 32 groups per row): one 64-row block, full tables, contiguous and act-order,
+    # 9 sub-tiles of 128 columns split over workgroups in runs of 2 (the last run short)
     (33, 128, 384, 64, "sym", True), (130, 192, 1024, 128, "asym", False),
+    (64, 64, 256, 32, "asym", True), (20, 128, 4096, 128, "asym", True), (33, 192, 2048, 64, "asym", False),
+    (17, 4096, 1152, 128, "sym", False),
+    # more than 32 groups per row: the tiled layout without value tables
+    (24, 64, 4096, 64, "asym", True),
 ]
 
 
@@ -553,10 +559,11 @@ def test_grad_input_prefill_size():
 
 
 @pytest.mark.parametrize("M,K,mode,N", [(3, 520, "sym", 40), (24, 256, "asym", 40),
-                                        (40, 512, "asym", 128), (64, 256, "sym", 64)])
+                                        (40, 512, "asym", 128), (64, 256, "sym", 64), (48, 256, "asym", 128)])
 def test_grad_input_unit_rows_are_exact(M, K, mode, N):
     """dy row m = e_{n_m}: dx row m is the bf16 dequantized row n_m, bit for bit
-    (the last two shapes take the tiled transposed weight)."""
+    (the last three shapes take the tiled transposed weight, the last two through
+    value tables)."""
     G = 8
     rng = np.random.default_rng(32)
     w = (rng.standard_normal((N, K)) * 0.02).astype(np.float32)
