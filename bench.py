@@ -235,8 +235,8 @@ def run_counters(w4):
     """Eager launches for rocprofv3 --pmc: 12 decode calls over 3 weight
     copies, then 3 plain device copies of 256 MiB that calibrate the counters,
     then 8 batched-decode calls over 2 weight copies, 8 act-order decode calls
-    over 2 weight copies, 2 codec round trips (quantize_pack + dequantize) and
-    3 prefill calls."""
+    over 2 weight copies, 2 codec round trips (quantize_pack + dequantize),
+    3 prefill calls and 3 prefill-shape input-gradient calls."""
     from int4_group_wise_amd.workloads import workload, generate
     dev = "cuda:0"
     wl = workload("decode")
@@ -300,6 +300,11 @@ def run_counters(w4):
     ws = torch.empty(w4.linear_workspace_bytes(wl.M, wl.N, wl.K, wl.G, wl.mode, True), dtype=torch.uint8, device=dev)
     for _ in range(3):
         w4.linear(x, c, s, z, gi, wl.K, wl.G, wl.mode, None, out=y, workspace=ws)
+    torch.cuda.synchronize()
+    # prefill-shape input gradient (transposed dequantize + GEMM)
+    dy = y.clone()
+    for _ in range(3):
+        w4.linear_grad_input(dy, c, s, z, gi, wl.K, wl.G, wl.mode)
     torch.cuda.synchronize()
     print("counter launches done", flush=True)
 

@@ -265,6 +265,9 @@ CODEC_SHAPES = [
     (6, 4100, 128, torch.bfloat16), (4, 3000, 256, torch.float32), (3, 16384, 512, torch.bfloat16),
     (2, 16383, 8, torch.float32), (3, 16385, 64, torch.bfloat16), (9, 2047, 16, torch.bfloat16),
     (13, 2111, 64, torch.float32), (3, 6000, 48, torch.bfloat16),
+    # groups of 32 (a lane per group, runs of 64 groups): one partial group, a partial
+    # third run with rows at 4-byte offsets, fp32 rows past two runs
+    (5, 21, 32, torch.float32), (6, 4190, 32, torch.bfloat16), (3, 6145, 32, torch.float32),
 ]
 
 
@@ -329,10 +332,11 @@ def test_codec_degenerate_values():
     w[6, ::7] = 1.0                                           # sparse
     w[7] = -0.0
     wide = w.repeat(1, 2048 // K)                             # the same rows at K = 2048
-    for mode in ("sym", "asym"):
-        for x, lab in ((w, ""), (wide, " wide")):
-            _check_codec(x, G, mode, label=f"degenerate{lab} {mode}")
-            _check_codec(x.to(torch.bfloat16), G, mode, label=f"degenerate{lab} bf16 {mode}")
+    for gs in (G, 32):                                        # 32: the lane-per-group quantizer
+        for mode in ("sym", "asym"):
+            for x, lab in ((w, ""), (wide, " wide")):
+                _check_codec(x, gs, mode, label=f"degenerate{lab} G{gs} {mode}")
+                _check_codec(x.to(torch.bfloat16), gs, mode, label=f"degenerate{lab} G{gs} bf16 {mode}")
 
 
 def _subnormal_scale_rows(K, G):
