@@ -401,13 +401,13 @@ def bench_secondary(w4):
     del c, s
     y = torch.empty(wl.M, wl.N, dtype=torch.bfloat16, device=dev)
     bws = torch.empty(max(1, w4.linear_workspace_bytes(wl.M, wl.N, wl.K, wl.G, wl.mode)), dtype=torch.uint8, device=dev)
-    steps = 100
+    steps = 1000   # about 40 ms timed, as long as the headline's warm-up
 
     def call_b(i):
         cc, ss = rot.sets[i]
         w4.linear(x, cc, ss, None, None, wl.K, wl.G, wl.mode, None, out=y, workspace=bws)
 
-    ev_ms, _ = time_graph(call_b, rot.count * 5, steps, rot.count, rot.count)
+    ev_ms, _ = time_graph(call_b, rot.count * 10, steps, rot.count * 10, rot.count)
     nb = algorithmic_bytes_linear(wl.M, wl.N, wl.K, wl.G, False, False)
     gbs = nb * steps / (ev_ms * 1e-3) / 1e9
     out["batched_decode"] = {"metric": "W4A16 linear HBM GB/s M=16", "value": round(gbs, 1), "unit": "GB/s",
