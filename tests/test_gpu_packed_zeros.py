@@ -49,6 +49,7 @@ LINEAR_CASES = [
     (1, 300, 4096, 128, True),      # act-order decode on the matrix cores
     (1, 70, 2048, 128, True),       # the same, 16 groups (one half)
     (16, 256, 4096, 128, False),    # one-launch batched decode
+    (12, 16500, 2048, 64, False),   # one-launch batched decode, 258 workgroups
     (64, 256, 1024, 128, True),     # prefill, tiled weight, act-order
     (48, 256, 2048, 128, False),    # prefill, tiled weight
     (40, 130, 640, 64, False),      # prefill, row-major weight (N % 128 != 0), 10 groups

@@ -172,6 +172,11 @@ CASES = [
     (8, 96, 6144, 64, "sym", False, "f32", "none"),
     (13, 200, 7168, 128, "asym", False, "bf16", "randn"),
     (16, 64, 12288, 128, "sym", False, "f32", "randn"),
+    # the one-launch batched decode over hundreds of workgroups (more than one
+    # per CU): 1, 3 and 4 batch pairs per wave, row tails
+    (5, 16400, 1024, 32, "asym", False, "f32", "randn"),
+    (16, 20000, 3072, 64, "sym", False, "bf16", "none"),
+    (12, 17000, 4096, 128, "sym", False, "f32", "randn"),
     (1, 37, 2048, 64, "asym", False, "f32", "randn"),   # staged decode, row tail
     (1, 50, 4096, 256, "sym", False, "bf16", "none"),   # staged decode, signed
     (1, 24, 16384, 256, "asym", False, "f32", "randn"), # staged decode, longest row, 64 groups
