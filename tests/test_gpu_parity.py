@@ -542,10 +542,11 @@ GRAD_CASES = [
     (1, 64, 4100, -1, "asym", False), (2, 50, 4096, -1, "sym", False), (20, 40, 300, -1, "sym", False),
     # transposed weight in the GEMM's tiled layout (N % 64 == 0, K % 128 == 0), through value
     # tables (at most 32 groups per row): one 64-row block, full tables, contiguous and act-order,
-    # 9 sub-tiles of 128 columns split over workgroups in runs of 2 (the last run short)
+    # 9 sub-tiles of 128 columns split over workgroups in runs of 2 (the last run short),
+    # one sub-tile of one row block, per-channel (one group)
     (33, 128, 384, 64, "sym", True), (130, 192, 1024, 128, "asym", False),
     (64, 64, 256, 32, "asym", True), (20, 128, 4096, 128, "asym", True), (33, 192, 2048, 64, "asym", False),
-    (17, 4096, 1152, 128, "sym", False),
+    (17, 4096, 1152, 128, "sym", False), (17, 64, 128, 64, "sym", False), (24, 64, 1024, -1, "asym", False),
     # more than 32 groups per row: the tiled layout without value tables
     (24, 64, 4096, 64, "asym", True),
 ]
