@@ -378,9 +378,11 @@ def bench_secondary(w4):
     x = t["x"].to(dev)
     y = torch.empty(wl.M, wl.N, dtype=torch.bfloat16, device=dev)
     ws = torch.empty(w4.linear_workspace_bytes(wl.M, wl.N, wl.K, wl.G, wl.mode, True), dtype=torch.uint8, device=dev)
-    steps = 200
+    # 400 warm-up calls (about 30 ms): the first few hundred calls of a process run a few
+    # percent slower than the steady state that 1000 timed calls then measure
+    steps = 1000
     ev_ms, host_ms = time_graph(lambda i: w4.linear(x, c, s, z, gi, wl.K, wl.G, wl.mode, None, out=y, workspace=ws),
-                                20, steps, 20, 1)
+                                20, steps, 400, 1)
     flops = 2.0 * wl.M * wl.N * wl.K
     tfs = flops * steps / (ev_ms * 1e-3) / 1e12
     out["prefill_gemm"] = {"metric": "W4A16 linear TFLOP/s M=2048", "value": round(tfs, 2), "unit": "TFLOP/s",
@@ -452,9 +454,9 @@ def bench_secondary(w4):
     del t
     dx = torch.empty(wl.M, wl.K, dtype=torch.bfloat16, device=dev)
     gws = torch.empty(w4.linear_grad_input_workspace_bytes(wl.M, wl.N, wl.K, wl.G, wl.mode, True), dtype=torch.uint8, device=dev)
-    steps = 200
+    steps = 1000   # warm-up and length as the prefill linear's
     ev_ms, _ = time_graph(lambda i: w4.linear_grad_input(dy, c, s, z, gi, wl.K, wl.G, wl.mode, out=dx, workspace=gws),
-                          20, steps, 20, 1)
+                          20, steps, 400, 1)
     tfs = 2.0 * wl.M * wl.N * wl.K * steps / (ev_ms * 1e-3) / 1e12
     out["grad_input_prefill"] = {"metric": "W4A16 input gradient TFLOP/s M=2048", "value": round(tfs, 2), "unit": "TFLOP/s",
                                  "us_per_call": round(ev_ms * 1e3 / steps, 2),
