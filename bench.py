@@ -365,11 +365,11 @@ def bench_secondary(w4):
     wf = t["w"].to(dev)
     c, s, z = w4.quantize_pack(wf, wl.G, wl.mode, gi)
     # its act-order quantize: fp32 W [4096, 4096] -> codes, scales, zero-points
-    ev_ms, _ = time_graph(lambda i: w4.quantize_pack(wf, wl.G, wl.mode, gi, out=(c, s, z)), 20, 200, 20, 1)
+    ev_ms, _ = time_graph(lambda i: w4.quantize_pack(wf, wl.G, wl.mode, gi, out=(c, s, z)), 20, 1000, 200, 1)
     qb = wf.numel() * 4 + gi.numel() * 4 + c.numel() + s.numel() * 4 + z.numel()
-    gq = qb * 200 / (ev_ms * 1e-3) / 1e9
+    gq = qb * 1000 / (ev_ms * 1e-3) / 1e9
     out["prefill_quantize"] = {"metric": "act-order quantize_pack HBM GB/s", "value": round(gq, 1), "unit": "GB/s",
-                               "us_per_call": round(ev_ms * 1e3 / 200, 2),
+                               "us_per_call": round(ev_ms * 1e3 / 1000, 2),
                                "roofline": {"bound": "hbm", "achieved": round(gq, 1), "peak": HBM_PEAK_GBS,
                                             "unit": "GB/s", "frac": round(gq / HBM_PEAK_GBS, 4)},
                                "config": {"workload": "prefill", "N": wl.N, "K": wl.K, "G": wl.G, "mode": wl.mode,
@@ -479,7 +479,7 @@ def bench_secondary(w4):
     outs = (torch.empty_like(c), torch.empty_like(s), torch.empty_like(z))
     steps = 200
     ev_ms, _ = time_graph(lambda i: w4.lora_merge(c, s, z, None, wl.K, wl.G, wl.mode, la, lb, 2.0, out=outs),
-                          20, steps, 20, 1)
+                          20, steps, 100, 1)
     sec = ev_ms * 1e-3 / steps
     fl = 2.0 * wl.N * wl.K * rank                        # fp64 multiply-adds of the update
     nbytes = 2 * (c.numel() + s.numel() * 4 + z.numel()) + (la.numel() + lb.numel()) * 4
@@ -499,10 +499,10 @@ def bench_secondary(w4):
     del t
     c, s, _ = w4.quantize_pack(w, wl.G, wl.mode)
     d = torch.empty(wl.N, wl.K, dtype=torch.bfloat16, device=dev)
-    # 20 untimed calls, then 40 timed: the quantizers are VALU-bound and their
-    # per-call time follows the clock under sustained load (about 120-170 us
-    # within one run), so the average is taken over a longer run
-    steps, warm = 40, 20
+    # 100 untimed calls, then 200 timed (about 30 ms): the quantizers are
+    # VALU-bound and their per-call time follows the clock under sustained load
+    # (about 120-170 us within one run), so the average is taken over a longer run
+    steps, warm = 200, 100
     c2, s2 = torch.empty_like(c), torch.empty_like(s)
     ev_q, _ = time_graph(lambda i: w4.quantize_pack(w, wl.G, wl.mode, out=(c2, s2, None)), 5, steps, warm, 1)
     ev_d, _ = time_graph(lambda i: w4.dequantize(c, s, None, None, wl.K, wl.G, wl.mode, out=d), 5, steps, warm, 1)
@@ -540,12 +540,12 @@ def bench_secondary(w4):
     zt = torch.randint(0, 16, (28672, 256), dtype=torch.uint8, device=dev)
     zp = w4.pack_zeros(zt)
     zu = torch.empty_like(zt)
-    ev_p, _ = time_graph(lambda i: w4.pack_zeros(zt, out=zp), 20, 200, 20, 1)
-    ev_u, _ = time_graph(lambda i: w4.unpack_zeros(zp, 256, out=zu), 20, 200, 20, 1)
+    ev_p, _ = time_graph(lambda i: w4.pack_zeros(zt, out=zp), 20, 2000, 200, 1)
+    ev_u, _ = time_graph(lambda i: w4.unpack_zeros(zp, 256, out=zu), 20, 2000, 200, 1)
     zb = zt.numel() + zp.numel()
     out["packed_zeros"] = {"metric": "zero-point pack / unpack HBM GB/s", "unit": "GB/s",
-                           "pack": {"GB/s": round(zb * 200 / (ev_p * 1e-3) / 1e9, 1), "us": round(ev_p * 1e3 / 200, 2)},
-                           "unpack": {"GB/s": round(zb * 200 / (ev_u * 1e-3) / 1e9, 1), "us": round(ev_u * 1e3 / 200, 2)},
+                           "pack": {"GB/s": round(zb * 2000 / (ev_p * 1e-3) / 1e9, 1), "us": round(ev_p * 1e3 / 2000, 2)},
+                           "unpack": {"GB/s": round(zb * 2000 / (ev_u * 1e-3) / 1e9, 1), "us": round(ev_u * 1e3 / 2000, 2)},
                            "config": {"N": 28672, "NG": 256}}
     return out
 
