@@ -81,7 +81,8 @@ __device__ __forceinline__ void a_issue(const ARows& R, uint32_t p, AStage& st) 
     st.gv[j][1] = g.y;
   }
 #pragma unroll
-  for (int i = 0; i < 2 * kARB; ++i) st.cw[i] = *reinterpret_cast<const u32x4*>(R.cb + (R.c[i] + 128u * p));
+  for (int i = 0; i < 2 * kARB; ++i)   // code words are read once: non-temporal
+    st.cw[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(R.cb + (R.c[i] + 128u * p)));
   __builtin_amdgcn_sched_barrier(0);
 }
 

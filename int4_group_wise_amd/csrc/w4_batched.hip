@@ -115,7 +115,8 @@ __device__ __forceinline__ void b_issue(const BRows<U>& R, uint32_t p, BStage& s
 #pragma unroll
   for (int j = 0; j < 8; ++j) st.x[j] = *reinterpret_cast<const u32x4*>(R.xb + (R.x[j & 3] + 512u * p + 256u * (j >> 2)));
 #pragma unroll
-  for (int i = 0; i < 2 * kBRB; ++i) st.cw[i] = *reinterpret_cast<const u32x4*>(R.cb + (R.c[i] + 128u * p));
+  for (int i = 0; i < 2 * kBRB; ++i)   // code words are read once: non-temporal
+    st.cw[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(R.cb + (R.c[i] + 128u * p)));
   __builtin_amdgcn_sched_barrier(0);
 }
 
