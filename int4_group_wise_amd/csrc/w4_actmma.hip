@@ -174,7 +174,8 @@ __device__ __forceinline__ void a_epilogue_loads(const LinearArgs& a, int64_t n0
       for (int h = 0; h < H; ++h) {
         const int g0 = 16 * h + 4 * q;
         const int gc = min(g0, NG - 4);
-        const f32x4_t v = *reinterpret_cast<const f32x4_t*>(a.scales + row * a.NG + gc);
+        // read once per call: non-temporal
+        const f32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(a.scales + row * a.NG + gc));
 #pragma unroll
         for (int t = 0; t < 4; ++t) ep.sc[rb][h][t] = g0 < NG ? v[t] : 0.0f;
         if constexpr (ZP == 1) ep.zw[rb][h][0] = *reinterpret_cast<const uint32_t*>(a.zeros + row * a.NG + gc);
@@ -225,7 +226,7 @@ __device__ __forceinline__ void a_table_issue(const LinearArgs& a, int64_t n0, i
   const int NG = static_cast<int>(a.NG);
   const int64_t row = min(n0 + 8 * w + (lane >> 3), a.N - 1);
   const int c = min(lane & 7, NG / 4 - 1);
-  tl.s = *reinterpret_cast<const f32x4_t*>(a.scales + row * a.NG + 4 * c);
+  tl.s = __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(a.scales + row * a.NG + 4 * c));
   if constexpr (ZP == 1) tl.z = *reinterpret_cast<const uint32_t*>(a.zeros + row * a.NG + 4 * c);
   if constexpr (ZP == 2) tl.z = *reinterpret_cast<const uint16_t*>(a.zeros + row * (a.NG / 2) + 2 * c);
 }

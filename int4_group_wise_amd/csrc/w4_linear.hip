@@ -497,7 +497,8 @@ __global__ __launch_bounds__(kTileWaves * kWave, 4) void skinny_mfma_kernel(Line
 #pragma unroll
     for (int j = 0; j < KR; ++j) {
       const uint32_t kb = static_cast<uint32_t>(min(kbs + j, nkb - 1));
-      cw[j] = *reinterpret_cast<const u32x4*>(cbase + rload * static_cast<uint32_t>(KB) + 64u * kb + 16u * cq);
+      cw[j] = __builtin_nontemporal_load(   // code words are read once
+          reinterpret_cast<const u32x4*>(cbase + rload * static_cast<uint32_t>(KB) + 64u * kb + 16u * cq));
     }
   };
   auto store_tab = [&]() {
@@ -694,7 +695,8 @@ __device__ __forceinline__ void rows_issue(const LinearArgs& a, int b, int nkb, 
 #pragma unroll
   for (int j = 0; j < kRowsKB; ++j) {
     const uint32_t kb = static_cast<uint32_t>(min(kbf + j, nkb - 1));
-    R.cw[j] = *reinterpret_cast<const u32x4*>(crow + 64u * kb + 16u * static_cast<uint32_t>(lane >> 4));
+    R.cw[j] = __builtin_nontemporal_load(   // code words are read once
+        reinterpret_cast<const u32x4*>(crow + 64u * kb + 16u * static_cast<uint32_t>(lane >> 4)));
   }
   __builtin_amdgcn_sched_barrier(0);
 }

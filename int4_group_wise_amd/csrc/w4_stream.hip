@@ -76,9 +76,11 @@ __global__ __launch_bounds__(kStreamWG * kWave) void gemv_stream_kernel(LinearAr
       cw[r][j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(a.codes + (n * KB + 16u * slice(j))));
 #pragma unroll
     for (int j = 0; j < S; ++j) {
-      sc[r][j] = *reinterpret_cast<const float*>(reinterpret_cast<const uint8_t*>(a.scales) + 4u * (n * NG + g[j]));
-      if constexpr (ZP == 1) zb[r][j] = a.zeros[n * NG + g[j]];
-      if constexpr (ZP == 2) zb[r][j] = a.zeros[n * ((NG + 1u) >> 1) + (g[j] >> 1)];
+      // scales and zero-points are read once per call too: non-temporal
+      sc[r][j] = __builtin_nontemporal_load(
+          reinterpret_cast<const float*>(reinterpret_cast<const uint8_t*>(a.scales) + 4u * (n * NG + g[j])));
+      if constexpr (ZP == 1) zb[r][j] = __builtin_nontemporal_load(a.zeros + (n * NG + g[j]));
+      if constexpr (ZP == 2) zb[r][j] = __builtin_nontemporal_load(a.zeros + (n * ((NG + 1u) >> 1) + (g[j] >> 1)));
       if constexpr (ZP == 0) zb[r][j] = 8u;
     }
     __builtin_amdgcn_sched_barrier(0);   // issue order = use order, row by row
