@@ -4,8 +4,8 @@
 // backward).
 //
 // M <= 16: the reduction runs over the rows of W, so the N rows are split
-// into P slices.  A workgroup of 4 waves takes 64 * CPT columns of dx and one
-// slice; a lane owns CPT consecutive columns (32, one 16-byte code load per
+// into P slices.  A workgroup of 4 waves (8 for one dy row and 32 columns per
+// lane) takes 64 * CPT columns of dx and one slice; a lane owns CPT consecutive columns (32, one 16-byte code load per
 // row, when groups are contiguous and a multiple of 32 wide and M <= 4; else
 // 8, one dword), streams the code words of its wave's rows (coalesced across
 // the wave) and accumulates dy[m, n] * w[n, k] in fp32, the dy values being
@@ -28,9 +28,16 @@ namespace {
 constexpr int kGThreads = 256;
 constexpr int kGWaves = kGThreads / kWave;
 // rows of a wave whose loads are issued together: 16 for contiguous groups
-// when a lane's accumulators are few (MT * CPT <= 32), else 8
-template <int MT, int CPT, bool GIDX>
-constexpr int grad_unroll() { return !GIDX && MT * CPT <= 32 ? 16 : 8; }
+// when a lane's accumulators are few (MT * CPT <= 32) and the workgroup has 4
+// waves, else 8
+template <int MT, int CPT, bool GIDX, int WV>
+constexpr int grad_unroll() { return !GIDX && MT * CPT <= 32 && WV == 4 ? 16 : 8; }
+
+// Waves per split workgroup: 8 for one dy row and 32 columns per lane (twice
+// the waves per SIMD for the same slices, so that one wave's arithmetic runs
+// while another waits for its loads), else 4.
+template <int MT, int CPT>
+constexpr int grad_waves() { return MT == 1 && CPT == 32 ? 8 : 4; }
 
 // Columns per lane: 32 (one 16-byte code load per row) for contiguous groups
 // of a multiple of 32 columns and at most 4 dy rows, else 8 (one dword).
@@ -49,18 +56,19 @@ __device__ __forceinline__ uint32_t load_bf16_uniform(const uint16_t* p, int64_t
   return (off & 2) ? (word >> 16) : (word & 0xFFFFu);
 }
 
-// The four waves' sums meet in LDS in one step (all four buffers at once, 32 KB
-// for 32 values per lane) when the buffers fit in 32 KB, else one buffer at a time.
-template <int MT, int CPT>
-constexpr bool grad_parallel_sum() { return kGWaves * MT * CPT * kWave * 4 <= 32768 && CPT % (4 * kGWaves) == 0; }
+// The waves' sums meet in LDS in one step (every wave's buffer at once: 32 KB
+// for 4 waves of 32 values per lane, 64 KB for 8) when a lane holds at most 32
+// values, else one buffer at a time.
+template <int MT, int CPT, int WV>
+constexpr bool grad_parallel_sum() { return MT * CPT * kWave * 4 <= 8192 && CPT % (4 * WV) == 0; }
 
 // One workgroup: 64 * CPT columns of dx (lane l owns columns CPT l ..), one
-// slice of rows of W; wave w takes rows w, w + 4, ... of the slice.  The 4
-// waves' sums are added through LDS in wave order and written as the slice's
-// partial (by all four waves, a quarter of the columns each, when the four
+// slice of rows of W; wave w of WV takes rows w, w + WV, ... of the slice.
+// The waves' sums are added through LDS in wave order and written as the
+// slice's partial (by all waves, an equal share of the columns each, when the
 // buffers fit; else by wave 0).
-template <bool ASYM, bool GIDX, int MT, int CPT>
-__global__ __launch_bounds__(kGThreads) void grad_split_kernel(GradArgs a, int rows_per) {
+template <bool ASYM, bool GIDX, int MT, int CPT, int WV>
+__global__ __launch_bounds__(WV * kWave) void grad_split_kernel(GradArgs a, int rows_per) {
   extern __shared__ __attribute__((aligned(16))) float gsm[];
   constexpr int kW = CPT / 8;                         // code dwords per row
   const int lane = lane_id();
@@ -95,8 +103,8 @@ __global__ __launch_bounds__(kGThreads) void grad_split_kernel(GradArgs a, int r
     for (int e = 0; e < CPT; ++e) acc[m][e] = 0.0f;
   }
 
-  constexpr int kGUnroll = grad_unroll<MT, CPT, GIDX>();
-  for (int64_t n0 = nb + w; n0 < ne; n0 += kGUnroll * kGWaves) {
+  constexpr int kGUnroll = grad_unroll<MT, CPT, GIDX, WV>();
+  for (int64_t n0 = nb + w; n0 < ne; n0 += kGUnroll * WV) {
     uint32_t d[kGUnroll][kW];
     float s[kGUnroll][kNGrp];
     uint32_t zb[kGUnroll][kNGrp];   // raw zero-point bytes; the zero-points are taken out at their use
@@ -104,7 +112,7 @@ __global__ __launch_bounds__(kGThreads) void grad_split_kernel(GradArgs a, int r
     // loads of this wave's next kGUnroll rows first (past the slice: reload the last)
 #pragma unroll
     for (int u = 0; u < kGUnroll; ++u) {
-      const int64_t n = min(n0 + u * kGWaves, ne - 1);
+      const int64_t n = min(n0 + u * WV, ne - 1);
       const uint8_t* crow = a.codes + n * KB + CPT / 2 * (k0 / CPT);
       if (aligned) {
         if constexpr (kW == 4) {
@@ -132,10 +140,11 @@ __global__ __launch_bounds__(kGThreads) void grad_split_kernel(GradArgs a, int r
     }
 #pragma unroll
     for (int u = 0; u < kGUnroll; ++u) {
-      // rows past the slice (their loads repeated the last row) and rows
-      // m >= M (reading row M - 1) add nothing: their dy factor is 0
-      const int64_t n = n0 + u * kGWaves;
-      const bool valid = n < ne;
+      // rows past the slice (their loads repeated the last row) are skipped,
+      // a uniform branch; rows m >= M (reading row M - 1) add nothing: their
+      // dy factor is 0
+      const int64_t n = n0 + u * WV;
+      if (n >= ne) break;
       float z[kNGrp];
 #pragma unroll
       for (int e = 0; e < kNGrp; ++e)
@@ -144,7 +153,7 @@ __global__ __launch_bounds__(kGThreads) void grad_split_kernel(GradArgs a, int r
 #pragma unroll
       for (int m = 0; m < MT; ++m) {
         const float dv = bf16_to_f32(dyr[u][m]);
-        dm[m] = valid && m < M ? dv : 0.0f;
+        dm[m] = m < M ? dv : 0.0f;
       }
       if constexpr (GIDX) {
 #pragma unroll
@@ -191,19 +200,19 @@ __global__ __launch_bounds__(kGThreads) void grad_split_kernel(GradArgs a, int r
       for (int e = 0; e < CPT; ++e) acc[m][e] -= corr[m];
   }
 
-  // add the 4 waves' sums in wave order 0..3 (the same order either way)
+  // add the waves' sums in wave order 0, 1, .. (the same order either way)
   float* part = a.partial + static_cast<int64_t>(blockIdx.y) * M * a.K;
-  if constexpr (grad_parallel_sum<MT, CPT>()) {
+  if constexpr (grad_parallel_sum<MT, CPT, WV>()) {
     // every wave stores its sums (register order [m][e], lane-major so the
-    // accesses are unit-stride), then wave w adds columns e of its quarter
-    // over the four waves and writes them
+    // accesses are unit-stride), then wave w adds columns e of its share
+    // over the waves and writes them
 #pragma unroll
     for (int m = 0; m < MT; ++m)
 #pragma unroll
       for (int e = 0; e < CPT; ++e) gsm[((w * MT + m) * CPT + e) * kWave + lane] = acc[m][e];
     __syncthreads();
     if (!live) return;
-    constexpr int kQ = CPT / kGWaves;                 // columns per wave
+    constexpr int kQ = CPT / WV;                      // columns per wave
 #pragma unroll
     for (int m = 0; m < MT; ++m) {
       if (m >= M) continue;
@@ -213,7 +222,7 @@ __global__ __launch_bounds__(kGThreads) void grad_split_kernel(GradArgs a, int r
         const int e = w * kQ + i;
         t[i] = gsm[((0 * MT + m) * CPT + e) * kWave + lane];
 #pragma unroll
-        for (int src = 1; src < kGWaves; ++src) t[i] += gsm[((src * MT + m) * CPT + e) * kWave + lane];
+        for (int src = 1; src < WV; ++src) t[i] += gsm[((src * MT + m) * CPT + e) * kWave + lane];
       }
       float* dst = part + static_cast<int64_t>(m) * a.K + k0 + w * kQ;
       if (cnt == CPT && (a.K & 3) == 0) {
@@ -228,7 +237,7 @@ __global__ __launch_bounds__(kGThreads) void grad_split_kernel(GradArgs a, int r
     return;
   }
   // larger tiles: waves 1..3 in turn through one buffer
-  for (int src = 1; src < kGWaves; ++src) {
+  for (int src = 1; src < WV; ++src) {
     if (w == src) {
 #pragma unroll
       for (int m = 0; m < MT; ++m)
@@ -263,9 +272,10 @@ __global__ __launch_bounds__(kGThreads) void grad_split_kernel(GradArgs a, int r
 
 // dx[i] = bf16(sum over slices p = 0 .. P-1 of partial[p][i]), i over M * K.
 // A workgroup takes 64 outputs; its 16 waves sum 16 fixed ranges of slices
-// (8 loads in flight per lane), then wave 0 adds the 16 range sums in order,
-// so the result does not depend on scheduling.
+// (16 loads in flight per lane: one round when P <= 256), then wave 0 adds
+// the 16 range sums in order, so the result does not depend on scheduling.
 constexpr int kRParts = 16;
+constexpr int kRLoads = 16;
 __global__ __launch_bounds__(kRParts * kWave) void grad_reduce_kernel(const float* __restrict__ partial,
                                                                       int P, int64_t total, uint16_t* __restrict__ dx) {
   __shared__ float red[kRParts][kWave];
@@ -276,12 +286,12 @@ __global__ __launch_bounds__(kRParts * kWave) void grad_reduce_kernel(const floa
   const int per = (P + kRParts - 1) / kRParts;
   const int p0 = part * per, p1 = min(P, p0 + per);
   float sum = 0.0f;
-  for (int p = p0; p < p1; p += 8) {
-    float v[8];
+  for (int p = p0; p < p1; p += kRLoads) {
+    float v[kRLoads];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) v[u] = partial[static_cast<int64_t>(min(p + u, p1 - 1)) * total + ic];
+    for (int u = 0; u < kRLoads; ++u) v[u] = partial[static_cast<int64_t>(min(p + u, p1 - 1)) * total + ic];
 #pragma unroll
-    for (int u = 0; u < 8; ++u)
+    for (int u = 0; u < kRLoads; ++u)
       if (p + u < p1) sum += v[u];
   }
   red[part][lane] = sum;
@@ -414,8 +424,9 @@ __global__ __launch_bounds__(kGThreads) void dequantize_t_kernel(DequantArgs a, 
 template <bool ASYM, bool GIDX, int MT, int CPT>
 hipError_t launch_split4(const GradArgs& a, int P, int rows_per, hipStream_t s) {
   const dim3 grid(static_cast<uint32_t>((a.K + kWave * CPT - 1) / (kWave * CPT)), static_cast<uint32_t>(P));
-  const size_t lds = static_cast<size_t>(grad_parallel_sum<MT, CPT>() ? kGWaves : 1) * MT * CPT * kWave * sizeof(float);
-  grad_split_kernel<ASYM, GIDX, MT, CPT><<<grid, dim3(kGThreads), lds, s>>>(a, rows_per);
+  constexpr int WV = grad_waves<MT, CPT>();
+  const size_t lds = static_cast<size_t>(grad_parallel_sum<MT, CPT, WV>() ? WV : 1) * MT * CPT * kWave * sizeof(float);
+  grad_split_kernel<ASYM, GIDX, MT, CPT, WV><<<grid, dim3(WV * kWave), lds, s>>>(a, rows_per);
   return hipGetLastError();
 }
 
