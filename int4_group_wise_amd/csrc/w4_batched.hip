@@ -293,17 +293,25 @@ __global__ __launch_bounds__(kBWaves * kWave, 2) void batched_kernel(LinearArgs 
     BStage st[2];
     b_issue<U>(R, p0, st[0]);
     b_table<ZP>(a, n0, br, S, lane, stab, ztab);   // wave-private: the wave's own LDS writes precede its reads
-    // whole rounds of two pairs, with no exit inside the loop body (an exit
-    // would leave stage loads pending on a path back to the loop head, and
-    // the wait there would cover every load in flight)
+    // whole rounds of two pairs while a pair follows them, with no exit
+    // inside the loop body (an exit would leave stage loads pending on a path
+    // back to the loop head, and the wait there would cover every load in
+    // flight); the last one or two pairs after the loop, so that no pair is
+    // loaded twice
     uint32_t p = p0;
-    for (; p + 1 <= pl; p += 2) {
+    for (; p + 2 <= pl; p += 2) {
       b_issue<U>(R, p + 1, st[1]);
       b_compute<ZP, U>(R, p, st[0], mask, stab, ztab, S, g_lo, lane, xl, cl, out);
-      b_issue<U>(R, min(p + 2, pl), st[0]);
+      b_issue<U>(R, p + 2, st[0]);
       b_compute<ZP, U>(R, p + 1, st[1], mask, stab, ztab, S, g_lo, lane, xl, cl, out);
     }
-    if (p <= pl) b_compute<ZP, U>(R, p, st[0], mask, stab, ztab, S, g_lo, lane, xl, cl, out);   // already in st[0]
+    if (p + 1 <= pl) {
+      b_issue<U>(R, p + 1, st[1]);
+      b_compute<ZP, U>(R, p, st[0], mask, stab, ztab, S, g_lo, lane, xl, cl, out);
+      b_compute<ZP, U>(R, p + 1, st[1], mask, stab, ztab, S, g_lo, lane, xl, cl, out);
+    } else {
+      b_compute<ZP, U>(R, p, st[0], mask, stab, ztab, S, g_lo, lane, xl, cl, out);   // already in st[0]
+    }
   }
 
   // the K quarters' tiles meet in LDS; wave 0 adds them in wave order
