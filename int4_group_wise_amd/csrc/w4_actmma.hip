@@ -71,7 +71,14 @@ struct ARows {
   }
 };
 
-__device__ __forceinline__ void a_issue(const ARows& R, uint32_t p, AStage& st) {
+// Pair p of the wave's range p0 .. pl.  A prefetch past the range (the loop
+// issues whole rounds) reads, in place of code words, 1 KB of the activations,
+// which every wave reads and the cache holds, so that no code line is fetched
+// twice; its stage is never computed.
+__device__ __forceinline__ void a_issue(const ARows& R, uint32_t p, uint32_t pl, AStage& st) {
+  const bool past = p > pl;
+  const uint8_t* cbase = past ? R.xb : R.cb;
+  p = min(p, pl);
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
     const uint32_t k0 = 256u * p + 128u * j;   // first column of batch j
@@ -82,7 +89,7 @@ __device__ __forceinline__ void a_issue(const ARows& R, uint32_t p, AStage& st) 
   }
 #pragma unroll
   for (int i = 0; i < 2 * kARB; ++i)   // code words are read once: non-temporal
-    st.cw[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(R.cb + (R.c[i] + 128u * p)));
+    st.cw[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(cbase + (past ? 4u * R.l4 : R.c[i] + 128u * p)));
   __builtin_amdgcn_sched_barrier(0);
 }
 
@@ -271,9 +278,9 @@ __global__ __launch_bounds__(kAWaves * kWave) void act_mma_kernel(LinearArgs a) 
     const ARows R(a, n0, lane);
     const uint32_t p0 = static_cast<uint32_t>(bb) / 2, pl = static_cast<uint32_t>(be - 1) / 2;
     AStage st[4];
-    a_issue(R, p0, st[0]);
-    a_issue(R, min(p0 + 1, pl), st[1]);
-    a_issue(R, min(p0 + 2, pl), st[2]);
+    a_issue(R, p0, pl, st[0]);
+    a_issue(R, p0 + 1, pl, st[1]);
+    a_issue(R, p0 + 2, pl, st[2]);
     if constexpr (V4) a_table_store<ZP>(NG, w, lane, tl, stab, ztab);
     else a_epilogue_loads<ZP, H, V4>(a, n0, lane, ep);
     // the A buffer starts at zero (the wave's own stores precede its reads)
@@ -284,13 +291,13 @@ __global__ __launch_bounds__(kAWaves * kWave) void act_mma_kernel(LinearArgs a) 
     // there would cover every load in flight)
     uint32_t p = p0;
     for (; p + 3 <= pl; p += 4) {
-      a_issue(R, min(p + 3, pl), st[3]);
+      a_issue(R, p + 3, pl, st[3]);
       a_compute<ZP, H>(st[0], NG, mask, lane, al, cl, prev, acc);
-      a_issue(R, min(p + 4, pl), st[0]);
+      a_issue(R, p + 4, pl, st[0]);
       a_compute<ZP, H>(st[1], NG, mask, lane, al, cl, prev, acc);
-      a_issue(R, min(p + 5, pl), st[1]);
+      a_issue(R, p + 5, pl, st[1]);
       a_compute<ZP, H>(st[2], NG, mask, lane, al, cl, prev, acc);
-      a_issue(R, min(p + 6, pl), st[2]);
+      a_issue(R, p + 6, pl, st[2]);
       a_compute<ZP, H>(st[3], NG, mask, lane, al, cl, prev, acc);
     }
     // the last 0 to 3 pairs are already in st[0 .. 2]
