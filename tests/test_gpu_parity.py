@@ -549,6 +549,10 @@ GRAD_CASES = [
     (17, 4096, 1152, 128, "sym", False), (17, 64, 128, 64, "sym", False), (24, 64, 1024, -1, "asym", False),
     # more than 32 groups per row: the tiled layout without value tables
     (24, 64, 4096, 64, "asym", True),
+    # one dy row, 32 columns per lane (8-wave slices): 32 slices, the last of 8 rows (one per
+    # wave); 3 slices of 25-26 rows (waves of 3 or 4 rows); K % 2048 != 0 (a lane with 24 columns,
+    # lanes past K)
+    (1, 1000, 2048, 64, "sym", False), (1, 77, 4096, 32, "asym", False), (1, 300, 3000, 64, "asym", False),
 ]
 
 
