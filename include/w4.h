@@ -76,7 +76,7 @@ extern "C" {
 typedef enum {
   W4_OK = 0,
   W4_ERR_INVALID_ARG = 1,  /* bad size, null pointer, misaligned pointer, mode */
-  W4_ERR_UNSUPPORTED = 2,  /* valid request this build does not implement   */
+  W4_ERR_UNSUPPORTED = 2,  /* valid request the library does not implement  */
   W4_ERR_HIP = 3           /* a HIP runtime call or kernel launch failed     */
 } w4_status;
 
