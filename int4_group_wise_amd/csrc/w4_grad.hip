@@ -446,7 +446,12 @@ GradPlan grad_plan(int64_t M, int64_t N, int64_t K, int64_t G, bool has_g_idx) {
   if (M <= kGradSkinnyMax) {
     const int cpt = !has_g_idx && G % 32 == 0 && M <= 4 ? 32 : 8;     // columns per lane
     const int64_t cb = (K + kWave * cpt - 1) / (kWave * cpt);        // column blocks
-    int64_t P = std::max<int64_t>(1, 512 / cb);                      // about 2 workgroups per CU
+    // about 2048 waves (two per SIMD): 256 workgroups of 8 waves (M = 1 with 32
+    // columns per lane) or 512 of 4; at the decode layer's shape (K = 4096) 128
+    // slices of 112 rows took 13.2-13.4 us per call against 13.6-14.1 us with
+    // 256 slices of 56 rows (64, 96 and 192 slices: 17.9, 14.7, 15.5 us)
+    const int wv = M <= 1 && cpt == 32 ? 8 : 4;                      // grad_waves<MT, CPT>()
+    int64_t P = std::max<int64_t>(1, 2048 / wv / cb);
     P = std::min<int64_t>(P, (N + 31) / 32);                          // at least 32 rows per slice
     const int64_t per_slice = M * K * 4;
     P = std::min<int64_t>(P, std::max<int64_t>(1, kGradPartialBytes / per_slice));
